@@ -1,0 +1,180 @@
+"""Seeded synthetic inputs for the DFlash 2 path selector.
+
+This module only draws random numbers and lays them out; it holds none of the
+selector's arithmetic.  Both the HIP path (through the binding) and the CPU
+oracle are fed from here, so that every comparison runs on the same bytes.
+
+Workload recipes (value distributions and shapes) follow the five named
+workloads of the selector: a tiny fp32 case, a Qwen3-4B-shaped drafter at
+batch 1, a 27B-target-shaped drafter at concurrency 8 and 32, and a stress
+sweep.  The pages ("DFlash 2: Keep Drafting Parallel", section "A Lightweight
+Path Selector") fix the shape of the method: top-16 candidates per draft
+position and 256-dimensional token embeddings; a block of 8 holds one verified
+token and 7 draft positions (dev.to model-card article, benchmark setup).
+
+Readings of the recipe wording:
+  * "N(mu, s)" means standard deviation s; "N(0, 1/sqrt(r))" is std 1/16.
+  * Peaked rows: m ~ U{1,2,3} peak tokens drawn uniformly over V, boosted by
+    4 + 6/k for k = 1..m (+10, +7, +6).
+  * Sequence b draws its logits, peaks and prev_tok from sub-seed
+    seed * 1000 + b ("per-sequence seeded").
+  * Flat rows are N(0, 1) with no peak; the saturation workload makes exactly
+    round(0.2 * B * P) rows flat, chosen by a seeded permutation; the stress
+    workload makes 30 % flat and, in a peaked row at t >= 1, reuses the
+    previous row's top-peak token with probability 0.25.
+  * Hidden states are N(0, 1) (the recipe does not state them).
+bf16 tensors are produced by round-to-nearest-even from fp32 and kept as raw
+uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "Inputs", "make_inputs", "f32_to_bf16_bits",
+    "bf16_bits_to_f64", "to_f64",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int            # index into WORKLOADS; base seed is 0xDF2000 + wid
+    B: int              # sequences
+    P: int              # draft positions (block size minus the verified token)
+    V: int              # vocabulary
+    d: int              # drafter hidden size
+    K: int              # candidates kept per position
+    r: int = 256        # embedding rank of A, B, H
+    dtype: str = "bf16"     # "f32" or "bf16" for logits, hidden, A, B, W_H
+    logit_kind: str = "zipf"   # "true_token" | "zipf"
+    flat_frac: float = 0.0
+    flat_mode: str = "exact"   # "exact": round(frac*rows) rows; "mixed": per-row draw
+    dup_prob: float = 0.0
+    pair_scale: float = 1.0    # multiplies A and B (test preset: pair-dominant)
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.P
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_f32": Workload("tiny_f32", 0, B=1, P=7, V=32000, d=1024, K=16,
+                         dtype="f32", logit_kind="true_token"),
+    "qwen3_4b_b1": Workload("qwen3_4b_b1", 1, B=1, P=7, V=151936, d=2560, K=16),
+    "t27b_b8": Workload("t27b_b8", 2, B=8, P=7, V=151936, d=5120, K=16),
+    "t27b_b32": Workload("t27b_b32", 3, B=32, P=7, V=151936, d=5120, K=16,
+                         flat_frac=0.2, flat_mode="exact"),
+    "stress_b256": Workload("stress_b256", 4, B=256, P=15, V=262144, d=5120, K=32,
+                            flat_frac=0.3, flat_mode="mixed", dup_prob=0.25),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even fp32 -> bf16, returned as uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float64."""
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host arrays in storage form: float32 for "f32", uint16 bits for "bf16"."""
+    wl: Workload
+    logits: np.ndarray    # [B, P, V]
+    hidden: np.ndarray    # [B, P, d]
+    A: np.ndarray         # [V, r]
+    Bt: np.ndarray        # [V, r]
+    W: np.ndarray         # [r, d]
+    prev: np.ndarray      # [B] int32
+
+    def f64(self):
+        dt = self.wl.dtype
+        return dict(logits=to_f64(self.logits, dt), hidden=to_f64(self.hidden, dt),
+                    A=to_f64(self.A, dt), Bt=to_f64(self.Bt, dt), W=to_f64(self.W, dt),
+                    prev=self.prev)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None,
+                logits_override: Optional[np.ndarray] = None) -> Inputs:
+    """Draw one full input set for workload `wl`.
+
+    `logits_override` (float32 [B, P, V]) replaces the drawn logits; tests use
+    it for hand-built tie patterns.
+    """
+    base = (0xDF2000 + wl.wid) if seed is None else int(seed)
+    g = np.random.Generator(np.random.PCG64(base))
+    B, P, V, d, r = wl.B, wl.P, wl.V, wl.d, wl.r
+    s = 1.0 / math.sqrt(r)
+    A = g.standard_normal((V, r), dtype=np.float32) * np.float32(s * wl.pair_scale)
+    Bt = g.standard_normal((V, r), dtype=np.float32) * np.float32(s * wl.pair_scale)
+    W = g.standard_normal((r, d), dtype=np.float32) * np.float32(s)
+    hidden = g.standard_normal((B, P, d), dtype=np.float32)
+
+    flat = np.zeros(B * P, dtype=bool)
+    if wl.flat_frac > 0 and wl.flat_mode == "exact":
+        n_flat = int(round(wl.flat_frac * B * P))
+        flat[g.permutation(B * P)[:n_flat]] = True
+    elif wl.flat_frac > 0:
+        flat = g.random(B * P) < wl.flat_frac
+    flat = flat.reshape(B, P)
+
+    prev = np.empty(B, dtype=np.int32)
+    if logits_override is not None:
+        logits = np.ascontiguousarray(logits_override, dtype=np.float32).reshape(B, P, V)
+        for b in range(B):
+            gb = np.random.Generator(np.random.PCG64(base * 1000 + b))
+            prev[b] = gb.integers(0, V)
+    else:
+        logits = np.empty((B, P, V), dtype=np.float32)
+        for b in range(B):
+            gb = np.random.Generator(np.random.PCG64(base * 1000 + b))
+            prev[b] = gb.integers(0, V)
+            if wl.logit_kind == "true_token":
+                row = gb.standard_normal((P, V), dtype=np.float32)
+                true_tok = gb.integers(0, V, size=P)
+                row[np.arange(P), true_tok] += np.float32(6.0)
+                logits[b] = row
+                continue
+            last_top = -1
+            for t in range(P):
+                if flat[b, t]:
+                    logits[b, t] = gb.standard_normal(V, dtype=np.float32)
+                    last_top = -1
+                    continue
+                row = gb.standard_normal(V, dtype=np.float32) * np.float32(2.0)
+                m = int(gb.integers(1, 4))
+                toks = gb.integers(0, V, size=m)
+                if wl.dup_prob > 0 and last_top >= 0 and gb.random() < wl.dup_prob:
+                    toks[0] = last_top
+                for k in range(m):
+                    row[toks[k]] += np.float32(4.0 + 6.0 / (k + 1))
+                last_top = int(toks[0])
+                logits[b, t] = row
+    dt = wl.dtype
+    return Inputs(wl=wl, logits=_store(logits, dt), hidden=_store(hidden, dt),
+                  A=_store(A, dt), Bt=_store(Bt, dt), W=_store(W, dt), prev=prev)

@@ -1,0 +1,166 @@
+"""CPU oracle for the DFlash 2 path selector (ctypes wrapper over oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and
+by bench.py's cpu_baseline leg.  The GPU product path never imports it.
+
+All arithmetic is float64 on inputs widened exactly from their storage type.
+The steps follow "DFlash 2: Keep Drafting Parallel", section "A Lightweight
+Path Selector" (top-16 candidates, the pair-score equation, one walk from the
+last verified token); the walk is read as max-sum Viterbi with backtrack and
+H(h_t) as a bias-free linear map d -> r (see the header of oracle.c).
+
+Every function here is pinned by CPU tests against something other than
+itself (brute-force enumeration, closed forms, exact integer cases, an
+independent sort); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (IEEE semantics, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-fno-fast-math", "-ffp-contract=off",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.orc_topk.argtypes = [P, I, I, ctypes.c_int32, P, P]
+        lib.orc_topk.restype = ctypes.c_int
+        lib.orc_project.argtypes = [P, P, I, I, I, P]
+        lib.orc_project.restype = None
+        lib.orc_pair_scores.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P]
+        lib.orc_pair_scores.restype = None
+        lib.orc_viterbi.argtypes = [P, P, I, I, I, P, P, P]
+        lib.orc_viterbi.restype = ctypes.c_int
+        lib.orc_second_best.argtypes = [P, P, I, I, I, P]
+        lib.orc_second_best.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def topk(x: np.ndarray, K: int):
+    """Top-K per row of x[..., V]: (idx int32 [..., K], val float64 [..., K])."""
+    x = _f64(x)
+    V = x.shape[-1]
+    rows = x.size // V if V else 0
+    idx = np.empty(x.shape[:-1] + (K,), dtype=np.int32)
+    val = np.empty(x.shape[:-1] + (K,), dtype=np.float64)
+    if rows and _load().orc_topk(_p(x), rows, V, K, _p(idx), _p(val)) != 0:
+        raise ValueError("orc_topk: bad K/V or out of memory")
+    return idx, val
+
+
+def project(h: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """H[..., q] = sum_m W[q, m] h[..., m]  (W is [r, d])."""
+    h = _f64(h)
+    W = _f64(W)
+    r, d = W.shape
+    M = h.size // d
+    H = np.empty(h.shape[:-1] + (r,), dtype=np.float64)
+    _load().orc_project(_p(h), _p(W), M, d, r, _p(H))
+    return H
+
+
+def pair_scores(cand, U, H, A, Bt, prev):
+    """S[b, t, i, j] and the tolerance scale sigma, both [B, P, K, K] float64."""
+    cand = _i32(cand)
+    U = _f64(U)
+    H = _f64(H)
+    A = _f64(A)
+    Bt = _f64(Bt)
+    prev = _i32(prev)
+    Bn, P, K = cand.shape
+    r = H.shape[-1]
+    S = np.empty((Bn, P, K, K), dtype=np.float64)
+    sig = np.empty((Bn, P, K, K), dtype=np.float64)
+    _load().orc_pair_scores(_p(cand), _p(U), _p(H), _p(A), _p(Bt), _p(prev),
+                            Bn, P, K, r, _p(S), _p(sig))
+    return S, sig
+
+
+def viterbi(S, cand):
+    """(path_rank [B,P] int32, path_tok [B,P] int32, score [B] float64)."""
+    S = _f64(S)
+    cand = _i32(cand)
+    Bn, P, K = cand.shape
+    pr = np.empty((Bn, P), dtype=np.int32)
+    pt = np.empty((Bn, P), dtype=np.int32)
+    sc = np.empty(Bn, dtype=np.float64)
+    if _load().orc_viterbi(_p(S), _p(cand), Bn, P, K, _p(pr), _p(pt), _p(sc)) != 0:
+        raise MemoryError("orc_viterbi")
+    return pr, pt, sc
+
+
+def second_best(S, path_rank) -> np.ndarray:
+    """Second-best path score per sequence (-inf when K == 1)."""
+    S = _f64(S)
+    path_rank = _i32(path_rank)
+    Bn, P = path_rank.shape
+    K = S.shape[-1]
+    out = np.empty(Bn, dtype=np.float64)
+    if _load().orc_second_best(_p(S), _p(path_rank), Bn, P, K, _p(out)) != 0:
+        raise MemoryError("orc_second_best")
+    return out
+
+
+def select(logits, hidden, A, Bt, W, prev, K: int,
+           seqs: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """The whole selector on float64 inputs; returns every intermediate.
+
+    logits [B,P,V], hidden [B,P,d], A/Bt [V,r], W [r,d], prev [B].
+    `seqs` restricts the work to a subset of sequences (sampled checks on
+    large workloads); outputs then follow the order of `seqs`.
+    """
+    if seqs is not None:
+        seqs = np.asarray(seqs, dtype=np.int64)
+        logits = np.asarray(logits)[seqs]
+        hidden = np.asarray(hidden)[seqs]
+        prev = np.asarray(prev)[seqs]
+    cand, U = topk(logits, K)
+    H = project(hidden, W)
+    S, sig = pair_scores(cand, U, H, A, Bt, prev)
+    pr, pt, sc = viterbi(S, cand)
+    sec = second_best(S, pr)
+    P = cand.shape[1]
+    # scale of the best path: sum of sigma along it (tolerance for scores)
+    sig_path = np.zeros(cand.shape[0], dtype=np.float64)
+    for b in range(cand.shape[0]):
+        sig_path[b] = sig[b, 0, 0, pr[b, 0]] + sum(
+            sig[b, t, pr[b, t - 1], pr[b, t]] for t in range(1, P))
+    return dict(cand=cand, U=U, H=H, S=S, sigma=sig, path_rank=pr, path=pt,
+                score=sc, second=sec, margin=sc - sec, sigma_path=sig_path)

@@ -1,0 +1,256 @@
+/*
+ * CPU oracle for the DFlash 2 path selector.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  The GPU
+ * product path never calls it, and it shares no code with the GPU path.
+ *
+ * Everything here is the plain definition of each step, in float64, written
+ * for a reader to check against the pages by eye:
+ *
+ *   "DFlash 2: Keep Drafting Parallel", section "A Lightweight Path Selector":
+ *     - keep the top 16 candidates at each draft position;
+ *     - score every adjacent pair (predecessor a, current candidate b) with
+ *       the selector equation  S_t(a,b) = U_t(b) + < A(a) (.) H(h_t), B(b) >,
+ *       where U_t is the drafter's own logit, A and B are 256-dimensional
+ *       token embeddings and H(h_t) is a gate computed from the drafter's
+ *       hidden state;
+ *     - the only sequential work is one walk over the precomputed scores,
+ *       starting from the last verified token.
+ *
+ * Readings taken where the pages are silent or truncated:
+ *   - H(h_t) is a linear map d -> r without bias or activation:
+ *       H[q] = sum_m W_H[q][m] * h_t[m]           (W_H stored [r][d]).
+ *   - The walk is a max-sum (Viterbi) pass plus backtrack over the
+ *     candidate lattice; the predecessor of the first draft position is the
+ *     last verified token prev_tok.
+ *   - Top-K order is value descending; equal values (IEEE equality, so
+ *     -0 == +0) go to the lower vocabulary index.
+ *   - Viterbi ties go to the smaller predecessor rank; the final pick goes
+ *     to the smaller rank.
+ *   - U_t(b) is the raw logit.
+ *
+ * Parity pins (checked by the CPU test suite, not by this file): brute-force
+ * enumeration of all K^P paths on tiny inputs, zeroed pair term reducing to
+ * independent top-1 picks, K = 1 and P = 1 closed forms, exact integer
+ * fixtures, logit-shift invariance, and an independent lexicographic sort for
+ * top-K.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    double v;
+    int32_t i;
+} orc_item;
+
+/* Order: larger value first; for equal values the lower index first. */
+static int orc_item_cmp(const void* pa, const void* pb) {
+    const orc_item* a = (const orc_item*)pa;
+    const orc_item* b = (const orc_item*)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    if (a->i < b->i) return -1;
+    if (a->i > b->i) return 1;
+    return 0;
+}
+
+/*
+ * Top-K per row: sort the whole row and keep the first K entries
+ * (section "A Lightweight Path Selector": top 16 candidates per position).
+ *   x    [rows][V]   logits, already widened exactly to float64
+ *   idx  [rows][K]   vocabulary index of the k-th best candidate
+ *   val  [rows][K]   its logit U_t
+ * Returns 0, or -1 on allocation failure / bad sizes.
+ */
+int orc_topk(const double* x, int64_t rows, int64_t V, int32_t K,
+             int32_t* idx, double* val) {
+    if (K < 1 || K > V) return -1;
+    orc_item* items = (orc_item*)malloc(sizeof(orc_item) * (size_t)V);
+    if (!items) return -1;
+    for (int64_t row = 0; row < rows; ++row) {
+        const double* xr = x + row * V;
+        for (int64_t v = 0; v < V; ++v) {
+            items[v].v = xr[v];
+            items[v].i = (int32_t)v;
+        }
+        qsort(items, (size_t)V, sizeof(orc_item), orc_item_cmp);
+        for (int32_t k = 0; k < K; ++k) {
+            idx[row * K + k] = items[k].i;
+            val[row * K + k] = items[k].v;
+        }
+    }
+    free(items);
+    return 0;
+}
+
+/*
+ * Gate projection H = W_H h for every (sequence, position) row.
+ *   h  [M][d], W [r][d], H [M][r]
+ */
+void orc_project(const double* h, const double* W, int64_t M, int64_t d,
+                 int64_t r, double* H) {
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t q = 0; q < r; ++q) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < d; ++k) acc += W[q * d + k] * h[m * d + k];
+            H[m * r + q] = acc;
+        }
+    }
+}
+
+/*
+ * Pair scores, the selector equation of section "A Lightweight Path
+ * Selector":  S_t(a, b) = U_t(b) + sum_q A[a][q] * H_t[q] * B[b][q].
+ *
+ *   cand  [Bn][P][K] candidate token ids (rank order)
+ *   U     [Bn][P][K] their logits
+ *   H     [Bn][P][r] gate vectors
+ *   A, Bt [V][r]     token embeddings
+ *   prev  [Bn]       last verified token per sequence
+ *   S     [Bn][P][K][K]   S[b][t][i][j]: predecessor rank i, candidate rank j
+ *   sigma [Bn][P][K][K]   |U| + sum_q |A H B|, the scale used for tolerances
+ *
+ * The predecessor of rank i at position t >= 1 is cand[b][t-1][i]; at t = 0
+ * every row i uses prev[b] (only row 0 is meaningful; the rest repeat it).
+ */
+void orc_pair_scores(const int32_t* cand, const double* U, const double* H,
+                     const double* A, const double* Bt, const int32_t* prev,
+                     int64_t Bn, int64_t P, int64_t K, int64_t r,
+                     double* S, double* sigma) {
+    for (int64_t b = 0; b < Bn; ++b) {
+        for (int64_t t = 0; t < P; ++t) {
+            const double* Ht = H + (b * P + t) * r;
+            for (int64_t i = 0; i < K; ++i) {
+                int64_t a = (t == 0) ? prev[b] : cand[(b * P + (t - 1)) * K + i];
+                for (int64_t j = 0; j < K; ++j) {
+                    int64_t c = cand[(b * P + t) * K + j];
+                    double u = U[(b * P + t) * K + j];
+                    double dot = 0.0, mag = 0.0;
+                    for (int64_t q = 0; q < r; ++q) {
+                        double term = A[a * r + q] * Ht[q] * Bt[c * r + q];
+                        dot += term;
+                        mag += fabs(term);
+                    }
+                    int64_t o = ((b * P + t) * K + i) * K + j;
+                    S[o] = u + dot;
+                    if (sigma) sigma[o] = fabs(u) + mag;
+                }
+            }
+        }
+    }
+}
+
+/*
+ * Max-sum walk over the candidate lattice with backtrack.
+ *   delta_0[j] = S[b][0][0][j]
+ *   delta_t[j] = max_i delta_{t-1}[i] + S[b][t][i][j]      (t = 1 .. P-1)
+ *   psi_t[j]   = smallest i attaining that max
+ *   j_{P-1}    = smallest j attaining max_j delta_{P-1}[j]
+ *   j_{t-1}    = psi_t[j_t]
+ * Outputs per sequence: rank path [P], token path [P] (cand[b][t][j_t]) and
+ * the best score delta_{P-1}[j_{P-1}].
+ * Returns 0, or -1 on allocation failure.
+ */
+int orc_viterbi(const double* S, const int32_t* cand, int64_t Bn, int64_t P,
+                int64_t K, int32_t* path_rank, int32_t* path_tok, double* score) {
+    double* delta = (double*)malloc(sizeof(double) * (size_t)(P * K));
+    int32_t* psi = (int32_t*)malloc(sizeof(int32_t) * (size_t)(P * K));
+    if (!delta || !psi) {
+        free(delta);
+        free(psi);
+        return -1;
+    }
+    for (int64_t b = 0; b < Bn; ++b) {
+        const double* Sb = S + b * P * K * K;
+        for (int64_t j = 0; j < K; ++j) {
+            delta[j] = Sb[j];           /* t = 0, row i = 0 */
+            psi[j] = 0;
+        }
+        for (int64_t t = 1; t < P; ++t) {
+            for (int64_t j = 0; j < K; ++j) {
+                double best = delta[(t - 1) * K + 0] + Sb[(t * K + 0) * K + j];
+                int32_t arg = 0;
+                for (int64_t i = 1; i < K; ++i) {
+                    double v = delta[(t - 1) * K + i] + Sb[(t * K + i) * K + j];
+                    if (v > best) {
+                        best = v;
+                        arg = (int32_t)i;
+                    }
+                }
+                delta[t * K + j] = best;
+                psi[t * K + j] = arg;
+            }
+        }
+        int32_t jb = 0;
+        for (int64_t j = 1; j < K; ++j)
+            if (delta[(P - 1) * K + j] > delta[(P - 1) * K + jb]) jb = (int32_t)j;
+        score[b] = delta[(P - 1) * K + jb];
+        int32_t j = jb;
+        for (int64_t t = P - 1; t >= 0; --t) {
+            path_rank[b * P + t] = j;
+            path_tok[b * P + t] = cand[(b * P + t) * K + j];
+            if (t > 0) j = psi[t * K + j];
+        }
+    }
+    free(delta);
+    free(psi);
+    return 0;
+}
+
+/*
+ * Best-versus-second path margin, from max-marginals.
+ *   alpha_t = forward max-sum (delta above), beta_{P-1} = 0,
+ *   beta_t[i] = max_j S[b][t+1][i][j] + beta_{t+1}[j],
+ *   M_t[j] = alpha_t[j] + beta_t[j] = best score of a path through rank j at t.
+ * Every path other than the best one leaves the best path's rank at some t,
+ * so the second-best score is max over t and j != path_rank[t] of M_t[j].
+ * second[b] = -inf when K == 1 (no other path).
+ * Returns 0, or -1 on allocation failure.
+ */
+int orc_second_best(const double* S, const int32_t* path_rank, int64_t Bn,
+                    int64_t P, int64_t K, double* second) {
+    double* alpha = (double*)malloc(sizeof(double) * (size_t)(P * K));
+    double* beta = (double*)malloc(sizeof(double) * (size_t)(P * K));
+    if (!alpha || !beta) {
+        free(alpha);
+        free(beta);
+        return -1;
+    }
+    for (int64_t b = 0; b < Bn; ++b) {
+        const double* Sb = S + b * P * K * K;
+        for (int64_t j = 0; j < K; ++j) alpha[j] = Sb[j];
+        for (int64_t t = 1; t < P; ++t)
+            for (int64_t j = 0; j < K; ++j) {
+                double best = -INFINITY;
+                for (int64_t i = 0; i < K; ++i) {
+                    double v = alpha[(t - 1) * K + i] + Sb[(t * K + i) * K + j];
+                    if (v > best) best = v;
+                }
+                alpha[t * K + j] = best;
+            }
+        for (int64_t j = 0; j < K; ++j) beta[(P - 1) * K + j] = 0.0;
+        for (int64_t t = P - 2; t >= 0; --t)
+            for (int64_t i = 0; i < K; ++i) {
+                double best = -INFINITY;
+                for (int64_t j = 0; j < K; ++j) {
+                    double v = Sb[((t + 1) * K + i) * K + j] + beta[(t + 1) * K + j];
+                    if (v > best) best = v;
+                }
+                beta[t * K + i] = best;
+            }
+        double sec = -INFINITY;
+        for (int64_t t = 0; t < P; ++t)
+            for (int64_t j = 0; j < K; ++j) {
+                if (j == path_rank[b * P + t]) continue;
+                double m = alpha[t * K + j] + beta[t * K + j];
+                if (m > sec) sec = m;
+            }
+        second[b] = sec;
+    }
+    free(alpha);
+    free(beta);
+    return 0;
+}
