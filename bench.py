@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash 2 path selector on one MI355X.
+
+One step = one dflash2_select launch over one batch: top-K of every logits
+row, the gate projection, all pair scores and the walk.  Inputs are seeded
+synthetic data resident in HBM; several copies of the per-cycle inputs
+(logits, hidden) are rotated so that the 256 MB Infinity Cache cannot serve
+them from the previous step.
+
+Prints ONE JSON line:
+  value       drafted positions/s (B*P per step) on the concurrency-32 workload
+              (B=32, P=7, V=151936, d=5120, K=16, bf16), wall clock over the
+              timed steps;
+  us_per_cycle / b1   the same for the batch-1 Qwen3-4B-shaped workload
+              (B=1, P=7, V=151936, d=2560, K=16, bf16), as microseconds per
+              draft-verify cycle;
+  roofline    algorithmic bytes per launch / average launch time (HIP events on
+              the launch stream) against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "path-select µs/cycle at B=1, drafted positions/s at B=32; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("common.hpp", "topk.hpp", "project.hpp", "tail.hpp", "dflash2.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes the method must move once per cycle: every logit, every hidden
+    value, W_H, the gathered A/B embedding rows ((2P-1)K+1 per sequence: K
+    candidate rows B(.) at each of P positions, K predecessor rows A(.) at
+    P-1 positions plus prev_tok's row), and the outputs."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    logits = wl.B * wl.P * wl.V * esz
+    hidden = wl.B * wl.P * wl.d * esz
+    w = wl.r * wl.d * esz
+    rows = wl.B * ((2 * wl.P - 1) * wl.K + 1) * wl.r * esz
+    out = wl.B * wl.P * 4 + wl.B * 4
+    return logits + hidden + w + rows + out
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "draft_selection_topk16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def time_workload(wl, steps: int, warmup: int, rotate_mb: float):
+    import torch
+    import draft_selection_topk16_amd as df2
+    from draft_selection_topk16_amd import synth
+    import numpy as np
+
+    t0 = time.perf_counter()
+    x = synth.make_inputs(wl)
+    log("  inputs for %s drawn in %.1f s" % (wl.name, time.perf_counter() - t0))
+
+    def dev(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    dt = wl.dtype
+    logits, hidden = dev(x.logits, dt), dev(x.hidden, dt)
+    A, Bt, W = dev(x.A, dt), dev(x.Bt, dt), dev(x.W, dt)
+    prev = torch.from_numpy(x.prev).cuda()
+    per_set = logits.nbytes + hidden.nbytes
+    nsets = max(1, int(math.ceil(rotate_mb * 1e6 / per_set)))
+    sets = [(logits, hidden)] + [(logits.clone(), hidden.clone()) for _ in range(nsets - 1)]
+    calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K) for (l, h) in sets]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        calls[i % nsets]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        calls[(warmup + i) % nsets]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ks = sorted(a.elapsed_time(b) for a, b in ev)      # ms per launch
+    res = dict(ms_per_step=wall * 1e3 / steps,
+               kernel_ms_avg=statistics.fmean(ks),
+               kernel_ms_p10=ks[len(ks) // 10], kernel_ms_p50=ks[len(ks) // 2],
+               kernel_ms_p90=ks[(9 * len(ks)) // 10],
+               rotation_sets=nsets, rotation_mb=nsets * per_set / 1e6)
+    # warm (same buffers every step) for reference only
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[0]()
+    torch.cuda.synchronize()
+    res["warm_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
+    del calls, sets
+    torch.cuda.empty_cache()
+    return x, res
+
+
+def cpu_baseline(x, seconds: float):
+    """The oracle, as it stands, on whole sequences of the workload, one at a
+    time, until `seconds` of CPU work; single-threaded C."""
+    import oracle
+    f = x.f64()
+    B, P = x.wl.B, x.wl.P
+    oracle.select(f["logits"][:1], f["hidden"][:1], f["A"], f["Bt"], f["W"], f["prev"][:1], x.wl.K)
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        b = n % B
+        oracle.select(f["logits"], f["hidden"], f["A"], f["Bt"], f["W"], f["prev"], x.wl.K,
+                      seqs=[b])
+        n += 1
+    el = time.perf_counter() - t0
+    return {"value": n * P / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole sequences (P=%d, V=%d) of the same workload, one at a time, "
+                      "%.1f s" % (n, P, x.wl.V, el)}
+
+
+def copy_calibration(mb: float, reps: int):
+    """A plain device-to-device copy of known size, for scaling counters."""
+    import torch
+    n = int(mb * 1e6) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": a.nbytes, "copy_bytes_written": b.nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="t27b_b32")
+    ap.add_argument("--b1-workload", default="qwen3_4b_b1")
+    ap.add_argument("--rotate-mb", type=float, default=600.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-b1", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the selector runs per sequence with no "
+              "cross-GPU exchange, and this build has no multi-GPU path (--gpus %d refused)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration_mb > 0:
+        copy_calibration(args.copy_calibration_mb, args.steps)
+        return
+
+    from draft_selection_topk16_amd import synth
+    import draft_selection_topk16_amd as df2
+    df2.load()
+
+    wl = synth.WORKLOADS[args.workload]
+    log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
+    x, res = time_workload(wl, args.steps, args.warmup, args.rotate_mb)
+    pos_per_s = wl.B * wl.P / (res["ms_per_step"] * 1e-3)
+    abytes = algorithmic_bytes(wl)
+    achieved = abytes / (res["kernel_ms_avg"] * 1e-3) / 1e9
+    log("  %.2f us/step wall, %.2f us/launch (events), %.0f GB/s algorithmic"
+        % (res["ms_per_step"] * 1e3, res["kernel_ms_avg"] * 1e3, achieved))
+
+    out = {
+        "metric": METRIC,
+        "value": pos_per_s,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d P=%d V=%d d=%d K=%d r=%d %s logits/hidden/tables, "
+                               "fp32 accumulation" % (wl.name, wl.B, wl.P, wl.V, wl.d, wl.K, wl.r, wl.dtype),
+                   "B": wl.B, "P": wl.P, "V": wl.V, "d": wl.d, "K": wl.K, "r": wl.r,
+                   "parallelism": "single-gpu"},
+        "us_per_cycle": res["ms_per_step"] * 1e3,
+        "hbm_frac": achieved / HBM_PEAK_GBS,
+        "timing": res,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(wl.name),
+                     "kernel": "k_select (fused selector)",
+                     "algorithmic_bytes_per_launch": abytes},
+    }
+    if not args.no_b1:
+        wl1 = synth.WORKLOADS[args.b1_workload]
+        log("timing %s" % wl1.name)
+        _, r1 = time_workload(wl1, args.steps, args.warmup, args.rotate_mb)
+        ab1 = algorithmic_bytes(wl1)
+        out["b1"] = {"workload": "%s: B=%d P=%d V=%d d=%d K=%d" % (wl1.name, wl1.B, wl1.P, wl1.V, wl1.d, wl1.K),
+                     "us_per_cycle": r1["ms_per_step"] * 1e3,
+                     "kernel_us_avg": r1["kernel_ms_avg"] * 1e3,
+                     "positions_per_s": wl1.B * wl1.P / (r1["ms_per_step"] * 1e-3),
+                     "hbm_frac": ab1 / (r1["kernel_ms_avg"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "timing": r1}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle for %.0f s" % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) DFlash 2 path selector.
+
+The compute path is the HIP library libdflash2.so (C ABI: include/dflash2.h);
+`binding` marshals torch tensors into it.  `synth` draws seeded synthetic
+inputs.  Importing the package does not load the library: the first call
+does, and raises if it has not been built.
+"""
+from .binding import (PreparedSelect, SelectorError, device_error, load, pair_scores, project,
+                      release, select, topk, version, viterbi)
+
+__all__ = ["PreparedSelect", "SelectorError", "device_error", "load", "pair_scores", "project", "release",
+           "select", "topk", "version", "viterbi"]

@@ -1,0 +1,220 @@
+"""ctypes binding of libdflash2.so (the C ABI in include/dflash2.h).
+
+Argument marshalling only: every step of the selector runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the stream.  If
+the library has not been built, every call raises; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdflash2.so")
+
+DF2_F32 = 0
+DF2_BF16 = 1
+
+EXPORTED = (
+    "dflash2_select", "dflash2_topk", "dflash2_project", "dflash2_pair_scores",
+    "dflash2_viterbi", "dflash2_device_error", "dflash2_release",
+    "dflash2_status_string", "dflash2_last_error", "dflash2_version",
+)
+
+
+class SelectorError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("P", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("r", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libdflash2.so is not built; run `python -m draft_selection_topk16_amd.build` "
+            "(the selector has no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32)
+    dp = ctypes.POINTER(Dims)
+    sig = {
+        "dflash2_select": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
+        "dflash2_topk": [vp, i64, i32, ctypes.c_int, i32, vp, vp, vp],
+        "dflash2_project": [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp],
+        "dflash2_pair_scores": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp],
+        "dflash2_viterbi": [vp, vp, i32, i32, i32, vp, vp, vp],
+        "dflash2_device_error": [vp, u32p],
+        "dflash2_release": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    for name in ("dflash2_status_string",):
+        getattr(lib, name).argtypes = [ctypes.c_int]
+        getattr(lib, name).restype = ctypes.c_char_p
+    for name in ("dflash2_last_error", "dflash2_version"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        msg = "%s: %s" % (lib.dflash2_status_string(status).decode(),
+                          lib.dflash2_last_error().decode())
+        raise SelectorError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DF2_BF16
+    if t.dtype == torch.float32:
+        return DF2_F32
+    raise TypeError("expected bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class PreparedSelect:
+    """The checked arguments of one dflash2_select call, for repeated
+    launches with little host overhead (the tensors are kept alive and must
+    not be reallocated).  Calling it enqueues one launch on the stream that
+    was current when it was prepared."""
+
+    def __init__(self, logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor,
+                 Bt: torch.Tensor, W: torch.Tensor, prev: torch.Tensor, K: int,
+                 out_path: Optional[torch.Tensor] = None,
+                 out_score: Optional[torch.Tensor] = None):
+        lib = load()
+        B, P, V = logits.shape
+        d = hidden.shape[-1]
+        r = A.shape[-1]
+        dt = _dtype_code(logits)
+        for name, t in (("hidden", hidden), ("A", A), ("Bt", Bt), ("W", W)):
+            if t.dtype != logits.dtype:
+                raise TypeError("%s must have the logits dtype" % name)
+        if (hidden.shape != (B, P, d) or A.shape != (V, r) or Bt.shape != (V, r)
+                or W.shape != (r, d)):
+            raise ValueError("inconsistent shapes")
+        if prev.dtype != torch.int32 or prev.shape != (B,):
+            raise ValueError("prev must be int32 [B]")
+        if out_path is None:
+            out_path = torch.empty((B, P), dtype=torch.int32, device=logits.device)
+        if out_score is None:
+            out_score = torch.empty((B,), dtype=torch.float32, device=logits.device)
+        self.out_path, self.out_score = out_path, out_score
+        self._keep = (logits, hidden, A, Bt, W, prev)
+        self._dims = Dims(B, P, V, d, r, dt)
+        self._fn = lib.dflash2_select
+        self._args = (ctypes.byref(self._dims), _dev(logits, "logits"), _dev(hidden, "hidden"),
+                      _dev(A, "A"), _dev(Bt, "Bt"), _dev(W, "W"), _dev(prev, "prev"), int(K),
+                      _dev(out_path, "out_path"), _dev(out_score, "out_score"),
+                      _stream(logits.device))
+
+    def __call__(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        _check(self._fn(*self._args))
+        return self.out_path, self.out_score
+
+
+def select(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torch.Tensor,
+           W: torch.Tensor, prev: torch.Tensor, K: int,
+           out_path: Optional[torch.Tensor] = None,
+           out_score: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Selected path [B, P] int32 and its score [B] float32 (one launch)."""
+    return PreparedSelect(logits, hidden, A, Bt, W, prev, K, out_path, out_score)()
+
+
+def topk(logits: torch.Tensor, K: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-K of each row of logits[..., V]: (idx int32, val float32)."""
+    lib = load()
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    idx = torch.empty(logits.shape[:-1] + (K,), dtype=torch.int32, device=logits.device)
+    val = torch.empty(logits.shape[:-1] + (K,), dtype=torch.float32, device=logits.device)
+    _check(lib.dflash2_topk(_dev(logits, "logits"), rows, V, _dtype_code(logits), int(K),
+                            _dev(idx, "idx"), _dev(val, "val"), _stream(logits.device)))
+    return idx, val
+
+
+def project(hidden: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
+    """H[..., q] = sum_m W[q, m] hidden[..., m], float32."""
+    lib = load()
+    r, d = W.shape
+    M = hidden.numel() // d
+    if W.dtype != hidden.dtype:
+        raise TypeError("W must have the hidden dtype")
+    H = torch.empty(hidden.shape[:-1] + (r,), dtype=torch.float32, device=hidden.device)
+    _check(lib.dflash2_project(_dev(hidden, "hidden"), _dev(W, "W"), M, d, r,
+                               _dtype_code(hidden), _dev(H, "H"), _stream(hidden.device)))
+    return H
+
+
+def pair_scores(cand: torch.Tensor, cval: torch.Tensor, H: torch.Tensor, A: torch.Tensor,
+                Bt: torch.Tensor, prev: torch.Tensor) -> torch.Tensor:
+    """S [B, P, K, K] float32 from candidates [B, P, K], gates H [B, P, r]."""
+    lib = load()
+    B, P, K = cand.shape
+    V, r = A.shape
+    dims = Dims(B, P, V, 32, r, _dtype_code(A))
+    S = torch.empty((B, P, K, K), dtype=torch.float32, device=cand.device)
+    _check(lib.dflash2_pair_scores(ctypes.byref(dims), _dev(cand, "cand"), _dev(cval, "cval"),
+                                   _dev(H, "H"), _dev(A, "A"), _dev(Bt, "Bt"), _dev(prev, "prev"),
+                                   int(K), _dev(S, "S"), _stream(cand.device)))
+    return S
+
+
+def viterbi(S: torch.Tensor, cand: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Walk over S [B, P, K, K]: (path [B, P] int32, score [B] float32)."""
+    lib = load()
+    B, P, K = cand.shape
+    path = torch.empty((B, P), dtype=torch.int32, device=S.device)
+    score = torch.empty((B,), dtype=torch.float32, device=S.device)
+    _check(lib.dflash2_viterbi(_dev(S, "S"), _dev(cand, "cand"), B, P, K, _dev(path, "path"),
+                               _dev(score, "score"), _stream(S.device)))
+    return path, score
+
+
+def device_error(device: Optional[torch.device] = None) -> int:
+    """Waits for the current stream; returns and clears its device input flags."""
+    lib = load()
+    flags = ctypes.c_uint32(0)
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    _check(lib.dflash2_device_error(_stream(dev), ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def release() -> None:
+    _check(load().dflash2_release())
+
+
+def version() -> str:
+    return load().dflash2_version().decode()

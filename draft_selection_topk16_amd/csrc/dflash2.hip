@@ -1,0 +1,666 @@
+// MI355X (gfx950) DFlash 2 path selector: kernels and the C ABI declared in
+// include/dflash2.h.
+//
+// The selector ("DFlash 2: Keep Drafting Parallel", section "A Lightweight
+// Path Selector") keeps the top-K candidates per draft position, scores every
+// adjacent pair with S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, and walks
+// the scores once from the last verified token.
+//
+// dflash2_select runs everything in ONE launch.  The grid holds two kinds of
+// workgroups that run side by side:
+//   * gate workgroups (the first n_proj): one slice of one H tile each;
+//   * chunk workgroups: one vocabulary chunk of one logits row each.
+// Work that needs several workgroups' results is done by whichever of them
+// arrives last on a counter (no workgroup ever waits for another):
+//   * the last chunk of a row merges the row's candidates;
+//   * the last slice of an H tile sums the slices;
+//   * the last of a sequence's row merges and H tiles runs the pair scores
+//     and the walk for that sequence.
+// Counters live in the scratch buffer and are reset by the workgroup that
+// consumes them, so every launch starts from zero without a memset.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "dflash2.h"
+#include "common.hpp"
+#include "project.hpp"
+#include "tail.hpp"
+#include "topk.hpp"
+
+using namespace df2;
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// Launch description shared by the kernels (passed by value).
+// ----------------------------------------------------------------------------
+struct Params {
+    const void* logits;
+    const void* hidden;
+    const void* A;
+    const void* Bt;
+    const void* W;
+    const int32_t* prev;
+    int32_t* out_path;
+    float* out_score;
+    // scratch
+    uint64_t* part;       // [rows, C, K] candidate words
+    int32_t* cand;        // [rows, K]
+    float* cval;          // [rows, K]
+    float* ppart;         // [S, M, r] gate partials (S > 1)
+    float* H;             // [M, r]
+    uint32_t* err;        // device input-error flags
+    uint32_t* row_cnt;    // [rows]
+    uint32_t* tile_cnt;   // [mtiles * qtiles]
+    uint32_t* seq_cnt;    // [B]
+    // sizes
+    int B, P, V, d, r, K;
+    int64_t rows;
+    int C;                // chunks per row
+    int aligned;          // logits rows are 16-byte aligned and V % per-vector == 0
+    int mtiles, qtiles, S, n_proj;
+};
+
+union SharedAll {
+    ChunkLds c;
+    MergeLds m;
+    ProjLds p;
+    TailLds t;
+};
+
+__device__ __forceinline__ TailArgs tail_args(const Params& p) {
+    TailArgs a;
+    a.cand = p.cand;
+    a.cval = p.cval;
+    a.H = p.H;
+    a.A = p.A;
+    a.Bt = p.Bt;
+    a.prev = p.prev;
+    a.in_S = nullptr;
+    a.out_S = nullptr;
+    a.out_path = p.out_path;
+    a.out_score = p.out_score;
+    a.err = p.err;
+    a.P = p.P;
+    a.V = p.V;
+    a.r = p.r;
+    a.K = p.K;
+    return a;
+}
+
+// Arrivals a sequence waits for: its P row merges plus every H tile that
+// covers one of its rows.
+__device__ __forceinline__ uint32_t seq_expected(const Params& p, int b) {
+    const int lo = b * p.P, hi = b * p.P + p.P - 1;
+    const int n_mt = hi / 16 - lo / 16 + 1;
+    return (uint32_t)(p.P + p.qtiles * n_mt);
+}
+
+template <bool BF16, int NV>
+__device__ void chunk_role(const Params& p, int64_t cb, bool fused, SharedAll& sm,
+                           uint32_t* flag) {
+    const int64_t row = cb / p.C;
+    const int chunk = (int)(cb % p.C);
+    const size_t esz = BF16 ? 2 : 4;
+    const char* rowp = reinterpret_cast<const char*>(p.logits) + (size_t)row * p.V * esz;
+    chunk_topk<BF16, NV>(rowp, p.V, chunk, p.K, p.aligned != 0,
+                         p.part + ((size_t)row * p.C + chunk) * p.K, sm.c);
+    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.C, flag)) return;
+    merge_row<BF16>(p.part + (size_t)row * p.C * p.K, p.C, p.K, p.cand + row * p.K,
+                    p.cval + row * p.K, sm.m);
+    if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
+    if (!fused) return;
+    const int b = (int)(row / p.P);
+    if (!block_arrive_last(&p.seq_cnt[b], seq_expected(p, b), flag)) return;
+    tail_seq<BF16>(tail_args(p), b, kTailFull, sm.t);
+    if (threadIdx.x == 0) reset_counter(&p.seq_cnt[b]);
+}
+
+template <bool BF16, int NQ>
+__device__ void proj_role(const Params& p, int pb, bool fused, SharedAll& sm, uint32_t* flag) {
+    const int s = pb % p.S, tile = pb / p.S;
+    const int mt = tile / p.qtiles, qt = tile % p.qtiles;
+    const int M = (int)p.rows;
+    proj_block<BF16, NQ>(p.hidden, p.W, M, p.d, p.r, mt, qt, s, p.S,
+                         p.S > 1 ? p.ppart : p.H, sm.p);
+    if (p.S > 1) {
+        if (!block_arrive_last(&p.tile_cnt[tile], (uint32_t)p.S, flag)) return;
+        proj_reduce_tile<NQ>(p.ppart, M, p.r, mt, qt, p.S, p.H);
+        if (threadIdx.x == 0) reset_counter(&p.tile_cnt[tile]);
+    }
+    if (!fused) return;
+    const int b_lo = (mt * 16) / p.P;
+    const int b_hi = (min(M, mt * 16 + 16) - 1) / p.P;
+    for (int b = b_lo; b <= b_hi; ++b) {
+        if (block_arrive_last(&p.seq_cnt[b], seq_expected(p, b), flag)) {
+            tail_seq<BF16>(tail_args(p), b, kTailFull, sm.t);
+            if (threadIdx.x == 0) reset_counter(&p.seq_cnt[b]);
+        }
+    }
+}
+
+// The whole selector in one launch.
+template <bool BF16, int NV, int NQ>
+__global__ __launch_bounds__(kWG) void k_select(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    const int64_t g = blockIdx.x;
+    if (g < p.n_proj) {
+        proj_role<BF16, NQ>(p, (int)g, true, sm, &flag);
+    } else {
+        chunk_role<BF16, NV>(p, g - p.n_proj, true, sm, &flag);
+    }
+}
+
+// Top-K alone: chunk workgroups with the row merge on last arrival.
+template <bool BF16, int NV>
+__global__ __launch_bounds__(kWG) void k_topk(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    chunk_role<BF16, NV>(p, blockIdx.x, false, sm, &flag);
+}
+
+// Gate projection alone.
+template <bool BF16, int NQ>
+__global__ __launch_bounds__(kWG) void k_project(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    proj_role<BF16, NQ>(p, blockIdx.x, false, sm, &flag);
+}
+
+// Pair scores alone (written to global memory), or the walk alone.
+template <bool BF16>
+__global__ __launch_bounds__(kWG) void k_tail(TailArgs a, int mode) {
+    __shared__ TailLds sm;
+    tail_seq<BF16>(a, blockIdx.x, mode, sm);
+}
+
+// ----------------------------------------------------------------------------
+// Host side.
+// ----------------------------------------------------------------------------
+thread_local std::string g_last_error;
+
+df2_status fail(df2_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+df2_status hip_fail(hipError_t e, const char* what) {
+    return fail(DF2_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+struct Scratch {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    size_t zeroed_counter_bytes = 0;   // prefix known to hold only zeros
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+// Scratch of at least `bytes`, whose first `counter_bytes` are zero when the
+// stream reaches the next launch.
+df2_status get_scratch(hipStream_t stream, size_t bytes, size_t counter_bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    Scratch& s = g_scratch[std::make_pair(dev, stream)];
+    if (s.bytes < bytes) {
+        if (s.ptr) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(s.ptr);
+            s.ptr = nullptr;
+            s.bytes = 0;
+        }
+        size_t nb = align_up(std::max(bytes, (size_t)1 << 20), (size_t)1 << 20);
+        e = hipMalloc(&s.ptr, nb);
+        if (e != hipSuccess) {
+            s.ptr = nullptr;
+            return fail(DF2_ENOMEM, std::string("hipMalloc scratch: ") + hipGetErrorString(e));
+        }
+        e = hipMemset(s.ptr, 0, nb);
+        if (e != hipSuccess) return hip_fail(e, "hipMemset scratch");
+        s.bytes = nb;
+        s.zeroed_counter_bytes = nb;
+    }
+    if (s.zeroed_counter_bytes < counter_bytes) {
+        e = hipMemsetAsync(s.ptr, 0, counter_bytes, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync counters");
+        s.zeroed_counter_bytes = counter_bytes;
+    }
+    *out = s.ptr;
+    return DF2_OK;
+}
+
+// Later layouts may put data where earlier ones kept counters: remember that
+// only the counter prefix of the latest layout is known to be zero.
+void note_layout(hipStream_t stream, size_t counter_bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_scratch.find(std::make_pair(dev, stream));
+    if (it != g_scratch.end()) it->second.zeroed_counter_bytes = counter_bytes;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+struct Plan {
+    Params p;
+    int nv = 1, nq = 1;
+    bool bf16 = true;
+    int64_t n_chunk_blocks = 0;
+    size_t counter_bytes = 0, total_bytes = 0;
+    size_t off_part = 0, off_cand = 0, off_cval = 0, off_ppart = 0, off_H = 0;
+};
+
+// Chunk size: the largest that still gives every CU several workgroups, and
+// small enough that a row's merge fits the registers of one workgroup.
+int choose_nv(int64_t rows, int V, int K, bool bf16) {
+    const int pv = bf16 ? 8 : 4;
+    int forced = env_int("DF2_NV", 0);
+    auto chunks = [&](int nv) { return (int64_t)((V + (int64_t)kWG * pv * nv - 1) / ((int64_t)kWG * pv * nv)); };
+    auto fits = [&](int nv) { return chunks(nv) * K <= (int64_t)kWG * kMergeItems; };
+    if (forced == 1 || forced == 2 || forced == 4 || forced == 8) {
+        if (fits(forced)) return forced;
+    }
+    const int opts[4] = {8, 4, 2, 1};
+    for (int nv : opts)
+        if (fits(nv) && rows * chunks(nv) >= 1024) return nv;
+    for (int nv : {1, 2, 4, 8})
+        if (fits(nv)) return nv;
+    return -1;
+}
+
+void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits) {
+    Params& p = pl.p;
+    pl.bf16 = bf16;
+    const int pv = bf16 ? 8 : 4;
+    pl.nv = choose_nv(rows, V, K, bf16);
+    const int64_t ce = (int64_t)kWG * pv * std::max(pl.nv, 1);
+    p.C = (int)((V + ce - 1) / ce);
+    p.rows = rows;
+    p.V = V;
+    p.K = K;
+    p.aligned = (aligned16(logits) && (V % pv) == 0) ? 1 : 0;
+    pl.n_chunk_blocks = rows * p.C;
+}
+
+void plan_proj(Plan& pl, int64_t M, int d, int r) {
+    Params& p = pl.p;
+    pl.nq = (M >= 64) ? 4 : 1;
+    int forced_nq = env_int("DF2_NQ", 0);
+    if (forced_nq == 1 || forced_nq == 4) pl.nq = forced_nq;
+    p.mtiles = (int)((M + 15) / 16);
+    p.qtiles = r / (16 * pl.nq);
+    const int tiles = p.mtiles * p.qtiles;
+    const int KS = d / 32;
+    int S = 1;
+    while (S < 8 && tiles * S < 256 && KS >= 2 * S * kWaves) S *= 2;
+    int forced_s = env_int("DF2_S", 0);
+    if (forced_s >= 1 && forced_s <= KS) S = forced_s;
+    p.S = S;
+    p.n_proj = tiles * S;
+    p.d = d;
+    p.r = r;
+}
+
+// Scratch layout: counters first (err, rows, tiles, sequences), then data.
+void plan_layout(Plan& pl, int64_t rows, int64_t M, int B) {
+    Params& p = pl.p;
+    const size_t ncnt = 1 + (size_t)rows + (size_t)p.mtiles * p.qtiles + (size_t)B;
+    pl.counter_bytes = align_up(ncnt * 4, 256);
+    size_t off = pl.counter_bytes;
+    pl.off_part = off;
+    off = align_up(off + (size_t)rows * p.C * p.K * 8, 256);
+    pl.off_cand = off;
+    off = align_up(off + (size_t)rows * p.K * 4, 256);
+    pl.off_cval = off;
+    off = align_up(off + (size_t)rows * p.K * 4, 256);
+    pl.off_ppart = off;
+    off = align_up(off + (p.S > 1 ? (size_t)p.S * M * p.r * 4 : 0), 256);
+    pl.off_H = off;
+    off = align_up(off + (size_t)M * p.r * 4, 256);
+    pl.total_bytes = off;
+}
+
+void bind_scratch(Plan& pl, void* base, int64_t rows, int B) {
+    Params& p = pl.p;
+    char* c = reinterpret_cast<char*>(base);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(c);
+    p.err = cnt;
+    p.row_cnt = cnt + 1;
+    p.tile_cnt = cnt + 1 + rows;
+    p.seq_cnt = cnt + 1 + rows + (size_t)p.mtiles * p.qtiles;
+    (void)B;
+    p.part = reinterpret_cast<uint64_t*>(c + pl.off_part);
+    p.cand = reinterpret_cast<int32_t*>(c + pl.off_cand);
+    p.cval = reinterpret_cast<float*>(c + pl.off_cval);
+    p.ppart = reinterpret_cast<float*>(c + pl.off_ppart);
+    p.H = reinterpret_cast<float*>(c + pl.off_H);
+}
+
+df2_status check_dims(const df2_dims* dims, bool need_d) {
+    if (!dims) return fail(DF2_EINVAL, "dims is NULL");
+    if (dims->dtype != DF2_F32 && dims->dtype != DF2_BF16) return fail(DF2_EINVAL, "unknown dtype");
+    if (dims->B < 0) return fail(DF2_EINVAL, "B < 0");
+    if (dims->P < 1 || dims->P > kMaxP) return fail(DF2_EINVAL, "P must be in [1, 64]");
+    if (dims->V < 1) return fail(DF2_EINVAL, "V < 1");
+    if (need_d && (dims->d < 32 || dims->d % 32 != 0))
+        return fail(DF2_EUNSUPPORTED, "d must be a positive multiple of 32");
+    if (dims->r < 64 || dims->r % 64 != 0 || dims->r > 1024)
+        return fail(DF2_EUNSUPPORTED, "r must be a multiple of 64 in [64, 1024]");
+    return DF2_OK;
+}
+
+df2_status check_k(int K, int V) {
+    if (K < 1 || K > kMaxK || K > V) return fail(DF2_EINVAL, "K must be in [1, min(V, 64)]");
+    return DF2_OK;
+}
+
+template <typename F>
+df2_status launch_checked(F&& f, const char* what) {
+    f();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, what);
+    return DF2_OK;
+}
+
+#define DF2_NV_CASES(BF, NQ_)                                                        \
+    switch (pl.nv) {                                                                 \
+        case 1: hipLaunchKernelGGL((k_select<BF, 1, NQ_>), grid, block, 0, stream, pl.p); break; \
+        case 2: hipLaunchKernelGGL((k_select<BF, 2, NQ_>), grid, block, 0, stream, pl.p); break; \
+        case 4: hipLaunchKernelGGL((k_select<BF, 4, NQ_>), grid, block, 0, stream, pl.p); break; \
+        default: hipLaunchKernelGGL((k_select<BF, 8, NQ_>), grid, block, 0, stream, pl.p); break; \
+    }
+
+void launch_select(const Plan& pl, hipStream_t stream) {
+    dim3 grid((unsigned)(pl.p.n_proj + pl.n_chunk_blocks)), block(kWG);
+    if (pl.bf16) {
+        if (pl.nq == 4) { DF2_NV_CASES(true, 4) } else { DF2_NV_CASES(true, 1) }
+    } else {
+        if (pl.nq == 4) { DF2_NV_CASES(false, 4) } else { DF2_NV_CASES(false, 1) }
+    }
+}
+
+void launch_topk(const Plan& pl, hipStream_t stream) {
+    dim3 grid((unsigned)pl.n_chunk_blocks), block(kWG);
+#define DF2_TOPK(BF)                                                                          \
+    switch (pl.nv) {                                                                          \
+        case 1: hipLaunchKernelGGL((k_topk<BF, 1>), grid, block, 0, stream, pl.p); break;   \
+        case 2: hipLaunchKernelGGL((k_topk<BF, 2>), grid, block, 0, stream, pl.p); break;   \
+        case 4: hipLaunchKernelGGL((k_topk<BF, 4>), grid, block, 0, stream, pl.p); break;   \
+        default: hipLaunchKernelGGL((k_topk<BF, 8>), grid, block, 0, stream, pl.p); break;  \
+    }
+    if (pl.bf16) { DF2_TOPK(true) } else { DF2_TOPK(false) }
+#undef DF2_TOPK
+}
+
+void launch_project(const Plan& pl, hipStream_t stream) {
+    dim3 grid((unsigned)pl.p.n_proj), block(kWG);
+    if (pl.bf16) {
+        if (pl.nq == 4) hipLaunchKernelGGL((k_project<true, 4>), grid, block, 0, stream, pl.p);
+        else hipLaunchKernelGGL((k_project<true, 1>), grid, block, 0, stream, pl.p);
+    } else {
+        if (pl.nq == 4) hipLaunchKernelGGL((k_project<false, 4>), grid, block, 0, stream, pl.p);
+        else hipLaunchKernelGGL((k_project<false, 1>), grid, block, 0, stream, pl.p);
+    }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+extern "C" {
+
+const char* dflash2_version(void) { return "0.1.0"; }
+
+const char* dflash2_status_string(df2_status s) {
+    switch (s) {
+        case DF2_OK: return "ok";
+        case DF2_EINVAL: return "invalid argument";
+        case DF2_EUNSUPPORTED: return "unsupported argument";
+        case DF2_EHIP: return "HIP error";
+        case DF2_ENOMEM: return "out of device memory";
+    }
+    return "unknown status";
+}
+
+const char* dflash2_last_error(void) { return g_last_error.c_str(); }
+
+df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* hidden,
+                          const void* A_tab, const void* B_tab, const void* W_H,
+                          const int32_t* prev_tok, int32_t K, int32_t* out_path,
+                          float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    df2_status st = check_dims(dims, true);
+    if (st != DF2_OK) return st;
+    if ((st = check_k(K, dims->V)) != DF2_OK) return st;
+    if (dims->B == 0) return DF2_OK;
+    if (!logits || !hidden || !A_tab || !B_tab || !W_H || !prev_tok || !out_path || !out_score)
+        return fail(DF2_EINVAL, "NULL pointer argument");
+    if (!aligned16(hidden) || !aligned16(A_tab) || !aligned16(B_tab) || !aligned16(W_H))
+        return fail(DF2_EINVAL, "hidden, A_tab, B_tab and W_H must be 16-byte aligned");
+    if (((uintptr_t)prev_tok & 3u) || ((uintptr_t)out_path & 3u) || ((uintptr_t)out_score & 3u))
+        return fail(DF2_EINVAL, "prev_tok, out_path and out_score must be 4-byte aligned");
+    const bool bf16 = dims->dtype == DF2_BF16;
+    if (!bf16 && ((uintptr_t)logits & 3u)) return fail(DF2_EINVAL, "fp32 logits must be 4-byte aligned");
+    if (bf16 && ((uintptr_t)logits & 1u)) return fail(DF2_EINVAL, "bf16 logits must be 2-byte aligned");
+    const int64_t rows = (int64_t)dims->B * dims->P;
+    Plan pl;
+    std::memset(&pl.p, 0, sizeof(pl.p));
+    plan_topk(pl, rows, dims->V, K, bf16, logits);
+    if (pl.nv < 0) return fail(DF2_EUNSUPPORTED, "V * K too large for the row merge");
+    plan_proj(pl, rows, dims->d, dims->r);
+    plan_layout(pl, rows, rows, dims->B);
+    Params& p = pl.p;
+    p.logits = logits;
+    p.hidden = hidden;
+    p.A = A_tab;
+    p.Bt = B_tab;
+    p.W = W_H;
+    p.prev = prev_tok;
+    p.out_path = out_path;
+    p.out_score = out_score;
+    p.B = dims->B;
+    p.P = dims->P;
+    void* base = nullptr;
+    if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
+    note_layout(stream, pl.counter_bytes);
+    bind_scratch(pl, base, rows, dims->B);
+    return launch_checked([&] { launch_select(pl, stream); }, "dflash2_select launch");
+}
+
+df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V, df2_dtype dtype, int32_t K,
+                        int32_t* out_idx, float* out_val, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != DF2_F32 && dtype != DF2_BF16) return fail(DF2_EINVAL, "unknown dtype");
+    if (rows < 0) return fail(DF2_EINVAL, "rows < 0");
+    if (V < 1) return fail(DF2_EINVAL, "V < 1");
+    df2_status st = check_k(K, V);
+    if (st != DF2_OK) return st;
+    if (rows == 0) return DF2_OK;
+    if (!logits || !out_idx || !out_val) return fail(DF2_EINVAL, "NULL pointer argument");
+    const bool bf16 = dtype == DF2_BF16;
+    if (((uintptr_t)out_idx & 3u) || ((uintptr_t)out_val & 3u))
+        return fail(DF2_EINVAL, "outputs must be 4-byte aligned");
+    if ((bf16 && ((uintptr_t)logits & 1u)) || (!bf16 && ((uintptr_t)logits & 3u)))
+        return fail(DF2_EINVAL, "logits misaligned for its dtype");
+    Plan pl;
+    std::memset(&pl.p, 0, sizeof(pl.p));
+    plan_topk(pl, rows, V, K, bf16, logits);
+    if (pl.nv < 0) return fail(DF2_EUNSUPPORTED, "V * K too large for the row merge");
+    if (pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "too many rows");
+    pl.p.mtiles = 0;
+    pl.p.qtiles = 0;
+    pl.p.S = 1;
+    pl.p.r = 0;
+    plan_layout(pl, rows, 0, 0);
+    Params& p = pl.p;
+    p.logits = logits;
+    p.P = 1;
+    void* base = nullptr;
+    if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
+    note_layout(stream, pl.counter_bytes);
+    bind_scratch(pl, base, rows, 0);
+    // results go straight to the caller's buffers
+    p.cand = out_idx;
+    p.cval = out_val;
+    return launch_checked([&] { launch_topk(pl, stream); }, "dflash2_topk launch");
+}
+
+df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M, int32_t d, int32_t r,
+                           df2_dtype dtype, float* out_H, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != DF2_F32 && dtype != DF2_BF16) return fail(DF2_EINVAL, "unknown dtype");
+    if (M < 0) return fail(DF2_EINVAL, "M < 0");
+    if (d < 32 || d % 32 != 0) return fail(DF2_EUNSUPPORTED, "d must be a positive multiple of 32");
+    if (r < 64 || r % 64 != 0 || r > 1024)
+        return fail(DF2_EUNSUPPORTED, "r must be a multiple of 64 in [64, 1024]");
+    if (M == 0) return DF2_OK;
+    if (M > (1 << 24)) return fail(DF2_EUNSUPPORTED, "M too large");
+    if (!hidden || !W_H || !out_H) return fail(DF2_EINVAL, "NULL pointer argument");
+    if (!aligned16(hidden) || !aligned16(W_H) || ((uintptr_t)out_H & 3u))
+        return fail(DF2_EINVAL, "hidden and W_H must be 16-byte aligned, out_H 4-byte");
+    Plan pl;
+    std::memset(&pl.p, 0, sizeof(pl.p));
+    pl.bf16 = dtype == DF2_BF16;
+    plan_proj(pl, M, d, r);
+    pl.p.C = 0;
+    pl.p.K = 0;
+    plan_layout(pl, 0, M, 0);
+    Params& p = pl.p;
+    p.rows = M;
+    p.hidden = hidden;
+    p.W = W_H;
+    void* base = nullptr;
+    df2_status st;
+    if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
+    note_layout(stream, pl.counter_bytes);
+    bind_scratch(pl, base, 0, 0);
+    p.H = out_H;
+    return launch_checked([&] { launch_project(pl, stream); }, "dflash2_project launch");
+}
+
+df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
+                               const float* cand_val, const float* H, const void* A_tab,
+                               const void* B_tab, const int32_t* prev_tok, int32_t K,
+                               float* out_S, hipStream_t stream) {
+    g_last_error.clear();
+    df2_status st = check_dims(dims, false);
+    if (st != DF2_OK) return st;
+    if ((st = check_k(K, dims->V)) != DF2_OK) return st;
+    if (dims->B == 0) return DF2_OK;
+    if (!cand_idx || !cand_val || !H || !A_tab || !B_tab || !prev_tok || !out_S)
+        return fail(DF2_EINVAL, "NULL pointer argument");
+    if (!aligned16(H) || !aligned16(A_tab) || !aligned16(B_tab))
+        return fail(DF2_EINVAL, "H, A_tab and B_tab must be 16-byte aligned");
+    void* base = nullptr;
+    if ((st = get_scratch(stream, 256, 4, &base)) != DF2_OK) return st;
+    TailArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.cand = cand_idx;
+    a.cval = cand_val;
+    a.H = H;
+    a.A = A_tab;
+    a.Bt = B_tab;
+    a.prev = prev_tok;
+    a.out_S = out_S;
+    a.err = reinterpret_cast<uint32_t*>(base);
+    a.P = dims->P;
+    a.V = dims->V;
+    a.r = dims->r;
+    a.K = K;
+    dim3 grid((unsigned)dims->B), block(kWG);
+    return launch_checked([&] {
+        if (dims->dtype == DF2_BF16)
+            hipLaunchKernelGGL((k_tail<true>), grid, block, 0, stream, a, (int)kTailScoresOnly);
+        else
+            hipLaunchKernelGGL((k_tail<false>), grid, block, 0, stream, a, (int)kTailScoresOnly);
+    }, "dflash2_pair_scores launch");
+}
+
+df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,
+                           int32_t K, int32_t* out_path, float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    if (B < 0) return fail(DF2_EINVAL, "B < 0");
+    if (P < 1 || P > kMaxP) return fail(DF2_EINVAL, "P must be in [1, 64]");
+    if (K < 1 || K > kMaxK) return fail(DF2_EINVAL, "K must be in [1, 64]");
+    if (B == 0) return DF2_OK;
+    if (!S || !cand_idx || !out_path || !out_score) return fail(DF2_EINVAL, "NULL pointer argument");
+    TailArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.cand = cand_idx;
+    a.in_S = S;
+    a.out_path = out_path;
+    a.out_score = out_score;
+    a.P = P;
+    a.K = K;
+    a.V = 0x7FFFFFFF;
+    dim3 grid((unsigned)B), block(kWG);
+    return launch_checked([&] {
+        hipLaunchKernelGGL((k_tail<true>), grid, block, 0, stream, a, (int)kTailWalkOnly);
+    }, "dflash2_viterbi launch");
+}
+
+df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {
+    g_last_error.clear();
+    if (!flags) return fail(DF2_EINVAL, "flags is NULL");
+    *flags = 0;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_scratch.find(std::make_pair(dev, stream));
+        if (it == g_scratch.end()) return DF2_OK;
+        ptr = it->second.ptr;
+    }
+    uint32_t v = 0;
+    if ((e = hipMemcpy(&v, ptr, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy flags");
+    if (v) {
+        const uint32_t zero = 0;
+        if ((e = hipMemcpy(ptr, &zero, 4, hipMemcpyHostToDevice)) != hipSuccess)
+            return hip_fail(e, "hipMemcpy flags");
+    }
+    *flags = v;
+    return DF2_OK;
+}
+
+df2_status dflash2_release(void) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lock(g_mu);
+    df2_status st = DF2_OK;
+    for (auto& kv : g_scratch) {
+        if (!kv.second.ptr) continue;
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(kv.first.first);
+        hipError_t e = hipFree(kv.second.ptr);
+        (void)hipSetDevice(cur);
+        if (e != hipSuccess) st = hip_fail(e, "hipFree");
+    }
+    g_scratch.clear();
+    return st;
+}
+
+}  // extern "C"

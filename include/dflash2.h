@@ -1,0 +1,169 @@
+/*
+ * dflash2.h -- C ABI of the MI355X (gfx950) DFlash 2 path selector.
+ *
+ * The selector is described on the page "DFlash 2: Keep Drafting Parallel",
+ * section "A Lightweight Path Selector": keep the top 16 candidates of the
+ * block drafter at every draft position, score every adjacent candidate pair
+ * with the selector equation
+ *
+ *     S_t(a, b) = U_t(b) + < A(a) (.) H(h_t), B(b) >
+ *
+ * (U_t is the drafter's own logit, A and B are 256-dimensional token
+ * embeddings, H(h_t) a gate computed from the drafter hidden state), and make
+ * one walk over the precomputed scores, starting from the last verified
+ * token.  This library reads H as a bias-free linear map d -> r,
+ * H_t = W_H h_t, and the walk as a max-sum (Viterbi) pass with backtrack.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *    owned by the caller.  The library reads inputs, writes outputs, keeps no
+ *    pointer after the call returns and never frees caller memory.
+ *  - Every tensor is dense row-major (C order), last dimension contiguous.
+ *  - Work is enqueued on `stream` and the call returns without waiting.
+ *  - Scratch memory (top-K partials, gate partials, arrival counters) comes
+ *    from a cache owned by the library, one buffer per (device, stream); it
+ *    grows with hipMalloc outside the launch and is zero-initialised when
+ *    allocated.  Calls on the same stream are ordered; calls on different
+ *    streams use different scratch.  Warm the cache with one call before
+ *    capturing a stream into a HIP graph.
+ *  - Argument errors are found on the host, before any launch: the call
+ *    returns DF2_EINVAL or DF2_EUNSUPPORTED, enqueues nothing, and
+ *    dflash2_last_error() describes the problem.  A failed launch returns
+ *    DF2_EHIP.  Out-of-range token ids read on the device (prev_tok, or a
+ *    caller's cand_idx, outside [0, V)) are replaced by token 0 and raise a
+ *    device flag that dflash2_device_error() reports.
+ *  - Non-finite logits (NaN) are outside the contract; +-inf are ordered.
+ *  - Top-K order: value descending; equal values (IEEE, -0 == +0) go to the
+ *    lower vocabulary index.  Walk ties go to the smaller predecessor rank,
+ *    the final pick to the smaller rank.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logits, hidden, A_tab, B_tab and W_H (all the same). */
+typedef enum { DF2_F32 = 0, DF2_BF16 = 1 } df2_dtype;
+
+typedef enum {
+    DF2_OK = 0,
+    DF2_EINVAL = 1,        /* bad pointer, size or combination of sizes */
+    DF2_EUNSUPPORTED = 2,  /* valid request outside what this build handles */
+    DF2_EHIP = 3,          /* HIP runtime or launch failure */
+    DF2_ENOMEM = 4         /* scratch allocation failed */
+} df2_status;
+
+/*
+ * Problem sizes.
+ *   B  sequences (B >= 0; B == 0 enqueues nothing)
+ *   P  draft positions per sequence, the block size minus the verified
+ *      token (1 <= P <= 64)
+ *   V  vocabulary size (K <= V < 2^31)
+ *   d  drafter hidden size (multiple of 32)
+ *   r  embedding rank of A, B and H (multiple of 64, <= 1024); the pages use 256
+ */
+typedef struct df2_dims {
+    int32_t B, P, V, d, r;
+    df2_dtype dtype;
+} df2_dims;
+
+/*
+ * The whole selector in one launch ("A Lightweight Path Selector": top-K,
+ * pair scores, one walk from the last verified token).
+ *   logits   [B, P, V]   drafter logits U_t
+ *   hidden   [B, P, d]   drafter hidden states h_t
+ *   A_tab    [V, r]      predecessor embeddings A(.)
+ *   B_tab    [V, r]      candidate embeddings B(.)
+ *   W_H      [r, d]      gate map, H_t = W_H h_t
+ *   prev_tok [B] int32   last verified token of each sequence
+ *   K        candidates per position, 1 <= K <= min(V, 64) (the pages use 16)
+ *   out_path  [B, P] int32   selected token at each draft position
+ *   out_score [B] float      score of the selected path, sum_t S_t (fp32)
+ * Arithmetic: gate and pair scores accumulate in fp32 (bf16 inputs are
+ * widened exactly).
+ */
+df2_status dflash2_select(const df2_dims* dims, const void* logits,
+                          const void* hidden, const void* A_tab,
+                          const void* B_tab, const void* W_H,
+                          const int32_t* prev_tok, int32_t K,
+                          int32_t* out_path, float* out_score,
+                          hipStream_t stream);
+
+/*
+ * Top-K of each row ("keep the top 16 candidates at each position").
+ *   logits  [rows, V] (dtype)
+ *   out_idx [rows, K] int32  candidate token ids, best first
+ *   out_val [rows, K] float  their logits widened to fp32 (a -0 logit is
+ *                            returned as +0)
+ * 1 <= K <= min(V, 64).  rows == 0 enqueues nothing.
+ */
+df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V,
+                        df2_dtype dtype, int32_t K, int32_t* out_idx,
+                        float* out_val, hipStream_t stream);
+
+/*
+ * Gate projection H = W_H h for M rows (the reading of H(h_t)).
+ *   hidden [M, d] (dtype), W_H [r, d] (dtype), out_H [M, r] float
+ * d multiple of 32, r multiple of 64 and <= 1024.
+ */
+df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M,
+                           int32_t d, int32_t r, df2_dtype dtype, float* out_H,
+                           hipStream_t stream);
+
+/*
+ * Pair scores of the selector equation for every adjacent candidate pair.
+ *   cand_idx [B, P, K] int32, cand_val [B, P, K] float (from dflash2_topk)
+ *   H        [B, P, r] float (from dflash2_project)
+ *   A_tab, B_tab [V, r] (dims->dtype), prev_tok [B] int32
+ *   out_S    [B, P, K, K] float, out_S[b][t][i][j] = S_t(pred_i, cand_j)
+ * The predecessor of rank i at t >= 1 is cand_idx[b][t-1][i]; at t == 0
+ * every row uses prev_tok[b], so all K rows of t == 0 are equal.
+ * dims->d is ignored.
+ */
+df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
+                               const float* cand_val, const float* H,
+                               const void* A_tab, const void* B_tab,
+                               const int32_t* prev_tok, int32_t K,
+                               float* out_S, hipStream_t stream);
+
+/*
+ * The walk alone: max-sum pass over S plus backtrack.
+ *   S        [B, P, K, K] float (row 0 of t == 0 is used)
+ *   cand_idx [B, P, K] int32
+ *   out_path [B, P] int32, out_score [B] float
+ */
+df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B,
+                           int32_t P, int32_t K, int32_t* out_path,
+                           float* out_score, hipStream_t stream);
+
+/*
+ * Waits for `stream`, then reports and clears the device-side input flag of
+ * its scratch buffer: *flags receives a bit mask (bit 0: a prev_tok outside
+ * [0, V) was replaced by 0; bit 1: a cand_idx entry outside [0, V) was
+ * replaced by 0).  Returns DF2_OK, or DF2_EHIP.
+ */
+df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags);
+
+/* Frees every scratch buffer the library holds (call with no work in flight). */
+df2_status dflash2_release(void);
+
+/* Static description of a status code. */
+const char* dflash2_status_string(df2_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dflash2_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* dflash2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH2_H */

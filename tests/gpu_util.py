@@ -1,0 +1,93 @@
+"""Helpers for the GPU parity tests: device copies of seeded inputs and the
+acceptance rule against the oracle.
+
+Tolerances (relative, against the scale sigma = |U| + sum_q |A H B| of each
+score, summed along the path for path scores): 1e-5 for fp32 inputs, 2e-2 for
+bf16 inputs.  Top-K indices and values must match exactly.  A selected path
+may differ from the oracle's only where the oracle's best-versus-second
+margin is within the tolerance, and then the oracle's own score of the GPU
+path must be within the tolerance of the best score.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from draft_selection_topk16_amd import synth
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
+
+
+def to_device(x: synth.Inputs, device="cuda"):
+    dt = x.wl.dtype
+    return dict(logits=dev_tensor(x.logits, dt, device), hidden=dev_tensor(x.hidden, dt, device),
+                A=dev_tensor(x.A, dt, device), Bt=dev_tensor(x.Bt, dt, device),
+                W=dev_tensor(x.W, dt, device),
+                prev=torch.from_numpy(np.ascontiguousarray(x.prev)).to(device))
+
+
+def run_oracle(x: synth.Inputs, seqs=None):
+    f = x.f64()
+    return oracle.select(f["logits"], f["hidden"], f["A"], f["Bt"], f["W"], f["prev"],
+                         x.wl.K, seqs=seqs)
+
+
+def path_score_under_oracle(o, b, path):
+    """Oracle score of a token path (its tokens must be oracle candidates)."""
+    P = o["cand"].shape[1]
+    ranks = []
+    for t in range(P):
+        hit = np.nonzero(o["cand"][b, t] == path[t])[0]
+        assert hit.size == 1, "GPU path token %d at t=%d is not an oracle candidate" % (path[t], t)
+        ranks.append(int(hit[0]))
+    s = o["S"][b, 0, 0, ranks[0]]
+    for t in range(1, P):
+        s += o["S"][b, t, ranks[t - 1], ranks[t]]
+    return s
+
+
+def check_select(path, score, o, tol, label=""):
+    """Apply the acceptance rule; returns the number of tolerated mismatches."""
+    path = np.asarray(path)
+    score = np.asarray(score, dtype=np.float64)
+    mism = 0
+    worst = 0.0
+    for b in range(path.shape[0]):
+        sp = o["sigma_path"][b]
+        if not np.array_equal(path[b], o["path"][b]):
+            mism += 1
+            assert o["margin"][b] <= tol * sp, (
+                "%s seq %d: path differs but margin %.3g > tol*sigma %.3g" % (label, b, o["margin"][b], tol * sp))
+            s = path_score_under_oracle(o, b, path[b])
+            assert s >= o["score"][b] - tol * sp, (label, b, s, o["score"][b])
+        err = abs(score[b] - o["score"][b]) / max(abs(o["score"][b]), sp)
+        worst = max(worst, err)
+        assert err <= tol, "%s seq %d: score %.9g vs oracle %.9g (rel %.3g)" % (
+            label, b, score[b], o["score"][b], err)
+    say("  %s: %d sequences, %d tolerated path mismatches, worst score rel err %.3g"
+        % (label, path.shape[0], mism, worst))
+    return mism
+
+
+def check_scores(S_gpu, S_ref, sigma, tol, label=""):
+    S_gpu = np.asarray(S_gpu, dtype=np.float64)
+    scale = np.maximum(np.abs(S_ref), sigma)
+    rel = np.abs(S_gpu - S_ref) / np.where(scale > 0, scale, 1.0)
+    worst = float(rel.max()) if rel.size else 0.0
+    say("  %s: worst pair-score rel err %.3g" % (label, worst))
+    assert worst <= tol, (label, worst)

@@ -1,0 +1,127 @@
+"""CPU checks of the C ABI: the library builds/loads, exports every entry point
+that include/dflash2.h declares, and rejects bad arguments on the host before
+any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import draft_selection_topk16_amd as df2
+from draft_selection_topk16_amd.binding import Dims, EXPORTED
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash2.h")
+
+DF2_OK, DF2_EINVAL, DF2_EUNSUPPORTED = 0, 1, 2
+FAKE = 0x10000      # a 16-byte aligned non-null address; never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash2_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return df2.load()
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", df2.binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    syms = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in syms, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert re.fullmatch(r"\d+\.\d+\.\d+", df2.version())
+    assert lib.dflash2_status_string(0) == b"ok"
+    assert lib.dflash2_status_string(1) == b"invalid argument"
+    assert lib.dflash2_status_string(99) == b"unknown status"
+
+
+def _select(lib, dims, K=16, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return lib.dflash2_select(ctypes.byref(dims) if dims is not None else None,
+                              p[0], p[1], p[2], p[3], p[4], p[5], K, FAKE, FAKE, None)
+
+
+@pytest.mark.parametrize("dims,K,status,msg", [
+    (None, 16, DF2_EINVAL, "dims is NULL"),
+    (Dims(1, 7, 32000, 1024, 256, 7), 16, DF2_EINVAL, "dtype"),
+    (Dims(-1, 7, 32000, 1024, 256, 1), 16, DF2_EINVAL, "B < 0"),
+    (Dims(1, 0, 32000, 1024, 256, 1), 16, DF2_EINVAL, "P must be"),
+    (Dims(1, 65, 32000, 1024, 256, 1), 16, DF2_EINVAL, "P must be"),
+    (Dims(1, 7, 0, 1024, 256, 1), 16, DF2_EINVAL, "V < 1"),
+    (Dims(1, 7, 32000, 1000, 256, 1), 16, DF2_EUNSUPPORTED, "d must be"),
+    (Dims(1, 7, 32000, 1024, 200, 1), 16, DF2_EUNSUPPORTED, "r must be"),
+    (Dims(1, 7, 32000, 1024, 2048, 1), 16, DF2_EUNSUPPORTED, "r must be"),
+    (Dims(1, 7, 32000, 1024, 256, 1), 0, DF2_EINVAL, "K must be"),
+    (Dims(1, 7, 32000, 1024, 256, 1), 65, DF2_EINVAL, "K must be"),
+    (Dims(1, 7, 10, 1024, 256, 1), 11, DF2_EINVAL, "K must be"),
+])
+def test_select_rejects_bad_sizes(lib, dims, K, status, msg):
+    assert _select(lib, dims, K) == status
+    assert msg in lib.dflash2_last_error().decode()
+
+
+def test_select_rejects_null_and_misaligned(lib):
+    dims = Dims(2, 7, 32000, 1024, 256, 1)
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = None
+        assert _select(lib, dims, 16, p) == DF2_EINVAL
+        assert "NULL" in lib.dflash2_last_error().decode()
+    for i in (1, 2, 3, 4):          # hidden, A, B, W need 16-byte alignment
+        p = [FAKE] * 6
+        p[i] = FAKE + 8
+        assert _select(lib, dims, 16, p) == DF2_EINVAL
+        assert "aligned" in lib.dflash2_last_error().decode()
+    p = [FAKE] * 6
+    p[0] = FAKE + 1                 # bf16 logits need 2-byte alignment
+    assert _select(lib, dims, 16, p) == DF2_EINVAL
+
+
+def test_empty_batch_is_a_noop(lib):
+    # B == 0 returns before touching the device (no GPU needed)
+    assert _select(lib, Dims(0, 7, 32000, 1024, 256, 1), 16) == DF2_OK
+    assert lib.dflash2_topk(FAKE, 0, 100, 1, 16, FAKE, FAKE, None) == DF2_OK
+    assert lib.dflash2_project(FAKE, FAKE, 0, 64, 64, 1, FAKE, None) == DF2_OK
+    assert lib.dflash2_viterbi(FAKE, FAKE, 0, 3, 4, FAKE, FAKE, None) == DF2_OK
+
+
+def test_stage_entry_points_reject_bad_arguments(lib):
+    assert lib.dflash2_topk(FAKE, 4, 100, 1, 0, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_topk(FAKE, 4, 10, 1, 11, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_topk(FAKE, -1, 100, 1, 4, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_topk(FAKE, 4, 100, 5, 4, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_topk(None, 4, 100, 1, 4, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_topk(FAKE + 1, 4, 100, 0, 4, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_project(FAKE, FAKE, 4, 48, 64, 1, FAKE, None) == DF2_EUNSUPPORTED
+    assert lib.dflash2_project(FAKE, FAKE, 4, 64, 96, 1, FAKE, None) == DF2_EUNSUPPORTED
+    assert lib.dflash2_project(FAKE + 4, FAKE, 4, 64, 64, 1, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_viterbi(FAKE, FAKE, 2, 0, 4, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_viterbi(FAKE, FAKE, 2, 3, 65, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_viterbi(None, FAKE, 2, 3, 4, FAKE, FAKE, None) == DF2_EINVAL
+    d = Dims(2, 3, 100, 32, 64, 1)
+    assert lib.dflash2_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 4,
+                                   FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 101,
+                                   FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_device_error(None, None) == DF2_EINVAL
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    x = torch.zeros(2, 3, 100, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        df2.topk(x, 4)

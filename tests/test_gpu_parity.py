@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case prints its name before touching the GPU.  Workloads follow the
+five seeded workloads of draft_selection_topk16_amd.synth; the stress
+workload is checked on sampled sequences/rows (the oracle runs them one by
+one), the others in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import draft_selection_topk16_amd as df2
+from draft_selection_topk16_amd import synth
+from gpu_util import (TOL, check_scores, check_select, dev_tensor, run_oracle, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+STRESS_SEQS = [0, 1, 77, 128, 200, 255]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    df2.load()
+    yield
+    torch.cuda.synchronize()
+
+
+_cache = {}
+
+
+def inputs(name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _cache:
+        wl = synth.WORKLOADS[name].with_(**kw) if kw else synth.WORKLOADS[name]
+        _cache.clear()      # keep at most one (possibly large) input set alive
+        _cache[key] = synth.make_inputs(wl)
+    return _cache[key]
+
+
+def gpu_topk(x_np, dtype, K):
+    t = dev_tensor(x_np, dtype)
+    idx, val = df2.topk(t, K)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+# --------------------------------------------------------------------- top-K
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_4b_b1", "t27b_b8", "t27b_b32", "stress_b256"])
+def test_topk_workloads(name):
+    x = inputs(name)
+    K, V = x.wl.K, x.wl.V
+    say("topk %s K=%d V=%d rows=%d" % (name, K, V, x.wl.rows))
+    idx, val = gpu_topk(x.logits.reshape(-1, V), x.wl.dtype, K)
+    f = synth.to_f64(x.logits.reshape(-1, V), x.wl.dtype)
+    rows = np.arange(f.shape[0])
+    if name == "stress_b256":
+        rows = np.unique(np.concatenate([np.arange(0, f.shape[0], 331), [f.shape[0] - 1]]))
+    oi, ov = oracle.topk(f[rows], K)
+    assert np.array_equal(idx[rows], oi)
+    assert np.array_equal(val[rows].astype(np.float64), ov)
+
+
+def _tie_rows(kind, V, rng):
+    if kind == "constant":
+        return np.full((3, V), 1.25, dtype=np.float32)
+    if kind == "signed_zero":
+        x = np.where(rng.random((3, V)) < 0.5, -0.0, 0.0).astype(np.float32)
+        x[:, ::97] = -1.0
+        return x
+    if kind == "flat_normal":
+        return rng.standard_normal((4, V)).astype(np.float32)
+    if kind == "two_levels":
+        return (rng.random((3, V)) < 0.002).astype(np.float32)
+    if kind == "all_negative":
+        return (-np.abs(rng.standard_normal((3, V))) - 3.0).astype(np.float32)
+    if kind == "neg_inf_mix":
+        x = rng.standard_normal((3, V)).astype(np.float32)
+        x[:, ::3] = -np.inf
+        x[0, :] = -np.inf
+        x[0, 5] = np.inf
+        return x
+    if kind == "ascending":
+        return np.tile(np.arange(V, dtype=np.float32) / V, (2, 1))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["constant", "signed_zero", "flat_normal", "two_levels",
+                                  "all_negative", "neg_inf_mix", "ascending"])
+@pytest.mark.parametrize("V,K", [(151936, 16), (40000, 32), (1001, 64), (37, 5), (16, 16), (20000, 1)])
+def test_topk_ties_and_edges(dtype, kind, V, K):
+    say("topk ties %s %s V=%d K=%d" % (dtype, kind, V, K))
+    rng = np.random.default_rng(V * 7 + K)
+    x32 = _tie_rows(kind, V, rng)
+    x = synth.f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+    idx, val = gpu_topk(x, dtype, K)
+    oi, ov = oracle.topk(synth.to_f64(x, dtype), K)
+    assert np.array_equal(idx, oi)
+    assert np.array_equal(val.astype(np.float64), ov)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_unaligned_rows(dtype):
+    """Row starts that are not 16-byte aligned take the element-wise loads."""
+    V, K, rows = 30001, 16, 5
+    say("topk unaligned %s" % dtype)
+    rng = np.random.default_rng(3)
+    flat32 = rng.standard_normal(rows * V + 1).astype(np.float32)
+    flat = synth.f32_to_bf16_bits(flat32) if dtype == "bf16" else flat32
+    t = dev_tensor(flat, dtype)[1:].reshape(rows, V)
+    assert t.data_ptr() % 16 != 0
+    idx, val = df2.topk(t, K)
+    oi, ov = oracle.topk(synth.to_f64(flat[1:].reshape(rows, V), dtype), K)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+    assert np.array_equal(val.cpu().numpy().astype(np.float64), ov)
+
+
+# ---------------------------------------------------------------- projection
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_4b_b1", "t27b_b8", "t27b_b32"])
+def test_project_workloads(name):
+    x = inputs(name)
+    say("project %s M=%d d=%d" % (name, x.wl.rows, x.wl.d))
+    t = to_device(x)
+    H = df2.project(t["hidden"], t["W"]).cpu().numpy().astype(np.float64)
+    f = x.f64()
+    Hr = oracle.project(f["hidden"], f["W"])
+    scale = np.abs(f["hidden"]) @ np.abs(f["W"]).T       # sum_m |W h|
+    rel = np.abs(H - Hr) / scale
+    say("  worst rel err %.3g" % rel.max())
+    assert rel.max() <= TOL[x.wl.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,d,r", [(1, 32, 64), (17, 96, 128), (64, 64, 64), (300, 512, 256), (3840, 256, 256)])
+def test_project_shapes(dtype, M, d, r):
+    say("project shape %s M=%d d=%d r=%d" % (dtype, M, d, r))
+    rng = np.random.default_rng(M + d + r)
+    h32 = rng.standard_normal((M, d)).astype(np.float32)
+    w32 = (rng.standard_normal((r, d)) / 8).astype(np.float32)
+    h = synth.f32_to_bf16_bits(h32) if dtype == "bf16" else h32
+    w = synth.f32_to_bf16_bits(w32) if dtype == "bf16" else w32
+    H = df2.project(dev_tensor(h, dtype), dev_tensor(w, dtype)).cpu().numpy().astype(np.float64)
+    hf, wf = synth.to_f64(h, dtype), synth.to_f64(w, dtype)
+    rel = np.abs(H - oracle.project(hf, wf)) / (np.abs(hf) @ np.abs(wf).T)
+    assert rel.max() <= TOL[dtype]
+
+
+# ------------------------------------------------------------- pair scores
+@pytest.mark.parametrize("name,kw", [("tiny_f32", {}), ("qwen3_4b_b1", {}),
+                                     ("t27b_b8", {"pair_scale": 8.0}),
+                                     ("stress_b256", {"B": 3, "V": 20000, "d": 256})])
+def test_pair_scores_stage(name, kw):
+    x = inputs(name, **kw)
+    say("pair_scores %s %s" % (name, kw))
+    o = run_oracle(x)
+    dt = x.wl.dtype
+    t = to_device(x)
+    cand = torch.from_numpy(o["cand"]).cuda()
+    cval = torch.from_numpy(o["U"].astype(np.float32)).cuda()
+    H32 = o["H"].astype(np.float32)
+    S = df2.pair_scores(cand, cval, torch.from_numpy(H32).cuda(), t["A"], t["Bt"], t["prev"])
+    S = S.cpu().numpy()
+    f = x.f64()
+    S_ref, sig = oracle.pair_scores(o["cand"], o["U"], H32.astype(np.float64), f["A"], f["Bt"], f["prev"])
+    check_scores(S, S_ref, sig, TOL[dt], "S " + name)
+
+
+# ------------------------------------------------------------------- walk
+@pytest.mark.parametrize("K,P", [(16, 7), (32, 15), (5, 3), (1, 4), (64, 2), (16, 64)])
+def test_viterbi_stage(K, P):
+    say("viterbi K=%d P=%d" % (K, P))
+    rng = np.random.default_rng(K * 100 + P)
+    B = 9
+    S = rng.standard_normal((B, P, K, K)).astype(np.float32)
+    S[:, 0, 1:, :] = S[:, 0, :1, :]       # t = 0 rows all equal row 0
+    cand = rng.integers(0, 1 << 20, size=(B, P, K)).astype(np.int32)
+    path, score = df2.viterbi(torch.from_numpy(S).cuda(), torch.from_numpy(cand).cuda())
+    pr, pt, sc = oracle.viterbi(S.astype(np.float64), cand)
+    sec = oracle.second_best(S.astype(np.float64), pr)
+    path = path.cpu().numpy()
+    score = score.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        if not np.array_equal(path[b], pt[b]):
+            assert sc[b] - sec[b] <= 1e-5 * P * 4, (b, sc[b], sec[b])
+        assert abs(score[b] - sc[b]) <= 1e-5 * P * 4
+
+
+def test_viterbi_integer_ties_exact():
+    """Small-integer scores are exact in fp32: ties must break exactly like
+    the oracle (smaller predecessor rank, smaller final rank)."""
+    rng = np.random.default_rng(42)
+    B, P, K = 16, 6, 8
+    S = rng.integers(-2, 3, size=(B, P, K, K)).astype(np.float32)
+    S[:, 0, 1:, :] = S[:, 0, :1, :]
+    cand = np.tile(np.arange(K, dtype=np.int32), (B, P, 1)) + 1000
+    path, score = df2.viterbi(torch.from_numpy(S).cuda(), torch.from_numpy(cand).cuda())
+    _, pt, sc = oracle.viterbi(S.astype(np.float64), cand)
+    assert np.array_equal(path.cpu().numpy(), pt)
+    assert np.array_equal(score.cpu().numpy().astype(np.float64), sc)
+
+
+# ------------------------------------------------------------ whole select
+def gpu_select(x):
+    t = to_device(x)
+    path, score = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K)
+    torch.cuda.synchronize()
+    return path.cpu().numpy(), score.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_4b_b1", "t27b_b8", "t27b_b32", "stress_b256"])
+def test_select_workloads(name):
+    x = inputs(name)
+    say("select %s B=%d P=%d V=%d K=%d" % (name, x.wl.B, x.wl.P, x.wl.V, x.wl.K))
+    path, score = gpu_select(x)
+    seqs = STRESS_SEQS if name == "stress_b256" else None
+    o = run_oracle(x, seqs=seqs)
+    if seqs is not None:
+        path, score = path[seqs], score[seqs]
+    check_select(path, score, o, TOL[x.wl.dtype], name)
+    assert flags_clear()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {"pair_scale": 8.0, "V": 4000}),
+    ("qwen3_4b_b1", {"pair_scale": 8.0}),
+    ("t27b_b8", {"pair_scale": 8.0, "V": 30000, "d": 512}),
+    ("stress_b256", {"pair_scale": 8.0, "B": 4, "V": 50000, "d": 512}),
+])
+def test_select_pair_dominant(name, kw):
+    """A and B scaled so the pair term outweighs logit gaps: the walk, not
+    the top-1 pick, decides the path."""
+    x = inputs(name, **kw)
+    say("select pair-dominant %s %s" % (name, kw))
+    path, score = gpu_select(x)
+    o = run_oracle(x)
+    top1 = o["cand"][:, :, 0]
+    say("  positions where the path leaves top-1: %d of %d" % (int((o["path"] != top1).sum()), top1.size))
+    check_select(path, score, o, TOL[x.wl.dtype], name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_integer_exact(dtype):
+    """Small-integer inputs keep every step exact on both sides (bf16 hi/lo
+    split included): paths and scores must match bit for bit."""
+    say("select integer-exact %s" % dtype)
+    rng = np.random.default_rng(7)
+    B, P, V, d, r, K = 6, 7, 3000, 64, 64, 16
+    wl = synth.Workload("int", 0, B=B, P=P, V=V, d=d, K=K, r=r, dtype=dtype)
+    logits = rng.integers(-6, 7, size=(B, P, V)).astype(np.float32)
+    x = synth.make_inputs(wl, seed=123, logits_override=logits)
+    for k, shape in (("hidden", (B, P, d)), ("A", (V, r)), ("Bt", (V, r)), ("W", (r, d))):
+        v = rng.integers(-2, 3, size=shape).astype(np.float32)
+        setattr(x, k, synth.f32_to_bf16_bits(v) if dtype == "bf16" else v)
+    path, score = gpu_select(x)
+    o = run_oracle(x)
+    assert np.array_equal(path, o["path"])
+    assert np.array_equal(score.astype(np.float64), o["score"])
+
+
+@pytest.mark.parametrize("B,P,V,K,d", [(1, 1, 5000, 16, 64), (3, 64, 3000, 16, 64),
+                                       (2, 5, 64, 64, 64), (2, 4, 300, 1, 64),
+                                       (5, 3, 16, 16, 32), (4, 7, 9999, 3, 96),
+                                       (33, 7, 2048, 16, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_edge_shapes(B, P, V, K, d, dtype):
+    say("select edge %s B=%d P=%d V=%d K=%d d=%d" % (dtype, B, P, V, K, d))
+    wl = synth.Workload("edge", 1, B=B, P=P, V=V, d=d, K=K, r=64, dtype=dtype, pair_scale=4.0)
+    x = synth.make_inputs(wl, seed=B * 1000 + P * 10 + K)
+    path, score = gpu_select(x)
+    check_select(path, score, run_oracle(x), TOL[dtype], "edge")
+
+
+def test_select_empty_batch():
+    say("select empty batch")
+    dev = "cuda"
+    logits = torch.empty((0, 7, 1000), dtype=torch.bfloat16, device=dev)
+    hidden = torch.empty((0, 7, 64), dtype=torch.bfloat16, device=dev)
+    A = torch.zeros((1000, 64), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((64, 64), dtype=torch.bfloat16, device=dev)
+    prev = torch.empty((0,), dtype=torch.int32, device=dev)
+    path, score = df2.select(logits, hidden, A, A, W, prev, 16)
+    assert path.shape == (0, 7) and score.shape == (0,)
+
+
+def test_select_deterministic_and_scratch_reuse():
+    say("select determinism and scratch reuse")
+    big = inputs("t27b_b32")
+    tb = to_device(big)
+    small = synth.make_inputs(synth.WORKLOADS["tiny_f32"].with_(V=5000))
+    ts = to_device(small)
+    ref_b = df2.select(tb["logits"], tb["hidden"], tb["A"], tb["Bt"], tb["W"], tb["prev"], 16)
+    ref_s = df2.select(ts["logits"], ts["hidden"], ts["A"], ts["Bt"], ts["W"], ts["prev"], 16)
+    ref_b = [a.clone() for a in ref_b]
+    ref_s = [a.clone() for a in ref_s]
+    for i in range(20):
+        if i % 2:
+            p, s = df2.select(tb["logits"], tb["hidden"], tb["A"], tb["Bt"], tb["W"], tb["prev"], 16)
+            assert torch.equal(p, ref_b[0]) and torch.equal(s, ref_b[1])
+        else:
+            p, s = df2.select(ts["logits"], ts["hidden"], ts["A"], ts["Bt"], ts["W"], ts["prev"], 16)
+            assert torch.equal(p, ref_s[0]) and torch.equal(s, ref_s[1])
+    o = run_oracle(small)
+    check_select(ref_s[0].cpu().numpy(), ref_s[1].cpu().numpy(), o, TOL["f32"], "small after big")
+
+
+def flags_clear():
+    return df2.device_error() == 0
+
+
+def test_prev_tok_out_of_range_sets_flag():
+    say("select prev_tok out of range")
+    x = synth.make_inputs(synth.WORKLOADS["tiny_f32"].with_(V=3000, B=2))
+    t = to_device(x)
+    assert df2.device_error() == 0
+    bad = t["prev"].clone()
+    bad[1] = 3000
+    path, score = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], bad, 16)
+    assert df2.device_error() == 1
+    assert df2.device_error() == 0          # reading clears the flag
+    x.prev = np.array([x.prev[0], 0], dtype=np.int32)   # replaced by token 0
+    check_select(path.cpu().numpy(), score.cpu().numpy(), run_oracle(x), TOL["f32"], "bad prev")
+
+
+def test_stages_compose_to_select():
+    """topk -> project -> pair_scores -> viterbi gives the fused result."""
+    x = inputs("qwen3_4b_b1")
+    say("stages compose")
+    t = to_device(x)
+    B, P, V = x.wl.B, x.wl.P, x.wl.V
+    idx, val = df2.topk(t["logits"], 16)
+    H = df2.project(t["hidden"], t["W"])
+    S = df2.pair_scores(idx, val, H, t["A"], t["Bt"], t["prev"])
+    p1, s1 = df2.viterbi(S, idx)
+    p2, s2 = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], 16)
+    assert torch.equal(p1, p2)
+    assert torch.allclose(s1, s2, rtol=1e-6, atol=1e-6)
