@@ -65,6 +65,13 @@ __device__ __forceinline__ float wave_max_f32(float x) {
     return x;
 }
 
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Sum over the workgroup; `red` holds kWaves words of LDS.  Every thread of
 // the workgroup must call it.
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t x, uint32_t* red) {
@@ -97,28 +104,60 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Arrival on a counter in global memory with release/acquire ordering at
-// device scope.  The caller's workgroup must have fenced its stores; returns
-// the value before the increment.
+// ---------------------------------------------------------------------------
+// Workgroup-to-workgroup hand-off inside one launch.
+//
+// Each XCD has its own L2.  A device-scope fence on gfx950 writes back and
+// invalidates the whole L2 (buffer_wbl2 / buffer_inv), which is far too
+// costly to pay once per workgroup.  Instead, every value that one
+// workgroup writes for another goes through an agent-scope atomic store and
+// is read back with an agent-scope atomic load: both carry the sc1 bit and
+// are coherent across XCDs by themselves.  A producer drains its own stores
+// (s_waitcnt vmcnt(0)), meets the workgroup barrier, and one thread then
+// bumps a counter with a device-scope atomic add.  The workgroup that sees
+// the last count reads the data after that add has returned.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void xstore(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T xload(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Eight consecutive floats (32-byte aligned) through four 8-byte loads.
+__device__ __forceinline__ void xload_f8(const float* p, float out[8]) {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t w = xload(q + i);
+        out[2 * i] = __uint_as_float((uint32_t)w);
+        out[2 * i + 1] = __uint_as_float((uint32_t)(w >> 32));
+    }
+}
+
+// Wait until this wave's outstanding vector-memory operations (in particular
+// its stores) have completed.  simm16 0x0F70 = vmcnt(0), expcnt and lgkmcnt
+// left at their maxima.
+__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ uint32_t arrive(uint32_t* cnt) {
-    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void reset_counter(uint32_t* cnt) {
     __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every thread publishes its stores, then one thread arrives.  Returns true
-// (uniformly) in the workgroup that arrives last, after an acquire fence so
-// that it sees what every earlier arrival wrote.
+// Every wave publishes its hand-off stores, then one thread arrives.  Returns
+// true (uniformly) in the workgroup that arrives last; that workgroup then
+// reads the other arrivals' data with xload.
 __device__ __forceinline__ bool block_arrive_last(uint32_t* cnt, uint32_t expected,
                                                   uint32_t* lds_flag) {
-    __threadfence();
+    drain_stores();
     __syncthreads();
     if (threadIdx.x == 0) *lds_flag = (arrive(cnt) == expected - 1u) ? 1u : 0u;
     __syncthreads();
-    bool last = (*lds_flag != 0u);
-    if (last) __threadfence();
-    return last;
+    return *lds_flag != 0u;
 }
 
 }  // namespace df2

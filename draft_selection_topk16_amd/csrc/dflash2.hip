@@ -9,10 +9,11 @@
 // dflash2_select runs everything in ONE launch.  The grid holds two kinds of
 // workgroups that run side by side:
 //   * gate workgroups (the first n_proj): one slice of one H tile each;
-//   * chunk workgroups: one vocabulary chunk of one logits row each.
+//   * segment workgroups: one contiguous vocabulary segment of one logits row
+//     each, streamed chunk by chunk.
 // Work that needs several workgroups' results is done by whichever of them
 // arrives last on a counter (no workgroup ever waits for another):
-//   * the last chunk of a row merges the row's candidates;
+//   * the last segment of a row merges the row's candidates;
 //   * the last slice of an H tile sums the slices;
 //   * the last of a sequence's row merges and H tiles runs the pair scores
 //     and the walk for that sequence.
@@ -52,7 +53,7 @@ struct Params {
     int32_t* out_path;
     float* out_score;
     // scratch
-    uint64_t* part;       // [rows, C, K] candidate words
+    uint64_t* part;       // [rows, nseg, K] candidate words
     int32_t* cand;        // [rows, K]
     float* cval;          // [rows, K]
     float* ppart;         // [S, M, r] gate partials (S > 1)
@@ -65,6 +66,8 @@ struct Params {
     int B, P, V, d, r, K;
     int64_t rows;
     int C;                // chunks per row
+    int nseg;             // segments per row
+    int cps;              // chunks per segment
     int aligned;          // logits rows are 16-byte aligned and V % per-vector == 0
     int mtiles, qtiles, S, n_proj;
 };
@@ -105,16 +108,17 @@ __device__ __forceinline__ uint32_t seq_expected(const Params& p, int b) {
 }
 
 template <bool BF16, int NV>
-__device__ void chunk_role(const Params& p, int64_t cb, bool fused, SharedAll& sm,
+__device__ void chunk_role(const Params& p, int64_t sb, bool fused, SharedAll& sm,
                            uint32_t* flag) {
-    const int64_t row = cb / p.C;
-    const int chunk = (int)(cb % p.C);
+    const int64_t row = sb / p.nseg;
+    const int seg = (int)(sb % p.nseg);
     const size_t esz = BF16 ? 2 : 4;
     const char* rowp = reinterpret_cast<const char*>(p.logits) + (size_t)row * p.V * esz;
-    chunk_topk<BF16, NV>(rowp, p.V, chunk, p.K, p.aligned != 0,
-                         p.part + ((size_t)row * p.C + chunk) * p.K, sm.c);
-    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.C, flag)) return;
-    merge_row<BF16>(p.part + (size_t)row * p.C * p.K, p.C, p.K, p.cand + row * p.K,
+    const int c0 = seg * p.cps, c1 = min(p.C, c0 + p.cps);
+    segment_topk<BF16, NV>(rowp, p.V, c0, c1, p.K, p.aligned != 0,
+                           p.part + ((size_t)row * p.nseg + seg) * p.K, sm.c);
+    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, flag)) return;
+    merge_row<BF16>(p.part + (size_t)row * p.nseg * p.K, p.nseg, p.K, p.cand + row * p.K,
                     p.cval + row * p.K, sm.m);
     if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
     if (!fused) return;
@@ -270,36 +274,40 @@ struct Plan {
     size_t off_part = 0, off_cand = 0, off_cval = 0, off_ppart = 0, off_H = 0;
 };
 
-// Chunk size: the largest that still gives every CU several workgroups, and
-// small enough that a row's merge fits the registers of one workgroup.
-int choose_nv(int64_t rows, int V, int K, bool bf16) {
-    const int pv = bf16 ? 8 : 4;
-    int forced = env_int("DF2_NV", 0);
-    auto chunks = [&](int nv) { return (int64_t)((V + (int64_t)kWG * pv * nv - 1) / ((int64_t)kWG * pv * nv)); };
-    auto fits = [&](int nv) { return chunks(nv) * K <= (int64_t)kWG * kMergeItems; };
-    if (forced == 1 || forced == 2 || forced == 4 || forced == 8) {
-        if (fits(forced)) return forced;
-    }
-    const int opts[4] = {8, 4, 2, 1};
-    for (int nv : opts)
-        if (fits(nv) && rows * chunks(nv) >= 1024) return nv;
-    for (int nv : {1, 2, 4, 8})
-        if (fits(nv)) return nv;
-    return -1;
-}
-
+// Chunk size (16-byte vectors per thread) and segmentation of the rows.
+// Chunks of 256 x 4 vectors keep two register buffers per thread cheap;
+// smaller chunks are used when there are too few rows to give every CU a
+// workgroup.  Rows are then cut into segments so that about `target`
+// workgroups stream in total, each pays one hand-off per segment, and the
+// row merge stays within one workgroup's registers.
 void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits) {
     Params& p = pl.p;
     pl.bf16 = bf16;
     const int pv = bf16 ? 8 : 4;
-    pl.nv = choose_nv(rows, V, K, bf16);
-    const int64_t ce = (int64_t)kWG * pv * std::max(pl.nv, 1);
-    p.C = (int)((V + ce - 1) / ce);
+    auto chunks = [&](int nv) { return (int)((V + (int64_t)kWG * pv * nv - 1) / ((int64_t)kWG * pv * nv)); };
+    int nv = 1;
+    for (int cand : {4, 2, 1}) {
+        if (rows * chunks(cand) >= 256) { nv = cand; break; }
+    }
+    const int forced = env_int("DF2_NV", 0);
+    if (forced == 1 || forced == 2 || forced == 4) nv = forced;
+    pl.nv = nv;
+    p.C = chunks(nv);
+    const int64_t target = std::max(1, env_int("DF2_WGS", 1024));
+    int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, (target + rows - 1) / rows));
+    int cps = (p.C + nseg - 1) / nseg;
+    nseg = (p.C + cps - 1) / cps;
+    while ((int64_t)nseg * K > (int64_t)kWG * kMergeItems) {
+        ++cps;
+        nseg = (p.C + cps - 1) / cps;
+    }
+    p.nseg = nseg;
+    p.cps = cps;
     p.rows = rows;
     p.V = V;
     p.K = K;
     p.aligned = (aligned16(logits) && (V % pv) == 0) ? 1 : 0;
-    pl.n_chunk_blocks = rows * p.C;
+    pl.n_chunk_blocks = rows * nseg;
 }
 
 void plan_proj(Plan& pl, int64_t M, int d, int r) {
@@ -321,14 +329,15 @@ void plan_proj(Plan& pl, int64_t M, int d, int r) {
     p.r = r;
 }
 
-// Scratch layout: counters first (err, rows, tiles, sequences), then data.
+// Scratch layout: counters first (err, row arrivals, tiles, sequences), then
+// data.
 void plan_layout(Plan& pl, int64_t rows, int64_t M, int B) {
     Params& p = pl.p;
     const size_t ncnt = 1 + (size_t)rows + (size_t)p.mtiles * p.qtiles + (size_t)B;
     pl.counter_bytes = align_up(ncnt * 4, 256);
     size_t off = pl.counter_bytes;
     pl.off_part = off;
-    off = align_up(off + (size_t)rows * p.C * p.K * 8, 256);
+    off = align_up(off + (size_t)rows * p.nseg * p.K * 8, 256);
     pl.off_cand = off;
     off = align_up(off + (size_t)rows * p.K * 4, 256);
     pl.off_cval = off;
@@ -364,8 +373,8 @@ df2_status check_dims(const df2_dims* dims, bool need_d) {
     if (dims->V < 1) return fail(DF2_EINVAL, "V < 1");
     if (need_d && (dims->d < 32 || dims->d % 32 != 0))
         return fail(DF2_EUNSUPPORTED, "d must be a positive multiple of 32");
-    if (dims->r < 64 || dims->r % 64 != 0 || dims->r > 1024)
-        return fail(DF2_EUNSUPPORTED, "r must be a multiple of 64 in [64, 1024]");
+    if (dims->r < 64 || dims->r % 64 != 0 || dims->r > kMaxR)
+        return fail(DF2_EUNSUPPORTED, "r must be a multiple of 64 in [64, 512]");
     return DF2_OK;
 }
 
@@ -386,8 +395,7 @@ df2_status launch_checked(F&& f, const char* what) {
     switch (pl.nv) {                                                                 \
         case 1: hipLaunchKernelGGL((k_select<BF, 1, NQ_>), grid, block, 0, stream, pl.p); break; \
         case 2: hipLaunchKernelGGL((k_select<BF, 2, NQ_>), grid, block, 0, stream, pl.p); break; \
-        case 4: hipLaunchKernelGGL((k_select<BF, 4, NQ_>), grid, block, 0, stream, pl.p); break; \
-        default: hipLaunchKernelGGL((k_select<BF, 8, NQ_>), grid, block, 0, stream, pl.p); break; \
+        default: hipLaunchKernelGGL((k_select<BF, 4, NQ_>), grid, block, 0, stream, pl.p); break; \
     }
 
 void launch_select(const Plan& pl, hipStream_t stream) {
@@ -405,8 +413,7 @@ void launch_topk(const Plan& pl, hipStream_t stream) {
     switch (pl.nv) {                                                                          \
         case 1: hipLaunchKernelGGL((k_topk<BF, 1>), grid, block, 0, stream, pl.p); break;   \
         case 2: hipLaunchKernelGGL((k_topk<BF, 2>), grid, block, 0, stream, pl.p); break;   \
-        case 4: hipLaunchKernelGGL((k_topk<BF, 4>), grid, block, 0, stream, pl.p); break;   \
-        default: hipLaunchKernelGGL((k_topk<BF, 8>), grid, block, 0, stream, pl.p); break;  \
+        default: hipLaunchKernelGGL((k_topk<BF, 4>), grid, block, 0, stream, pl.p); break;  \
     }
     if (pl.bf16) { DF2_TOPK(true) } else { DF2_TOPK(false) }
 #undef DF2_TOPK
@@ -467,7 +474,6 @@ df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* 
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     plan_topk(pl, rows, dims->V, K, bf16, logits);
-    if (pl.nv < 0) return fail(DF2_EUNSUPPORTED, "V * K too large for the row merge");
     plan_proj(pl, rows, dims->d, dims->r);
     plan_layout(pl, rows, rows, dims->B);
     Params& p = pl.p;
@@ -506,7 +512,6 @@ df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V, df2_dtype d
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     plan_topk(pl, rows, V, K, bf16, logits);
-    if (pl.nv < 0) return fail(DF2_EUNSUPPORTED, "V * K too large for the row merge");
     if (pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "too many rows");
     pl.p.mtiles = 0;
     pl.p.qtiles = 0;

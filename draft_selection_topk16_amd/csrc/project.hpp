@@ -92,7 +92,7 @@ __device__ void proj_block(const void* __restrict__ hidden, const void* __restri
                           sm.red[3][n][v][l];
         const int mm = mt * 16 + (l >> 4) * 4 + v;
         const int q = qbase + n * 16 + (l & 15);
-        if (mm < M) out[(int64_t)mm * r + q] = sum;
+        if (mm < M) xstore(out + (int64_t)mm * r + q, sum);
     }
 }
 
@@ -106,8 +106,8 @@ __device__ void proj_reduce_tile(const float* __restrict__ part, int M, int r, i
         const int q = qt * cols + x % cols;
         if (mm >= M) continue;
         float acc = 0.f;
-        for (int s = 0; s < S; ++s) acc += part[((int64_t)s * M + mm) * r + q];
-        H[(int64_t)mm * r + q] = acc;
+        for (int s = 0; s < S; ++s) acc += xload(part + ((int64_t)s * M + mm) * r + q);
+        xstore(H + (int64_t)mm * r + q, acc);
     }
 }
 

@@ -28,10 +28,13 @@ namespace df2 {
 constexpr int kTailFloats = 4096;   // scores of a group of positions in LDS
 constexpr int kMaxP = 64;
 constexpr int kMaxK = 64;
+constexpr int kMaxR = 512;
 
 struct TailLds {
     float S[kTailFloats];
+    float Hw[kWaves][kMaxR];        // each wave's copy of the gate row it scores
     uint8_t psi[kMaxP * kMaxK];
+    int32_t rank[kMaxP];
 };
 
 struct TailArgs {
@@ -52,17 +55,18 @@ struct TailArgs {
 enum { kTailFull = 0, kTailScoresOnly = 1, kTailWalkOnly = 2 };
 
 // One 16 x 16 tile (rows ti, columns tj) of S_t, computed by the calling wave
-// and stored to dst[i * K + j] (i, j < K).
+// and stored to dst[i * K + j] (i, j < K).  Hs: this wave's LDS copy of H_t.
 template <bool BF16>
 __device__ void pair_tile(const TailArgs& a, int b, int t, int ti, int tj, int prev,
-                          float* __restrict__ dst) {
+                          const float* __restrict__ Hs, float* __restrict__ dst) {
     const int lane = lane_id(), row = lane & 15, g = lane >> 4;
-    const int K = a.K, r = a.r;
+    const int K = a.K, r = a.r, nks = r / 32;
     const int i = ti * 16 + row, j = tj * 16 + row;
     const int ic = min(i, K - 1), jc = min(j, K - 1);
     const int64_t rt = (int64_t)b * a.P + t;
-    int atok = (t == 0) ? prev : a.cand[(rt - 1) * K + ic];
-    int ctok = a.cand[rt * K + jc];
+    int atok = (t == 0) ? prev : xload(a.cand + (rt - 1) * K + ic);
+    int ctok = xload(a.cand + rt * K + jc);
+    const float u = xload(a.cval + rt * K + jc);
     // Ids outside [0, V) (possible only from a caller's own candidate list)
     // are replaced by token 0 and flagged, so the gathers stay in bounds.
     if ((unsigned)atok >= (unsigned)a.V || (unsigned)ctok >= (unsigned)a.V) {
@@ -70,50 +74,74 @@ __device__ void pair_tile(const TailArgs& a, int b, int t, int ti, int tj, int p
         atok = ((unsigned)atok >= (unsigned)a.V) ? 0 : atok;
         ctok = ((unsigned)ctok >= (unsigned)a.V) ? 0 : ctok;
     }
-    const float* Hr = a.H + rt * r;
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // k steps in batches of four: all row loads of a batch are in flight
+    // together.
     if constexpr (BF16) {
         const uint16_t* Ar = reinterpret_cast<const uint16_t*>(a.A) + (int64_t)atok * r;
         const uint16_t* Br = reinterpret_cast<const uint16_t*>(a.Bt) + (int64_t)ctok * r;
-        for (int ks = 0; ks < r / 32; ++ks) {
-            const int k0 = ks * 32 + g * 8;
-            const u32x4_t av = *reinterpret_cast<const u32x4_t*>(Ar + k0);
-            const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(Br + k0);
-            const float4 h0 = *reinterpret_cast<const float4*>(Hr + k0);
-            const float4 h1 = *reinterpret_cast<const float4*>(Hr + k0 + 4);
-            const float gv[8] = {bf16_lo(av.x) * h0.x, bf16_hi(av.x) * h0.y,
-                                 bf16_lo(av.y) * h0.z, bf16_hi(av.y) * h0.w,
-                                 bf16_lo(av.z) * h1.x, bf16_hi(av.z) * h1.y,
-                                 bf16_lo(av.w) * h1.z, bf16_hi(av.w) * h1.w};
-            bf16x8_t hi, lo;
+        for (int ks0 = 0; ks0 < nks; ks0 += 4) {
+            u32x4_t av[4], bv[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 hb = (__bf16)gv[e];
-                hi[e] = hb;
-                lo[e] = (__bf16)(gv[e] - (float)hb);
+            for (int q = 0; q < 4; ++q) {
+                const int k0 = (ks0 + q) * 32 + g * 8;
+                if (ks0 + q < nks) {
+                    av[q] = *reinterpret_cast<const u32x4_t*>(Ar + k0);
+                    bv[q] = *reinterpret_cast<const u32x4_t*>(Br + k0);
+                }
             }
-            acc = mfma_bf16(hi, as_bf16x8(bv), acc);
-            acc = mfma_bf16(lo, as_bf16x8(bv), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (ks0 + q >= nks) break;
+                const int k0 = (ks0 + q) * 32 + g * 8;
+                const float4 h0 = *reinterpret_cast<const float4*>(Hs + k0);
+                const float4 h1 = *reinterpret_cast<const float4*>(Hs + k0 + 4);
+                const float gv[8] = {bf16_lo(av[q].x) * h0.x, bf16_hi(av[q].x) * h0.y,
+                                     bf16_lo(av[q].y) * h0.z, bf16_hi(av[q].y) * h0.w,
+                                     bf16_lo(av[q].z) * h1.x, bf16_hi(av[q].z) * h1.y,
+                                     bf16_lo(av[q].w) * h1.z, bf16_hi(av[q].w) * h1.w};
+                bf16x8_t hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const __bf16 hb = (__bf16)gv[e];
+                    hi[e] = hb;
+                    lo[e] = (__bf16)(gv[e] - (float)hb);
+                }
+                acc = mfma_bf16(hi, as_bf16x8(bv[q]), acc);
+                acc = mfma_bf16(lo, as_bf16x8(bv[q]), acc);
+            }
         }
     } else {
         const float* Ar = reinterpret_cast<const float*>(a.A) + (int64_t)atok * r;
         const float* Br = reinterpret_cast<const float*>(a.Bt) + (int64_t)ctok * r;
-        for (int ks = 0; ks < r / 32; ++ks) {
-            const int k0 = ks * 32 + g * 8;
-            const float4 a0 = *reinterpret_cast<const float4*>(Ar + k0);
-            const float4 a1 = *reinterpret_cast<const float4*>(Ar + k0 + 4);
-            const float4 b0 = *reinterpret_cast<const float4*>(Br + k0);
-            const float4 b1 = *reinterpret_cast<const float4*>(Br + k0 + 4);
-            const float4 h0 = *reinterpret_cast<const float4*>(Hr + k0);
-            const float4 h1 = *reinterpret_cast<const float4*>(Hr + k0 + 4);
-            const float gv[8] = {a0.x * h0.x, a0.y * h0.y, a0.z * h0.z, a0.w * h0.w,
-                                 a1.x * h1.x, a1.y * h1.y, a1.z * h1.z, a1.w * h1.w};
-            const float bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        for (int ks0 = 0; ks0 < nks; ks0 += 2) {
+            float4 av[2][2], bv[2][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = mfma_f32(gv[e], bw[e], acc);
+            for (int q = 0; q < 2; ++q) {
+                const int k0 = (ks0 + q) * 32 + g * 8;
+                if (ks0 + q < nks) {
+                    av[q][0] = *reinterpret_cast<const float4*>(Ar + k0);
+                    av[q][1] = *reinterpret_cast<const float4*>(Ar + k0 + 4);
+                    bv[q][0] = *reinterpret_cast<const float4*>(Br + k0);
+                    bv[q][1] = *reinterpret_cast<const float4*>(Br + k0 + 4);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (ks0 + q >= nks) break;
+                const int k0 = (ks0 + q) * 32 + g * 8;
+                const float4 h0 = *reinterpret_cast<const float4*>(Hs + k0);
+                const float4 h1 = *reinterpret_cast<const float4*>(Hs + k0 + 4);
+                const float gv[8] = {av[q][0].x * h0.x, av[q][0].y * h0.y, av[q][0].z * h0.z,
+                                     av[q][0].w * h0.w, av[q][1].x * h1.x, av[q][1].y * h1.y,
+                                     av[q][1].z * h1.z, av[q][1].w * h1.w};
+                const float bw[8] = {bv[q][0].x, bv[q][0].y, bv[q][0].z, bv[q][0].w,
+                                     bv[q][1].x, bv[q][1].y, bv[q][1].z, bv[q][1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = mfma_f32(gv[e], bw[e], acc);
+            }
         }
     }
-    const float u = a.cval[rt * K + jc];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int ii = ti * 16 + g * 4 + v;
@@ -124,7 +152,7 @@ __device__ void pair_tile(const TailArgs& a, int b, int t, int ti, int tj, int p
 // Scores and/or walk for sequence b.  Every thread of the workgroup calls it.
 template <bool BF16>
 __device__ void tail_seq(const TailArgs& a, int b, int mode, TailLds& sm) {
-    const int K = a.K, P = a.P;
+    const int K = a.K, P = a.P, r = a.r;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nT = (K + 15) / 16;
     const int KK = K * K;
@@ -138,13 +166,14 @@ __device__ void tail_seq(const TailArgs& a, int b, int mode, TailLds& sm) {
         }
     }
     float delta = -INFINITY;
+    int hw_t = -1;                       // position whose H row this wave holds
     for (int t0 = 0; t0 < P; t0 += G) {
         const int t1 = min(P, t0 + G);
         if (mode == kTailWalkOnly) {
             for (int x = tid; x < (t1 - t0) * KK; x += kWG) {
                 const int tt = t0 + x / KK, rem = x % KK;
                 const int i = (tt == 0) ? 0 : rem / K, j = rem % K;
-                sm.S[x] = a.in_S[(((int64_t)b * P + tt) * K + i) * K + j];
+                sm.S[x] = xload(a.in_S + (((int64_t)b * P + tt) * K + i) * K + j);
             }
         } else {
             const int items = (t1 - t0) * nT * nT;
@@ -152,7 +181,18 @@ __device__ void tail_seq(const TailArgs& a, int b, int mode, TailLds& sm) {
                 const int tt = t0 + it / (nT * nT), rem = it % (nT * nT);
                 const int ti = rem / nT, tj = rem % nT;
                 if (tt == 0 && ti > 0) continue;   // at t = 0 every row is row 0
-                pair_tile<BF16>(a, b, tt, ti, tj, prev, sm.S + (tt - t0) * KK);
+                if (hw_t != tt) {                  // stage H_t in this wave's LDS row
+                    const uint64_t* Hr =
+                        reinterpret_cast<const uint64_t*>(a.H + ((int64_t)b * P + tt) * r);
+                    for (int q = lane; q < r / 2; q += 64) {
+                        const uint64_t v = xload(Hr + q);
+                        sm.Hw[w][2 * q] = __uint_as_float((uint32_t)v);
+                        sm.Hw[w][2 * q + 1] = __uint_as_float((uint32_t)(v >> 32));
+                    }
+                    wave_sync();
+                    hw_t = tt;
+                }
+                pair_tile<BF16>(a, b, tt, ti, tj, prev, sm.Hw[w], sm.S + (tt - t0) * KK);
             }
         }
         __syncthreads();
@@ -169,14 +209,26 @@ __device__ void tail_seq(const TailArgs& a, int b, int mode, TailLds& sm) {
                     delta = (lane < K) ? St[lane] : -INFINITY;
                     continue;
                 }
+                // delta_{t-1}[i] is broadcast from lane i with readlane; the
+                // column S_t[., lane] is read from LDS 16 rows at a time.
                 float best = -INFINITY;
                 int arg = 0;
-                for (int i = 0; i < K; ++i) {
-                    const float di = __shfl(delta, i);
-                    const float v = di + ((lane < K) ? St[i * K + lane] : 0.f);
-                    if (v > best) {
-                        best = v;
-                        arg = i;
+                for (int i0 = 0; i0 < K; i0 += 16) {
+                    float sv[16];
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        sv[q] = (i0 + q < K && lane < K) ? St[(i0 + q) * K + lane] : 0.f;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        if (i0 + q < K) {
+                            const float di = __int_as_float(
+                                __builtin_amdgcn_readlane(__float_as_int(delta), i0 + q));
+                            const float v = di + sv[q];
+                            if (v > best) {
+                                best = v;
+                                arg = i0 + q;
+                            }
+                        }
                     }
                 }
                 delta = (lane < K) ? best : -INFINITY;
@@ -192,10 +244,15 @@ __device__ void tail_seq(const TailArgs& a, int b, int mode, TailLds& sm) {
         if (lane == 0) {
             int j = jb;
             for (int t = P - 1; t >= 0; --t) {
-                a.out_path[(int64_t)b * P + t] = a.cand[((int64_t)b * P + t) * K + j];
+                sm.rank[t] = j;
                 if (t > 0) j = sm.psi[t * K + j];
             }
             a.out_score[b] = m;
+        }
+        wave_sync();
+        if (lane < P) {
+            const int64_t rt = (int64_t)b * P + lane;
+            a.out_path[rt] = xload(a.cand + rt * K + sm.rank[lane]);
         }
     }
 }

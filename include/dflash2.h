@@ -66,7 +66,7 @@ typedef enum {
  *      token (1 <= P <= 64)
  *   V  vocabulary size (K <= V < 2^31)
  *   d  drafter hidden size (multiple of 32)
- *   r  embedding rank of A, B and H (multiple of 64, <= 1024); the pages use 256
+ *   r  embedding rank of A, B and H (multiple of 64, <= 512); the pages use 256
  */
 typedef struct df2_dims {
     int32_t B, P, V, d, r;

@@ -65,6 +65,7 @@ def _select(lib, dims, K=16, ptrs=None):
     (Dims(1, 7, 32000, 1000, 256, 1), 16, DF2_EUNSUPPORTED, "d must be"),
     (Dims(1, 7, 32000, 1024, 200, 1), 16, DF2_EUNSUPPORTED, "r must be"),
     (Dims(1, 7, 32000, 1024, 2048, 1), 16, DF2_EUNSUPPORTED, "r must be"),
+    (Dims(1, 7, 32000, 1024, 576, 1), 16, DF2_EUNSUPPORTED, "r must be"),
     (Dims(1, 7, 32000, 1024, 256, 1), 0, DF2_EINVAL, "K must be"),
     (Dims(1, 7, 32000, 1024, 256, 1), 65, DF2_EINVAL, "K must be"),
     (Dims(1, 7, 10, 1024, 256, 1), 11, DF2_EINVAL, "K must be"),
