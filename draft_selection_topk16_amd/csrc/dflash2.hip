@@ -6,17 +6,19 @@
 // adjacent pair with S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, and walks
 // the scores once from the last verified token.
 //
-// dflash2_select runs everything in ONE launch.  The grid holds two kinds of
-// workgroups that run side by side:
-//   * gate workgroups (the first n_proj): one slice of one H tile each;
-//   * segment workgroups: one contiguous vocabulary segment of one logits row
-//     each, streamed chunk by chunk.
-// Work that needs several workgroups' results is done by whichever of them
-// arrives last on a counter (no workgroup ever waits for another):
-//   * the last segment of a row merges the row's candidates;
-//   * the last slice of an H tile sums the slices;
-//   * the last of a sequence's row merges and H tiles runs the pair scores
-//     and the walk for that sequence.
+// dflash2_select runs everything in ONE launch.  Every workgroup has up to
+// two jobs, in this order:
+//   * one slice of one H tile (the first n_proj workgroups); the last slice
+//     of a tile to arrive sums the tile's slices;
+//   * one contiguous vocabulary segment of one logits row (the first n_chunk
+//     workgroups), streamed chunk by chunk, leaving a sorted list of K
+//     candidates.
+// Doing both in one workgroup keeps the grid small enough that segments do
+// not queue for a free slot behind separate gate workgroups.
+// Segment workgroups and summed H tiles then arrive on their sequence's
+// counter (no workgroup ever waits for another).  The last to arrive
+// finishes the sequence: it merges the rows' segment lists, scores the
+// candidate pairs and walks the scores.
 // Counters live in the scratch buffer and are reset by the workgroup that
 // consumes them, so every launch starts from zero without a memset.
 #include <hip/hip_runtime.h>
@@ -32,8 +34,8 @@
 
 #include "dflash2.h"
 #include "common.hpp"
+#include "finish.hpp"
 #include "project.hpp"
-#include "tail.hpp"
 #include "topk.hpp"
 
 using namespace df2;
@@ -56,7 +58,7 @@ struct Params {
     uint64_t* part;       // [rows, nseg, K] candidate words
     int32_t* cand;        // [rows, K]
     float* cval;          // [rows, K]
-    float* ppart;         // [S, M, r] gate partials (S > 1)
+    float* ppart;         // [S, M, r] gate partials
     float* H;             // [M, r]
     uint32_t* err;        // device input-error flags
     uint32_t* row_cnt;    // [rows]
@@ -70,25 +72,29 @@ struct Params {
     int cps;              // chunks per segment
     int aligned;          // logits rows are 16-byte aligned and V % per-vector == 0
     int mtiles, qtiles, S, n_proj;
+    int64_t n_chunk;      // segment workgroups (rows * nseg)
 };
 
 union SharedAll {
     ChunkLds c;
-    MergeLds m;
     ProjLds p;
-    TailLds t;
+    FinLds f;
 };
 
-__device__ __forceinline__ TailArgs tail_args(const Params& p) {
-    TailArgs a;
-    a.cand = p.cand;
-    a.cval = p.cval;
+__device__ __forceinline__ FinArgs fin_args(const Params& p) {
+    FinArgs a;
+    a.part = p.part;
+    a.cand = nullptr;
+    a.cval = nullptr;
     a.H = p.H;
     a.A = p.A;
     a.Bt = p.Bt;
     a.prev = p.prev;
     a.in_S = nullptr;
+    a.in_cand = nullptr;
     a.out_S = nullptr;
+    a.cand_out = p.cand;
+    a.cval_out = p.cval;
     a.out_path = p.out_path;
     a.out_score = p.out_score;
     a.err = p.err;
@@ -96,20 +102,39 @@ __device__ __forceinline__ TailArgs tail_args(const Params& p) {
     a.V = p.V;
     a.r = p.r;
     a.K = p.K;
+    a.nseg = p.nseg;
     return a;
 }
 
-// Arrivals a sequence waits for: its P row merges plus every H tile that
-// covers one of its rows.
+// Arrivals a sequence waits for: its P * nseg segments plus every H tile
+// that covers one of its rows (one arrival per tile, once H is summed).
 __device__ __forceinline__ uint32_t seq_expected(const Params& p, int b) {
     const int lo = b * p.P, hi = b * p.P + p.P - 1;
     const int n_mt = hi / 16 - lo / 16 + 1;
-    return (uint32_t)(p.P + p.qtiles * n_mt);
+    return (uint32_t)(p.P * p.nseg + p.qtiles * n_mt);
 }
 
+// Arrival on the counters of sequences [b_lo, b_hi] (at most 16); returns
+// the mask of those whose last arrival this was.  One thread per counter.
+__device__ uint32_t arrive_seqs(const Params& p, int b_lo, int b_hi, uint32_t* flag) {
+    drain_stores();
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int b = b_lo + (int)threadIdx.x;
+        bool last = false;
+        if (b <= b_hi) last = arrive(&p.seq_cnt[b]) == seq_expected(p, b) - 1u;
+        const uint64_t bal = __ballot(last);
+        if (threadIdx.x == 0) *flag = (uint32_t)bal;
+    }
+    __syncthreads();
+    return *flag;
+}
+
+// A workgroup's role; returns a bit mask of the sequences (from *b0 on)
+// whose finish falls to this workgroup (fused launches only).
 template <bool BF16, int NV>
-__device__ void chunk_role(const Params& p, int64_t sb, bool fused, SharedAll& sm,
-                           uint32_t* flag) {
+__device__ uint32_t chunk_role(const Params& p, int64_t sb, bool fused, SharedAll& sm,
+                               uint32_t* flag, int* b0) {
     const int64_t row = sb / p.nseg;
     const int seg = (int)(sb % p.nseg);
     const size_t esz = BF16 ? 2 : 4;
@@ -117,74 +142,89 @@ __device__ void chunk_role(const Params& p, int64_t sb, bool fused, SharedAll& s
     const int c0 = seg * p.cps, c1 = min(p.C, c0 + p.cps);
     segment_topk<BF16, NV>(rowp, p.V, c0, c1, p.K, p.aligned != 0,
                            p.part + ((size_t)row * p.nseg + seg) * p.K, sm.c);
-    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, flag)) return;
-    merge_row<BF16>(p.part + (size_t)row * p.nseg * p.K, p.nseg, p.K, p.cand + row * p.K,
-                    p.cval + row * p.K, sm.m);
-    if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
-    if (!fused) return;
+    if (!fused) {
+        if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, flag)) return 0;
+        merge_row<BF16>(p.part + (size_t)row * p.nseg * p.K, p.nseg, p.K, p.cand + row * p.K,
+                        p.cval + row * p.K, sm.c);
+        if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
+        return 0;
+    }
     const int b = (int)(row / p.P);
-    if (!block_arrive_last(&p.seq_cnt[b], seq_expected(p, b), flag)) return;
-    tail_seq<BF16>(tail_args(p), b, kTailFull, sm.t);
-    if (threadIdx.x == 0) reset_counter(&p.seq_cnt[b]);
+    *b0 = b;
+    return arrive_seqs(p, b, b, flag);
 }
 
 template <bool BF16, int NQ>
-__device__ void proj_role(const Params& p, int pb, bool fused, SharedAll& sm, uint32_t* flag) {
+__device__ uint32_t proj_role(const Params& p, int pb, bool fused, SharedAll& sm, uint32_t* flag,
+                              int* b0) {
     const int s = pb % p.S, tile = pb / p.S;
     const int mt = tile / p.qtiles, qt = tile % p.qtiles;
     const int M = (int)p.rows;
-    proj_block<BF16, NQ>(p.hidden, p.W, M, p.d, p.r, mt, qt, s, p.S,
-                         p.S > 1 ? p.ppart : p.H, sm.p);
+    proj_block<BF16, NQ>(p.hidden, p.W, M, p.d, p.r, mt, qt, s, p.S, p.S == 1 ? p.H : p.ppart,
+                         sm.p);
     if (p.S > 1) {
-        if (!block_arrive_last(&p.tile_cnt[tile], (uint32_t)p.S, flag)) return;
+        // the last slice of the tile to arrive sums the slices into H
+        if (!block_arrive_last(&p.tile_cnt[tile], (uint32_t)p.S, flag)) return 0;
         proj_reduce_tile<NQ>(p.ppart, M, p.r, mt, qt, p.S, p.H);
         if (threadIdx.x == 0) reset_counter(&p.tile_cnt[tile]);
     }
-    if (!fused) return;
+    if (!fused) return 0;
+    // a tile's 16 rows touch at most 16 sequences
     const int b_lo = (mt * 16) / p.P;
     const int b_hi = (min(M, mt * 16 + 16) - 1) / p.P;
-    for (int b = b_lo; b <= b_hi; ++b) {
-        if (block_arrive_last(&p.seq_cnt[b], seq_expected(p, b), flag)) {
-            tail_seq<BF16>(tail_args(p), b, kTailFull, sm.t);
-            if (threadIdx.x == 0) reset_counter(&p.seq_cnt[b]);
-        }
-    }
+    *b0 = b_lo;
+    return arrive_seqs(p, b_lo, b_hi, flag);
 }
 
-// The whole selector in one launch.
+// The whole selector in one launch.  Workgroup g computes H tile slice g
+// first (g < n_proj; slice s of every tile lands on XCD s when there are
+// eight slices, as workgroups are dealt to the XCDs round-robin), then
+// streams segment g (g < n_chunk), then finishes the sequences whose last
+// arrival it made.
 template <bool BF16, int NV, int NQ>
-__global__ __launch_bounds__(kWG) void k_select(Params p) {
+__global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
     const int64_t g = blockIdx.x;
-    if (g < p.n_proj) {
-        proj_role<BF16, NQ>(p, (int)g, true, sm, &flag);
-    } else {
-        chunk_role<BF16, NV>(p, g - p.n_proj, true, sm, &flag);
+    int pb0 = 0, cb0 = 0;
+    uint32_t pmask = 0, cmask = 0;
+    if (g < p.n_proj) pmask = proj_role<BF16, NQ>(p, (int)g, true, sm, &flag, &pb0);
+    if (g < p.n_chunk) cmask = chunk_role<BF16, NV>(p, g, true, sm, &flag, &cb0);
+    // a 16-bit gate mask and the segment's own sequence, in one word
+    uint32_t mask = pmask | (cmask << 16);
+    while (mask) {
+        const int bit = __builtin_ctz(mask);
+        mask &= mask - 1u;
+        const int b = (bit < 16) ? pb0 + bit : cb0;
+        finish_seq<BF16, kFinFused>(fin_args(p), b, sm.f);
+        __syncthreads();
+        if (threadIdx.x == 0) reset_counter(&p.seq_cnt[b]);
     }
 }
 
 // Top-K alone: chunk workgroups with the row merge on last arrival.
 template <bool BF16, int NV>
-__global__ __launch_bounds__(kWG) void k_topk(Params p) {
+__global__ __launch_bounds__(kWG, 5) void k_topk(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
-    chunk_role<BF16, NV>(p, blockIdx.x, false, sm, &flag);
+    int b0 = 0;
+    chunk_role<BF16, NV>(p, blockIdx.x, false, sm, &flag, &b0);
 }
 
 // Gate projection alone.
 template <bool BF16, int NQ>
-__global__ __launch_bounds__(kWG) void k_project(Params p) {
+__global__ __launch_bounds__(kWG, 5) void k_project(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
-    proj_role<BF16, NQ>(p, blockIdx.x, false, sm, &flag);
+    int b0 = 0;
+    proj_role<BF16, NQ>(p, blockIdx.x, false, sm, &flag, &b0);
 }
 
 // Pair scores alone (written to global memory), or the walk alone.
-template <bool BF16>
-__global__ __launch_bounds__(kWG) void k_tail(TailArgs a, int mode) {
-    __shared__ TailLds sm;
-    tail_seq<BF16>(a, blockIdx.x, mode, sm);
+template <bool BF16, int mode>
+__global__ __launch_bounds__(kWG, 5) void k_finish(FinArgs a) {
+    __shared__ FinLds sm;
+    finish_seq<BF16, mode>(a, blockIdx.x, sm);
 }
 
 // ----------------------------------------------------------------------------
@@ -297,7 +337,7 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, (target + rows - 1) / rows));
     int cps = (p.C + nseg - 1) / nseg;
     nseg = (p.C + cps - 1) / cps;
-    while ((int64_t)nseg * K > (int64_t)kWG * kMergeItems) {
+    while ((int64_t)nseg * K > kMergeMax) {
         ++cps;
         nseg = (p.C + cps - 1) / cps;
     }
@@ -308,23 +348,43 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     p.K = K;
     p.aligned = (aligned16(logits) && (V % pv) == 0) ? 1 : 0;
     pl.n_chunk_blocks = rows * nseg;
+    p.n_chunk = pl.n_chunk_blocks;
 }
 
-void plan_proj(Plan& pl, int64_t M, int d, int r) {
+// H tiles of 16 rows x 16*NQ columns, each cut into S slices of d (at most
+// eight; eight puts slice s of every tile on XCD s).  Preferred: every wave
+// issues all loads of its slice at once (one round trip), then the fewest
+// slices; and, inside a select launch, no more slices than segment
+// workgroups to host them.
+void plan_proj(Plan& pl, int64_t M, int d, int r, int64_t hosts) {
     Params& p = pl.p;
-    pl.nq = (M >= 64) ? 4 : 1;
-    int forced_nq = env_int("DF2_NQ", 0);
-    if (forced_nq == 1 || forced_nq == 4) pl.nq = forced_nq;
-    p.mtiles = (int)((M + 15) / 16);
-    p.qtiles = r / (16 * pl.nq);
-    const int tiles = p.mtiles * p.qtiles;
     const int KS = d / 32;
-    int S = 1;
-    while (S < 8 && tiles * S < 256 && KS >= 2 * S * kWaves) S *= 2;
+    p.mtiles = (int)((M + 15) / 16);
+    int best_nq = 1, best_S = 1;
+    int64_t best_key = -1;
+    for (int nq : {4, 2, 1}) {
+        const int kb = proj_kb(pl.bf16, nq);
+        int S = std::min(kMaxSlices, std::max(1, (KS + 4 * kb - 1) / (4 * kb)));
+        S = std::min(S, KS);
+        const int per_wave = ((KS + S - 1) / S + kWaves - 1) / kWaves;
+        const int64_t batches = (per_wave + kb - 1) / kb;
+        const int64_t n = (int64_t)p.mtiles * (r / (16 * nq)) * S;
+        const bool fits = hosts <= 0 || n <= std::max<int64_t>(hosts, 256);
+        const int64_t key = (fits ? 0 : (int64_t)1 << 40) + (batches << 24) + n;
+        if (best_key < 0 || key < best_key) {
+            best_key = key;
+            best_nq = nq;
+            best_S = S;
+        }
+    }
+    int forced_nq = env_int("DF2_NQ", 0);
+    if (forced_nq == 1 || forced_nq == 2 || forced_nq == 4) best_nq = forced_nq;
     int forced_s = env_int("DF2_S", 0);
-    if (forced_s >= 1 && forced_s <= KS) S = forced_s;
-    p.S = S;
-    p.n_proj = tiles * S;
+    if (forced_s >= 1 && forced_s <= std::min(KS, kMaxSlices)) best_S = forced_s;
+    pl.nq = best_nq;
+    p.qtiles = r / (16 * pl.nq);
+    p.S = best_S;
+    p.n_proj = p.mtiles * p.qtiles * p.S;
     p.d = d;
     p.r = r;
 }
@@ -343,7 +403,7 @@ void plan_layout(Plan& pl, int64_t rows, int64_t M, int B) {
     pl.off_cval = off;
     off = align_up(off + (size_t)rows * p.K * 4, 256);
     pl.off_ppart = off;
-    off = align_up(off + (p.S > 1 ? (size_t)p.S * M * p.r * 4 : 0), 256);
+    off = align_up(off + (size_t)p.S * M * p.r * 4, 256);
     pl.off_H = off;
     off = align_up(off + (size_t)M * p.r * 4, 256);
     pl.total_bytes = off;
@@ -399,11 +459,15 @@ df2_status launch_checked(F&& f, const char* what) {
     }
 
 void launch_select(const Plan& pl, hipStream_t stream) {
-    dim3 grid((unsigned)(pl.p.n_proj + pl.n_chunk_blocks)), block(kWG);
+    dim3 grid((unsigned)std::max<int64_t>(pl.p.n_proj, pl.n_chunk_blocks)), block(kWG);
     if (pl.bf16) {
-        if (pl.nq == 4) { DF2_NV_CASES(true, 4) } else { DF2_NV_CASES(true, 1) }
+        if (pl.nq == 4) { DF2_NV_CASES(true, 4) }
+        else if (pl.nq == 2) { DF2_NV_CASES(true, 2) }
+        else { DF2_NV_CASES(true, 1) }
     } else {
-        if (pl.nq == 4) { DF2_NV_CASES(false, 4) } else { DF2_NV_CASES(false, 1) }
+        if (pl.nq == 4) { DF2_NV_CASES(false, 4) }
+        else if (pl.nq == 2) { DF2_NV_CASES(false, 2) }
+        else { DF2_NV_CASES(false, 1) }
     }
 }
 
@@ -421,13 +485,14 @@ void launch_topk(const Plan& pl, hipStream_t stream) {
 
 void launch_project(const Plan& pl, hipStream_t stream) {
     dim3 grid((unsigned)pl.p.n_proj), block(kWG);
-    if (pl.bf16) {
-        if (pl.nq == 4) hipLaunchKernelGGL((k_project<true, 4>), grid, block, 0, stream, pl.p);
-        else hipLaunchKernelGGL((k_project<true, 1>), grid, block, 0, stream, pl.p);
-    } else {
-        if (pl.nq == 4) hipLaunchKernelGGL((k_project<false, 4>), grid, block, 0, stream, pl.p);
-        else hipLaunchKernelGGL((k_project<false, 1>), grid, block, 0, stream, pl.p);
+#define DF2_PROJ(BF)                                                                            \
+    switch (pl.nq) {                                                                            \
+        case 4: hipLaunchKernelGGL((k_project<BF, 4>), grid, block, 0, stream, pl.p); break;   \
+        case 2: hipLaunchKernelGGL((k_project<BF, 2>), grid, block, 0, stream, pl.p); break;   \
+        default: hipLaunchKernelGGL((k_project<BF, 1>), grid, block, 0, stream, pl.p); break;  \
     }
+    if (pl.bf16) { DF2_PROJ(true) } else { DF2_PROJ(false) }
+#undef DF2_PROJ
 }
 
 }  // namespace
@@ -474,7 +539,7 @@ df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* 
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     plan_topk(pl, rows, dims->V, K, bf16, logits);
-    plan_proj(pl, rows, dims->d, dims->r);
+    plan_proj(pl, rows, dims->d, dims->r, pl.n_chunk_blocks);
     plan_layout(pl, rows, rows, dims->B);
     Params& p = pl.p;
     p.logits = logits;
@@ -547,7 +612,7 @@ df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M, int32
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = dtype == DF2_BF16;
-    plan_proj(pl, M, d, r);
+    plan_proj(pl, M, d, r, 0);
     pl.p.C = 0;
     pl.p.K = 0;
     plan_layout(pl, 0, M, 0);
@@ -579,7 +644,7 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
         return fail(DF2_EINVAL, "H, A_tab and B_tab must be 16-byte aligned");
     void* base = nullptr;
     if ((st = get_scratch(stream, 256, 4, &base)) != DF2_OK) return st;
-    TailArgs a;
+    FinArgs a;
     std::memset(&a, 0, sizeof(a));
     a.cand = cand_idx;
     a.cval = cand_val;
@@ -593,12 +658,13 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
     a.V = dims->V;
     a.r = dims->r;
     a.K = K;
+    a.nseg = 1;
     dim3 grid((unsigned)dims->B), block(kWG);
     return launch_checked([&] {
         if (dims->dtype == DF2_BF16)
-            hipLaunchKernelGGL((k_tail<true>), grid, block, 0, stream, a, (int)kTailScoresOnly);
+            hipLaunchKernelGGL((k_finish<true, kFinScores>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((k_tail<false>), grid, block, 0, stream, a, (int)kTailScoresOnly);
+            hipLaunchKernelGGL((k_finish<false, kFinScores>), grid, block, 0, stream, a);
     }, "dflash2_pair_scores launch");
 }
 
@@ -610,18 +676,20 @@ df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, i
     if (K < 1 || K > kMaxK) return fail(DF2_EINVAL, "K must be in [1, 64]");
     if (B == 0) return DF2_OK;
     if (!S || !cand_idx || !out_path || !out_score) return fail(DF2_EINVAL, "NULL pointer argument");
-    TailArgs a;
+    FinArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.cand = cand_idx;
+    a.in_cand = cand_idx;
     a.in_S = S;
     a.out_path = out_path;
     a.out_score = out_score;
     a.P = P;
     a.K = K;
+    a.r = 64;
+    a.nseg = 1;
     a.V = 0x7FFFFFFF;
     dim3 grid((unsigned)B), block(kWG);
     return launch_checked([&] {
-        hipLaunchKernelGGL((k_tail<true>), grid, block, 0, stream, a, (int)kTailWalkOnly);
+        hipLaunchKernelGGL((k_finish<true, kFinWalk>), grid, block, 0, stream, a);
     }, "dflash2_viterbi launch");
 }
 

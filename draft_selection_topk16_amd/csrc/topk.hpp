@@ -19,49 +19,51 @@
 // maximum of the chunk is the bound.  Once a few chunks have been seen, most
 // chunks have no lane that reaches the bound and cost a handful of
 // instructions.  Vectors that do reach it are keyed exactly from
-// registers; words that beat the K-th kept word are compacted (ballot) and
-// merged into the list with all ranks found in parallel.  No step of a chunk
+// registers; words that beat the K-th kept word are compacted (ballot) into
+// an LDS buffer, which is merged into the list (all ranks found in parallel)
+// once to establish it and then only when it fills.  No step of a chunk
 // needs a workgroup barrier.
-// At the end of the segment the four waves' lists are ranked together.
+// At the end of the segment the four waves' lists are merged the same way.
 //
-// Stage 2 (merge): the last segment workgroup of a row to finish merges the
-// segments' K candidate words with a bound-then-rank scheme (per-wave bounds
-// over lane maxima of the words).
+// Stage 2 (merge): the segments' sorted lists of K candidate words are merged
+// by one wave (wave_merge_lists): a bound (the best K-th word of any list),
+// in-place compaction of the words that reach it, and ranks by counting.
 //
 // Candidate words (key << 32 | ~index) are distinct within a row, so every
 // selection is exact and independent of arrival order: results are
 // deterministic.
 #pragma once
 
+#include <math.h>
+
 #include "common.hpp"
 
 namespace df2 {
 
 constexpr int kMaxNV = 4;           // 16-byte vectors per lane per chunk
-constexpr int kMergeItems = 8;      // candidate words per thread (merge)
-constexpr int kMergeCap = 512;      // survivors ranked in LDS (merge)
+constexpr int kMergeMax = 128;      // words merged per row (segment lists * K)
+constexpr int kListWords = 256;     // words one wave merge takes (the four waves' lists, K <= 64)
+static_assert(kMergeMax <= kWG, "one word per thread when a row is loaded");
+static_assert(kMergeMax <= kListWords, "a row merge fits one wave merge");
 
-constexpr int kWCand = 256;         // candidate words buffered per wave before a merge
+constexpr int kWCand = 256;         // candidate words buffered per wave
+constexpr int kWPend = 64;          // pending vectors per wave before a flush
 
 struct WaveLds {
-    u32x4_t slot[64];                   // surviving vectors, one per lane at most
-    uint32_t slot_lane[64];
+    u32x4_t pend[kWPend];               // surviving vectors awaiting keying
+    uint32_t pend_e0[kWPend];           // row index of each one's first element
     uint64_t cand[kWCand];
-    uint64_t L[64];                     // the list, published for a merge
     uint64_t L2[64];                    // the merged list
 };
 
 struct ChunkLds {
     WaveLds wv[kWaves];
     uint64_t fin[kWaves * 64];          // the waves' lists at the end of a segment
-    uint32_t bound;                     // best K-th kept key among the four waves
-};
-
-struct MergeLds {
-    uint64_t thr[kWaves];
-    uint32_t red[kWaves];
-    uint32_t n;
-    uint64_t list[kMergeCap];
+    uint32_t lkey[kWG];                 // lane maxima of the first chunk
+    uint32_t bound;                     // a key at least K values of the segment reach
+    uint32_t qkey[kWaves];              // each wave's ceil(K/4)-th kept key
+    uint64_t top[64];                   // merge output
+    uint64_t rowlist[kMergeMax];        // a row's segment lists (row merge)
 };
 
 template <bool BF16>
@@ -187,63 +189,180 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Merges m distinct candidate words c[0..m) into the sorted list held one
-// word per lane (lane k: k-th best; unfilled slots and lanes >= K hold 0) and
-// returns the best K.  Every word finds its new rank in parallel: a list word
-// counts the candidates above it; a candidate binary-searches the sorted list
-// and counts the candidates above it.  Ranks below K are scattered to LDS.
+// Top K of nl sorted lists of K words (lists[l * K + k], descending, zero
+// padded), by one wave: emit(rank, word) is called once for every word of
+// rank < K.  Bound T: a word that at least K words reach, so every word of
+// the top K is >= T.  Two such words are known from the lists' order: the
+// largest K-th word of any list (that list alone holds K words that reach
+// it), and the smallest c-th word over all lists with c = ceil(K / nl)
+// (every list holds c words that reach it).  Words >= T are compacted in
+// place and ranked by counting.  nl * K <= kListWords.
+template <typename Emit>
+__device__ void wave_merge_lists_emit(uint64_t* lists, int nl, int K, Emit&& emit) {
+    const int lane = lane_id();
+    const int n = nl * K;
+    const int c = (K + nl - 1) / nl;
+    // LDS reads are issued eight at a time (indexes clamped into range) so
+    // that loops do not wait for each read in turn.
+    uint64_t Tk = 0, Tc = ~0ull;
+    for (int l0 = 0; l0 < nl; l0 += 8) {
+        uint64_t tk[8], tc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int l = min(l0 + j, nl - 1);
+            tk[j] = lists[l * K + K - 1];
+            tc[j] = lists[l * K + c - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            Tk = tk[j] > Tk ? tk[j] : Tk;
+            Tc = tc[j] < Tc ? tc[j] : Tc;
+        }
+    }
+    uint64_t T = Tk > Tc ? Tk : Tc;
+    T = T ? T : 1ull;
+    uint64_t x[kListWords / 64];
+#pragma unroll
+    for (int q = 0; q < kListWords / 64; ++q) {
+        const int e = q * 64 + lane;
+        x[q] = (e < n) ? lists[e] : 0ull;
+    }
+    wave_sync();
+    int m = 0;
+#pragma unroll
+    for (int q = 0; q < kListWords / 64; ++q) {
+        if (q * 64 < n) {
+            const bool s = x[q] >= T;
+            const uint64_t bal = __ballot(s);
+            if (s) lists[m + __popcll(bal & ((1ull << lane) - 1ull))] = x[q];
+            m += __popcll(bal);
+        }
+    }
+    wave_sync();
+    for (int s0 = 0; s0 < m; s0 += 64) {
+        const int si = s0 + lane;
+        const uint64_t y = (si < m) ? lists[si] : 0ull;
+        int rank = 0;
+        for (int u0 = 0; u0 < m; u0 += 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = lists[min(u0 + j, m - 1)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rank += (u0 + j < m && v[j] > y) ? 1 : 0;
+        }
+        if (si < m && rank < K) emit(rank, y);
+    }
+    wave_sync();
+}
+
+// The same, returning the k-th best word in lane k (0 where there is none);
+// top: K words of LDS.
+__device__ uint64_t wave_merge_lists(uint64_t* lists, int nl, int K, uint64_t* top) {
+    const int lane = lane_id();
+    if (lane < K) top[lane] = 0ull;
+    wave_sync();
+    wave_merge_lists_emit(lists, nl, K, [&](int rank, uint64_t y) { top[rank] = y; });
+    const uint64_t res = (lane < K) ? top[lane] : 0ull;
+    wave_sync();
+    return res;
+}
+
+// Merges m distinct candidate words c[0..m) (LDS, written by this wave) into
+// the sorted list held one word per lane (lane k: k-th best; unfilled slots
+// and lanes >= K hold 0) and returns the best K.  Candidates are taken 64 at
+// a time, one per lane; every rank is counted from registers (readlane over
+// the candidates and over the list), then the words whose rank is below K
+// are scattered through LDS.
 __device__ __forceinline__ uint64_t list_merge(uint64_t tk, const uint64_t* c, int m, int K,
                                                WaveLds& sm) {
     const int lane = lane_id();
-    if (lane < K) sm.L[lane] = tk;
-    sm.L2[lane] = 0;
     wave_sync();
-    if (lane < K && tk != 0) {
-        int r = lane;
-        int i = 0;
-        for (; i + 4 <= m; i += 4)
-            r += (c[i] > tk) + (c[i + 1] > tk) + (c[i + 2] > tk) + (c[i + 3] > tk);
-        for (; i < m; ++i) r += (c[i] > tk);
-        if (r < K) sm.L2[r] = tk;
-    }
-    for (int q = lane; q < m; q += 64) {
-        const uint64_t x = c[q];
-        int lo = 0, hi = K;                     // list words above x: first L[idx] < x
-#pragma unroll
-        for (int step = 0; step < 7; ++step) {
-            if (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (sm.L[mid] > x) lo = mid + 1;
-                else hi = mid;
-            }
+    for (int base = 0; base < m; base += 64) {
+        const int mg = min(64, m - base);
+        const uint64_t ci = (lane < mg) ? c[base + lane] : 0ull;
+        int rc = 0;         // candidates above ci
+        int rl = lane;      // new rank of the list word tk
+        for (int i = 0; i < mg; ++i) {
+            const uint64_t x = readlane_u64(ci, i);
+            rc += (x > ci) ? 1 : 0;
+            rl += (x > tk) ? 1 : 0;
         }
-        int r = lo;
-        int i = 0;
-        for (; i + 4 <= m; i += 4)
-            r += (c[i] > x) + (c[i + 1] > x) + (c[i + 2] > x) + (c[i + 3] > x);
-        for (; i < m; ++i) r += (c[i] > x);
-        if (r < K) sm.L2[r] = x;
+        int rk = 0;         // list words above ci
+        for (int k = 0; k < K; ++k) rk += (readlane_u64(tk, k) > ci) ? 1 : 0;
+        sm.L2[lane] = 0ull;
+        wave_sync();
+        if (lane < K && tk != 0 && rl < K) sm.L2[rl] = tk;
+        if (lane < mg && rc + rk < K) sm.L2[rc + rk] = ci;
+        wave_sync();
+        tk = (lane < K) ? sm.L2[lane] : 0ull;
+        wave_sync();
     }
-    wave_sync();
-    return (lane < K) ? sm.L2[lane] : 0ull;
+    return tk;
 }
 
-// Folds one wave chunk (in registers) into the wave's sorted list tk.
+// Keys the wave's pending vectors and merges every word that beats the K-th
+// kept word (and reaches Tm) into the sorted list tk.
+template <bool BF16>
+__device__ uint64_t flush_pending(int V, int K, uint32_t Tm, uint64_t tk, int np, WaveLds& sm) {
+    using E = Elem<BF16>;
+    constexpr int PV = E::kPerVec;
+    const int lane = lane_id();
+    uint64_t kth = readlane_u64(tk, K - 1);
+    Tm = max(Tm, (uint32_t)(kth >> 32));
+    wave_sync();
+    int n = 0;
+    const int nel = np * PV;
+#pragma unroll 1
+    for (int e0 = 0; e0 < nel; e0 += 64) {
+        const int e = e0 + lane;
+        bool pred = false;
+        uint64_t word = 0;
+        if (e < nel) {
+            const int sl = e / PV, p = e % PV;
+            const uint32_t wd = reinterpret_cast<const uint32_t*>(&sm.pend[sl])[BF16 ? (p >> 1) : p];
+            const uint32_t bits = BF16 ? ((p & 1) ? (wd >> 16) : (wd & 0xFFFFu)) : wd;
+            const int64_t gidx = (int64_t)sm.pend_e0[sl] + p;
+            const uint32_t key = E::key(bits);
+            word = cand_word(key, (uint32_t)gidx);
+            pred = gidx < V && key >= Tm && word > kth;
+        }
+        const uint64_t b2 = __ballot(pred);
+        if (pred) sm.cand[n + __popcll(b2 & ((1ull << lane) - 1ull))] = word;
+        n += __popcll(b2);
+        if (n > kWCand - 64) {
+            tk = list_merge(tk, sm.cand, n, K, sm);
+            n = 0;
+            kth = readlane_u64(tk, K - 1);
+            Tm = max(Tm, (uint32_t)(kth >> 32));
+        }
+    }
+    if (n > 0) tk = list_merge(tk, sm.cand, n, K, sm);
+    wave_sync();            // the pending slots are rewritten next
+    return tk;
+}
+
+// Folds one wave chunk (in registers) into the wave's state: the sorted list
+// tk and np pending vectors (vectors that reach the bound, not yet keyed).
 //   eb: row index of the chunk's first element; lane l, vector j, element p
 //   hold element eb + (j * 64 + l) * kPerVec + p.
 //   trow: a key that at least K values of the row are known to reach (the
 //   best K-th kept key among the workgroup's waves; 0 if none known).
 template <bool BF16, int NV, bool ALIGNED>
 __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV], uint64_t tk,
-                               uint32_t trow, WaveLds& sm) {
+                               uint32_t trow, int& np, WaveLds& sm) {
     using E = Elem<BF16>;
     constexpr int PV = E::kPerVec;
     const int lane = lane_id();
     u32x4_t v[NV];
+    uint32_t vk[NV];
+    uint32_t skey = 0;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = mask_vec<ALIGNED>(raw[j], eb + (int64_t)(j * 64 + lane) * PV, V);
-    const uint32_t skey = lane_max_key<BF16, NV>(v);
-    uint64_t kth = readlane_u64(tk, K - 1);     // 0 while the list is filling
+    for (int j = 0; j < NV; ++j) {
+        v[j] = mask_vec<ALIGNED>(raw[j], eb + (int64_t)(j * 64 + lane) * PV, V);
+        vk[j] = vec_max_key<BF16>(v[j]);
+        skey = max(skey, vk[j]);
+    }
+    const uint64_t kth = readlane_u64(tk, K - 1);     // 0 while the list is filling
     uint32_t Tm = max((uint32_t)(kth >> 32), trow);
     if (Tm == 0) {
         // Nothing known yet: the K-th largest lane maximum of this chunk, by
@@ -257,51 +376,25 @@ __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV
         Tm = T;
     }
     Tm = max(Tm, 1u);                           // real values have key >= 1
-    const bool lane_in = skey >= Tm;
-    if (__ballot(lane_in) == 0) return tk;      // the common case
-    // Vectors that reach the bound go to LDS slots (one per lane at most per
-    // vector index); the wave keys their elements and buffers every word that
-    // beats the K-th kept word (ballot compaction), merging when the buffer
-    // fills.
-    int n = 0;
+    if (__ballot(skey >= Tm) == 0) return tk;   // the common case
+    // Vectors that reach the bound wait in LDS; they are keyed and merged in
+    // batches (flush_pending), so a chunk only pays for copying them.
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const bool vin = lane_in && vec_max_key<BF16>(v[j]) >= Tm;
+        const bool vin = vk[j] >= Tm;
         const uint64_t bal = __ballot(vin);
         if (bal == 0) continue;
+        if (np + __popcll(bal) > kWPend) {
+            tk = flush_pending<BF16>(V, K, Tm, tk, np, sm);
+            np = 0;
+        }
         if (vin) {
-            const int slot = __popcll(bal & ((1ull << lane) - 1ull));
-            sm.slot[slot] = v[j];
-            sm.slot_lane[slot] = lane;
+            const int slot = np + __popcll(bal & ((1ull << lane) - 1ull));
+            sm.pend[slot] = v[j];
+            sm.pend_e0[slot] = (uint32_t)(eb + (int64_t)(j * 64 + lane) * PV);
         }
-        wave_sync();
-        const int nel = __popcll(bal) * PV;
-#pragma unroll 1
-        for (int e0 = 0; e0 < nel; e0 += 64) {
-            const int e = e0 + lane;
-            bool pred = false;
-            uint64_t word = 0;
-            if (e < nel) {
-                const int sl = e / PV, p = e % PV;
-                const uint32_t wd = reinterpret_cast<const uint32_t*>(&sm.slot[sl])[BF16 ? (p >> 1) : p];
-                const uint32_t bits = BF16 ? ((p & 1) ? (wd >> 16) : (wd & 0xFFFFu)) : wd;
-                const int64_t gidx = eb + (int64_t)(j * 64 + (int)sm.slot_lane[sl]) * PV + p;
-                const uint32_t key = E::key(bits);
-                word = cand_word(key, (uint32_t)gidx);
-                pred = gidx < V && key >= Tm && word > kth;
-            }
-            const uint64_t b2 = __ballot(pred);
-            if (pred) sm.cand[n + __popcll(b2 & ((1ull << lane) - 1ull))] = word;
-            n += __popcll(b2);
-            if (n > kWCand - 64) {
-                tk = list_merge(tk, sm.cand, n, K, sm);
-                kth = readlane_u64(tk, K - 1);
-                n = 0;
-            }
-        }
-        wave_sync();
+        np += __popcll(bal);
     }
-    if (n > 0) tk = list_merge(tk, sm.cand, n, K, sm);
     return tk;
 }
 
@@ -318,22 +411,38 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     constexpr int WE = 64 * PV * NV;           // elements per wave chunk
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     uint64_t tk = 0;
-    uint32_t published = 0;
+    int npend = 0;                             // pending vectors of this wave
+    const int kq = (K + kWaves - 1) / kWaves;
     auto eb_of = [&](int c) { return ((int64_t)c * kWaves + w) * WE; };
-    if (tid == 0) sm.bound = 0;
-    __syncthreads();
-    // Publishes the wave's K-th kept key as a bound for the whole workgroup;
-    // a wave may read an older (smaller) bound, which is still valid.
+    // Publishes two bounds that at least K values of the segment reach: the
+    // wave's own K-th kept key (raises sm.bound), and its ceil(K/4)-th kept
+    // key -- the four waves hold disjoint values, so the smallest of their
+    // four such keys is reached by at least K values.  Each word only grows;
+    // a reader may see an older value, which is still a valid bound.
     auto publish = [&]() {
         const uint32_t kk = (uint32_t)(readlane_u64(tk, K - 1) >> 32);
-        if (kk > published) {
-            if (lane == 0)
-                __hip_atomic_fetch_max(&sm.bound, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            published = kk;
+        const uint32_t qq = (uint32_t)(readlane_u64(tk, kq - 1) >> 32);
+        if (lane == 0) {
+            __hip_atomic_fetch_max(&sm.bound, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&sm.qkey[w], qq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     };
     auto wg_bound = [&]() {
-        return __hip_atomic_load(&sm.bound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        uint32_t q = __hip_atomic_load(&sm.qkey[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int u = 1; u < kWaves; ++u)
+            q = min(q, __hip_atomic_load(&sm.qkey[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        return max(q, __hip_atomic_load(&sm.bound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    };
+    // Flushes pending vectors once the buffer is half full (or at the end),
+    // filtered by the best bound known now, then republishes the bounds.
+    auto settle = [&](bool last) {
+        if (npend >= kWPend / 2 || (last && npend > 0)) {
+            const uint32_t Tb = max(wg_bound(), 1u);
+            tk = flush_pending<BF16>(V, K, Tb, tk, npend, sm.wv[w]);
+            npend = 0;
+            if (!last) publish();
+        }
     };
     // Two register buffers, used in turn without copies: while one chunk is
     // processed the next one's loads are in flight.  Past the segment end a
@@ -343,13 +452,36 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(c0) + (int64_t)(j * 64 + lane) * PV);
+    {
+        // Initial bound: the K-th largest of the workgroup's 256 lane maxima
+        // over its first chunk (one barrier per segment).
+        u32x4_t v[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            v[j] = mask_vec<ALIGNED>(b0[j], eb_of(c0) + (int64_t)(j * 64 + lane) * PV, V);
+        sm.lkey[tid] = lane_max_key<BF16, NV>(v);
+        if (tid < kWaves) sm.qkey[tid] = 0;
+        __syncthreads();
+        const uint32_t q0 = sm.lkey[lane], q1 = sm.lkey[lane + 64];
+        const uint32_t q2 = sm.lkey[lane + 128], q3 = sm.lkey[lane + 192];
+        uint32_t T = 0;
+#pragma unroll 1
+        for (int bit = Elem<BF16>::kKeyBits - 1; bit >= 0; --bit) {
+            const uint32_t c = T | (1u << bit);
+            const int cnt = ballot_count(q0 >= c) + ballot_count(q1 >= c) + ballot_count(q2 >= c) +
+                            ballot_count(q3 >= c);
+            if (cnt >= K) T = c;
+        }
+        if (tid == 0) sm.bound = T;
+        __syncthreads();
+    }
     for (int c = c0; c < c1; c += 2) {
         const int cn = min(c + 1, clast);
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             b1[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(cn) + (int64_t)(j * 64 + lane) * PV);
-        tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c), K, b0, tk, wg_bound(), sm.wv[w]);
-        publish();
+        tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c), K, b0, tk, wg_bound(), npend, sm.wv[w]);
+        settle(false);
         // Keep the next half's uses of its loads below this point: hoisting
         // one would wait on every load in flight, prefetch included.
         __builtin_amdgcn_sched_barrier(0);
@@ -358,26 +490,18 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(cnn) + (int64_t)(j * 64 + lane) * PV);
-        tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c + 1), K, b1, tk, wg_bound(), sm.wv[w]);
-        publish();
+        tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c + 1), K, b1, tk, wg_bound(), npend, sm.wv[w]);
+        settle(false);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // Rank the four waves' lists together; the best K leave in order.
+    settle(true);
+    // Merge the four waves' sorted lists; the best K leave in order.
     if (lane < K) sm.fin[w * K + lane] = tk;
     __syncthreads();
-    const int n = kWaves * K;
-    uint32_t nreal = 0;
-    for (int u = 0; u < n; ++u) nreal += (sm.fin[u] != 0) ? 1u : 0u;
-    if (tid < n) {
-        const uint64_t x = sm.fin[tid];
-        if (x != 0) {
-            uint32_t rank = 0;
-            for (int u = 0; u < n; ++u) rank += (sm.fin[u] > x) ? 1u : 0u;
-            if (rank < (uint32_t)K) xstore(out + rank, x);
-        }
+    if (w == 0) {
+        const uint64_t x = wave_merge_lists(sm.fin, kWaves, K, sm.top);
+        if (lane < K) xstore(out + lane, x);
     }
-    // slots beyond the number of real words stay empty
-    for (int k = (int)nreal + tid; k < K; k += kWG) xstore(out + k, (uint64_t)0);
 }
 
 template <bool BF16, int NV>
@@ -392,76 +516,23 @@ __device__ void segment_topk(const void* __restrict__ row, int V, int c0, int c1
         segment_topk_impl<BF16, 1, false>(row, V, c0 * NV, c1 * NV, K, out, sm);
 }
 
-// Stage 2: merge the K candidate words of each of `nchunks` chunks of a row
-// into the row's top-K, written as (index, value).
+// Stage 2: merge the nseg sorted segment lists of a row (K words each,
+// nseg * K <= kMergeMax) into the row's top-K, written as (index, value).
 template <bool BF16>
-__device__ void merge_row(const uint64_t* __restrict__ part, int nchunks, int K,
+__device__ void merge_row(const uint64_t* __restrict__ part, int nseg, int K,
                           int32_t* __restrict__ out_idx, float* __restrict__ out_val,
-                          MergeLds& sm) {
+                          ChunkLds& sm) {
     using E = Elem<BF16>;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nitems = nchunks * K;     // host guarantees <= kWG * kMergeItems
-    uint64_t it[kMergeItems];
-    uint64_t mx = 0;
-#pragma unroll
-    for (int q = 0; q < kMergeItems; ++q) {
-        int i = tid + q * kWG;
-        it[q] = (i < nitems) ? xload(part + i) : 0ull;
-        mx = it[q] > mx ? it[q] : mx;
-    }
-    // candidate words of bf16 rows are below 2^48 (16-bit keys)
-    const int top = BF16 ? 47 : 63;
-    uint64_t T = 0;
-#pragma unroll 1
-    for (int bit = top; bit >= 0; --bit) {
-        uint64_t c = T | (1ull << bit);
-        if (ballot_count(mx >= c) >= K) T = c;
-    }
-    if (lane == 0) sm.thr[w] = T;
-    if (tid == 0) sm.n = 0;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int n = nseg * K;     // <= kMergeMax <= kWG
+    const uint64_t x = xload(part + min(tid, n - 1));
+    if (tid < n) sm.rowlist[tid] = x;
     __syncthreads();
-    T = sm.thr[0];
-#pragma unroll
-    for (int q = 1; q < kWaves; ++q) T = sm.thr[q] > T ? sm.thr[q] : T;
-    if (T == 0) T = 1;
-#pragma unroll
-    for (int q = 0; q < kMergeItems; ++q) {
-        if (it[q] >= T) {
-            uint32_t pos = atomicAdd(&sm.n, 1u);
-            if (pos < (uint32_t)kMergeCap) sm.list[pos] = it[q];
-        }
-    }
-    __syncthreads();
-    if (sm.n > (uint32_t)kMergeCap) {
-        // Exact fallback: bitwise search for the K-th largest word.
-        uint64_t T64 = 0;
-#pragma unroll 1
-        for (int bit = top; bit >= 0; --bit) {
-            uint64_t c = T64 | (1ull << bit);
-            uint32_t cnt = 0;
-#pragma unroll
-            for (int q = 0; q < kMergeItems; ++q) cnt += (it[q] >= c && it[q] != 0) ? 1u : 0u;
-            if (block_sum_u32(cnt, sm.red) >= (uint32_t)K) T64 = c;
-        }
-        if (tid == 0) sm.n = 0;
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < kMergeItems; ++q) {
-            if (it[q] != 0 && it[q] >= T64) {
-                uint32_t pos = atomicAdd(&sm.n, 1u);
-                sm.list[pos] = it[q];
-            }
-        }
-        __syncthreads();
-    }
-    const uint32_t n = sm.n;
-    for (uint32_t c = tid; c < n; c += kWG) {
-        uint64_t x = sm.list[c];
-        uint32_t rank = 0;
-        for (uint32_t u = 0; u < n; ++u) rank += (sm.list[u] > x) ? 1u : 0u;
-        if (rank < (uint32_t)K) {
-            xstore(out_idx + rank, (int32_t)cand_index(x));
-            xstore(out_val + rank, E::value((uint32_t)(x >> 32)));
+    if (tid < 64) {
+        const uint64_t y = wave_merge_lists(sm.rowlist, nseg, K, sm.top);
+        if (lane < K) {
+            out_idx[lane] = y ? (int32_t)cand_index(y) : 0;
+            out_val[lane] = y ? E::value((uint32_t)(y >> 32)) : -INFINITY;
         }
     }
 }
