@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "path-select µs/cycle at B=1, drafted positions/s at B=32; % HBM peak"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("common.hpp", "topk.hpp", "project.hpp", "finish.hpp", "dflash2.hip")
+KERNEL_SOURCES = ("common.hpp", "topk.hpp", "gate.hpp", "pairs.hpp", "walk.hpp", "dflash2.hip")
 
 
 def log(*a):

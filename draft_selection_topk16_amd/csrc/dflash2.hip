@@ -6,19 +6,25 @@
 // adjacent pair with S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, and walks
 // the scores once from the last verified token.
 //
-// dflash2_select runs everything in ONE launch.  Every workgroup has up to
-// two jobs, in this order:
-//   * one slice of one H tile (the first n_proj workgroups); the last slice
-//     of a tile to arrive sums the tile's slices;
-//   * one contiguous vocabulary segment of one logits row (the first n_chunk
-//     workgroups), streamed chunk by chunk, leaving a sorted list of K
-//     candidates.
-// Doing both in one workgroup keeps the grid small enough that segments do
-// not queue for a free slot behind separate gate workgroups.
-// Segment workgroups and summed H tiles then arrive on their sequence's
-// counter (no workgroup ever waits for another).  The last to arrive
-// finishes the sequence: it merges the rows' segment lists, scores the
-// candidate pairs and walks the scores.
+// dflash2_select runs everything in ONE launch.  Workgroups are dealt out in
+// index order, and each one's job follows from its index:
+//   * the first n_gate compute one slice of one gate tile (a partial of H)
+//     and count it on the tile row's counter;
+//   * every other one streams one contiguous vocabulary segment of one
+//     logits row, leaving a sorted list of K candidates, and arrives on the
+//     row's counter.
+// The work after that is handed on by "last arrival": nobody waits for a
+// producer except for the gate, below.
+//   row:      the last segment of a row merges the row's lists into its
+//             top-K (ids and logits) and arrives on the counters of the two
+//             transitions the row takes part in (t - 1 -> t and t -> t + 1);
+//   pairs:    the second row of a transition to arrive scores it (the first
+//             transition of a sequence needs only its own row);
+//   walk:     the last transition of a sequence to be scored walks it.
+// The pair scores sum H_t from the gate partials; they wait (bounded spin)
+// for the gate tile row to be complete.  Gate workgroups have the lowest
+// indexes and never wait, so they have all been dispatched by the time any
+// pair job runs, and every wait ends.
 // Counters live in the scratch buffer and are reset by the workgroup that
 // consumes them, so every launch starts from zero without a memset.
 #include <hip/hip_runtime.h>
@@ -34,9 +40,10 @@
 
 #include "dflash2.h"
 #include "common.hpp"
-#include "finish.hpp"
-#include "project.hpp"
+#include "gate.hpp"
+#include "pairs.hpp"
 #include "topk.hpp"
+#include "walk.hpp"
 
 using namespace df2;
 
@@ -54,177 +61,269 @@ struct Params {
     const int32_t* prev;
     int32_t* out_path;
     float* out_score;
+    float* H;             // standalone projection output [M, r]
     // scratch
     uint64_t* part;       // [rows, nseg, K] candidate words
     int32_t* cand;        // [rows, K]
     float* cval;          // [rows, K]
     float* ppart;         // [S, M, r] gate partials
-    float* H;             // [M, r]
+    float* Sb;            // [rows, K, K] pair scores
     uint32_t* err;        // device input-error flags
-    uint32_t* row_cnt;    // [rows]
-    uint32_t* tile_cnt;   // [mtiles * qtiles]
-    uint32_t* seq_cnt;    // [B]
+    uint32_t* row_cnt;    // [rows] segments done
+    uint32_t* edge_cnt;   // [rows] rows ready of transition t - 1 -> t
+    uint32_t* seq_cnt;    // [B] transitions scored
+    uint32_t* gate_cnt;   // [mtiles] gate slices done
+    uint32_t* rd_cnt;     // [mtiles] pair jobs past the gate wait
     // sizes
     int B, P, V, d, r, K;
     int64_t rows;
     int C;                // chunks per row
     int nseg;             // segments per row
-    int cps;              // chunks per segment
     int aligned;          // logits rows are 16-byte aligned and V % per-vector == 0
-    int mtiles, qtiles, S, n_proj;
+    int gm_rows;          // rows per gate tile
+    int mtiles, ntiles, S, n_gate;
     int64_t n_chunk;      // segment workgroups (rows * nseg)
+    int64_t base;         // index of the launch's first workgroup
 };
 
 union SharedAll {
     ChunkLds c;
-    ProjLds p;
-    FinLds f;
+    MergeLds m;
+    GateLds g;
+    PairLds pr;
+    WalkLds wk;
+};
+// Five workgroups per CU: the LDS a workgroup asks for must stay well under
+// a fifth of the CU's 160 KB (32 KB blocks would leave room for four).
+static_assert(sizeof(SharedAll) + 64 <= 30720, "LDS budget of five workgroups per CU");
+
+template <int MB>
+struct GateShape {
+    static constexpr int NB = MB == 1 ? 4 : 2;
 };
 
-__device__ __forceinline__ FinArgs fin_args(const Params& p) {
-    FinArgs a;
-    a.part = p.part;
-    a.cand = nullptr;
-    a.cval = nullptr;
-    a.H = p.H;
-    a.A = p.A;
-    a.Bt = p.Bt;
-    a.prev = p.prev;
-    a.in_S = nullptr;
-    a.in_cand = nullptr;
-    a.out_S = nullptr;
-    a.cand_out = p.cand;
-    a.cval_out = p.cval;
-    a.out_path = p.out_path;
-    a.out_score = p.out_score;
-    a.err = p.err;
-    a.P = p.P;
-    a.V = p.V;
-    a.r = p.r;
-    a.K = p.K;
-    a.nseg = p.nseg;
-    return a;
-}
-
-// Arrivals a sequence waits for: its P * nseg segments plus every H tile
-// that covers one of its rows (one arrival per tile, once H is summed).
-__device__ __forceinline__ uint32_t seq_expected(const Params& p, int b) {
-    const int lo = b * p.P, hi = b * p.P + p.P - 1;
-    const int n_mt = hi / 16 - lo / 16 + 1;
-    return (uint32_t)(p.P * p.nseg + p.qtiles * n_mt);
-}
-
-// Arrival on the counters of sequences [b_lo, b_hi] (at most 16); returns
-// the mask of those whose last arrival this was.  One thread per counter.
-__device__ uint32_t arrive_seqs(const Params& p, int b_lo, int b_hi, uint32_t* flag) {
+// One slice of one gate tile, counted on the tile row's counter once its
+// partial is stored.
+template <bool BF16, int MB>
+__device__ void gate_role(const Params& p, int gb, GateLds& sm) {
+    const int s = gb % p.S, tile = gb / p.S;
+    const int mt = tile / p.ntiles, nt = tile % p.ntiles;
+    gate_slice<BF16, MB, GateShape<MB>::NB>(p.hidden, p.W, (int)p.rows, p.d, p.r, mt, nt, s, p.S,
+                                            p.ppart, sm);
     drain_stores();
     __syncthreads();
-    if (threadIdx.x < 64) {
-        const int b = b_lo + (int)threadIdx.x;
-        bool last = false;
-        if (b <= b_hi) last = arrive(&p.seq_cnt[b]) == seq_expected(p, b) - 1u;
-        const uint64_t bal = __ballot(last);
-        if (threadIdx.x == 0) *flag = (uint32_t)bal;
-    }
-    __syncthreads();
-    return *flag;
+    if (threadIdx.x == 0) arrive(&p.gate_cnt[mt]);
 }
 
-// A workgroup's role; returns a bit mask of the sequences (from *b0 on)
-// whose finish falls to this workgroup (fused launches only).
 template <bool BF16, int NV>
-__device__ uint32_t chunk_role(const Params& p, int64_t sb, bool fused, SharedAll& sm,
-                               uint32_t* flag, int* b0) {
-    const int64_t row = sb / p.nseg;
-    const int seg = (int)(sb % p.nseg);
+__device__ void segment_of(const Params& p, int64_t row, int seg, ChunkLds& sm) {
     const size_t esz = BF16 ? 2 : 4;
     const char* rowp = reinterpret_cast<const char*>(p.logits) + (size_t)row * p.V * esz;
-    const int c0 = seg * p.cps, c1 = min(p.C, c0 + p.cps);
-    segment_topk<BF16, NV>(rowp, p.V, c0, c1, p.K, p.aligned != 0,
-                           p.part + ((size_t)row * p.nseg + seg) * p.K, sm.c);
-    if (!fused) {
-        if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, flag)) return 0;
-        merge_row<BF16>(p.part + (size_t)row * p.nseg * p.K, p.nseg, p.K, p.cand + row * p.K,
-                        p.cval + row * p.K, sm.c);
-        if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
+    segment_topk<BF16, NV>(rowp, p.V, p.C, seg, p.nseg, p.K, p.aligned != 0,
+                           p.part + ((size_t)row * p.nseg + seg) * p.K, sm);
+}
+
+__device__ __forceinline__ int32_t checked_id(int32_t id, int V, uint32_t* err, uint32_t bit) {
+    if ((unsigned)id >= (unsigned)V) {
+        atomicOr(err, bit);
         return 0;
     }
-    const int b = (int)(row / p.P);
-    *b0 = b;
-    return arrive_seqs(p, b, b, flag);
+    return id;
 }
 
-template <bool BF16, int NQ>
-__device__ uint32_t proj_role(const Params& p, int pb, bool fused, SharedAll& sm, uint32_t* flag,
-                              int* b0) {
-    const int s = pb % p.S, tile = pb / p.S;
-    const int mt = tile / p.qtiles, qt = tile % p.qtiles;
-    const int M = (int)p.rows;
-    proj_block<BF16, NQ>(p.hidden, p.W, M, p.d, p.r, mt, qt, s, p.S, p.S == 1 ? p.H : p.ppart,
-                         sm.p);
-    if (p.S > 1) {
-        // the last slice of the tile to arrive sums the slices into H
-        if (!block_arrive_last(&p.tile_cnt[tile], (uint32_t)p.S, flag)) return 0;
-        proj_reduce_tile<NQ>(p.ppart, M, p.r, mt, qt, p.S, p.H);
-        if (threadIdx.x == 0) reset_counter(&p.tile_cnt[tile]);
+// Pair scores of positions e0 .. e0 + ne - 1 of sequence b (fused launch).
+template <bool BF16>
+__device__ void pairs_fused(const Params& p, int b, int e0, int ne, PairLds& sm) {
+    const int tid = threadIdx.x, K = p.K;
+    const int64_t rb = (int64_t)b * p.P;
+    // Candidate ids come from the row merges and are always in [0, V); they
+    // are still checked, so that no gather can leave the tables.
+    if (tid < K) {
+        int32_t id;
+        if (e0 > 0) {
+            id = checked_id(xload(p.cand + (rb + e0 - 1) * K + tid), p.V, p.err, 2u);
+        } else {
+            id = p.prev[b];
+            if ((unsigned)id >= (unsigned)p.V) {
+                if (tid == 0) atomicOr(p.err, 1u);
+                id = 0;
+            }
+        }
+        sm.ids[0][tid] = id;
+    } else if (tid >= 64 && tid < 64 + ne * K) {
+        const int x = tid - 64, q = x / K, k = x % K;
+        sm.ids[1 + q][k] = checked_id(xload(p.cand + (rb + e0 + q) * K + k), p.V, p.err, 2u);
+        sm.u[q][k] = xload(p.cval + (rb + e0 + q) * K + k);
+    } else if (tid >= 192 && tid < 192 + ne) {
+        // the gate tile row of the position's row must be complete
+        const int64_t grow = rb + e0 + (tid - 192);
+        const int mt = (int)(grow / p.gm_rows);
+        const uint32_t need = (uint32_t)(p.ntiles * p.S);
+        uint32_t it = 0;
+        while (xload(&p.gate_cnt[mt]) < need) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it > (1u << 20)) {
+                atomicOr(p.err, 4u);
+                break;
+            }
+        }
+        // the last of the tile row's pair jobs resets its counters
+        const int64_t lo = (int64_t)mt * p.gm_rows;
+        const uint32_t rows_in = (uint32_t)(std::min<int64_t>(p.rows, lo + p.gm_rows) - lo);
+        if (arrive(&p.rd_cnt[mt]) == rows_in - 1u) {
+            reset_counter(&p.gate_cnt[mt]);
+            reset_counter(&p.rd_cnt[mt]);
+        }
     }
-    if (!fused) return 0;
-    // a tile's 16 rows touch at most 16 sequences
-    const int b_lo = (mt * 16) / p.P;
-    const int b_hi = (min(M, mt * 16 + 16) - 1) / p.P;
-    *b0 = b_lo;
-    return arrive_seqs(p, b_lo, b_hi, flag);
+    __syncthreads();
+    pair_tiles<BF16>(p.A, p.Bt, K, p.r, e0, ne, p.Sb + (rb + e0) * K * K, sm, [&]() {
+        pair_sum_gate(p.ppart, p.S, p.rows, p.r, rb + e0, ne, sm);
+    });
 }
 
-// The whole selector in one launch.  Workgroup g computes H tile slice g
-// first (g < n_proj; slice s of every tile lands on XCD s when there are
-// eight slices, as workgroups are dealt to the XCDs round-robin), then
-// streams segment g (g < n_chunk), then finishes the sequences whose last
-// arrival it made.
-template <bool BF16, int NV, int NQ>
+// The whole selector in one launch.
+template <bool BF16, int NV, int MB>
 __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
-    const int64_t g = blockIdx.x;
-    int pb0 = 0, cb0 = 0;
-    uint32_t pmask = 0, cmask = 0;
-    if (g < p.n_proj) pmask = proj_role<BF16, NQ>(p, (int)g, true, sm, &flag, &pb0);
-    if (g < p.n_chunk) cmask = chunk_role<BF16, NV>(p, g, true, sm, &flag, &cb0);
-    // a 16-bit gate mask and the segment's own sequence, in one word
-    uint32_t mask = pmask | (cmask << 16);
-    while (mask) {
-        const int bit = __builtin_ctz(mask);
-        mask &= mask - 1u;
-        const int b = (bit < 16) ? pb0 + bit : cb0;
-        finish_seq<BF16, kFinFused>(fin_args(p), b, sm.f);
-        __syncthreads();
-        if (threadIdx.x == 0) reset_counter(&p.seq_cnt[b]);
+    const int tid = threadIdx.x;
+    const int64_t g = blockIdx.x + p.base;
+    if (g < p.n_gate) {
+        // the gate and everything after a segment are on the critical path;
+        // the streaming waves that share the SIMDs mostly wait on memory
+        __builtin_amdgcn_s_setprio(3);
+        gate_role<BF16, MB>(p, (int)g, sm.g);
+        return;
     }
+    const int64_t sb = g - p.n_gate;
+    const int64_t row = sb / p.nseg;
+    segment_of<BF16, NV>(p, row, (int)(sb % p.nseg), sm.c);
+    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
+    __builtin_amdgcn_s_setprio(3);
+    if (tid == 0) reset_counter(&p.row_cnt[row]);
+    const int K = p.K, P = p.P;
+    merge_row<BF16>(p.part + (size_t)row * p.nseg * K, p.nseg, K, p.cand + row * K,
+                    p.cval + row * K, sm.m);
+    // arrive on the transitions into and out of this row
+    const int b = (int)(row / P), t = (int)(row % P);
+    drain_stores();
+    __syncthreads();
+    if (tid < 64) {
+        bool mine = false;
+        if (tid == 0) mine = (t == 0) || arrive(&p.edge_cnt[row]) == 1u;
+        if (tid == 1 && t + 1 < P) mine = arrive(&p.edge_cnt[row + 1]) == 1u;
+        const uint64_t bal = __ballot(mine);
+        if (tid == 0) flag = (uint32_t)bal & 3u;
+    }
+    __syncthreads();
+    const uint32_t em = flag;
+    if (!em) return;
+    if (tid == 0 && (em & 1u) && t > 0) reset_counter(&p.edge_cnt[row]);
+    if (tid == 1 && (em & 2u)) reset_counter(&p.edge_cnt[row + 1]);
+    const int e0 = (em & 1u) ? t : t + 1;
+    const int ne = (em == 3u) ? 2 : 1;
+    pairs_fused<BF16>(p, b, e0, ne, sm.pr);
+    drain_stores();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&p.seq_cnt[b], (uint32_t)ne, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        flag = (old + (uint32_t)ne == (uint32_t)P) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!flag) return;
+    if (tid == 0) reset_counter(&p.seq_cnt[b]);
+    const int64_t rb = (int64_t)b * P;
+    walk_seq(p.Sb + rb * K * K, p.cand + rb * K, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
-// Top-K alone: chunk workgroups with the row merge on last arrival.
+// Top-K alone: segments, then the row merge on last arrival.
 template <bool BF16, int NV>
 __global__ __launch_bounds__(kWG, 5) void k_topk(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
-    int b0 = 0;
-    chunk_role<BF16, NV>(p, blockIdx.x, false, sm, &flag, &b0);
+    const int64_t row = blockIdx.x / p.nseg;
+    segment_of<BF16, NV>(p, row, (int)(blockIdx.x % p.nseg), sm.c);
+    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
+    if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
+    merge_row<BF16>(p.part + (size_t)row * p.nseg * p.K, p.nseg, p.K, p.cand + row * p.K,
+                    p.cval + row * p.K, sm.m);
 }
 
-// Gate projection alone.
-template <bool BF16, int NQ>
-__global__ __launch_bounds__(kWG, 5) void k_project(Params p) {
-    __shared__ SharedAll sm;
-    __shared__ uint32_t flag;
-    int b0 = 0;
-    proj_role<BF16, NQ>(p, blockIdx.x, false, sm, &flag, &b0);
+// Gate projection alone: slices into H (S == 1) or into partials.
+template <bool BF16, int MB>
+__global__ __launch_bounds__(kWG) void k_gate(Params p) {
+    __shared__ GateLds sm;
+    const int s = (int)(blockIdx.x % p.S), tile = (int)(blockIdx.x / p.S);
+    gate_slice<BF16, MB, GateShape<MB>::NB>(p.hidden, p.W, (int)p.rows, p.d, p.r,
+                                            tile / p.ntiles, tile % p.ntiles, s, p.S,
+                                            p.S == 1 ? p.H : p.ppart, sm);
 }
 
-// Pair scores alone (written to global memory), or the walk alone.
-template <bool BF16, int mode>
-__global__ __launch_bounds__(kWG, 5) void k_finish(FinArgs a) {
-    __shared__ FinLds sm;
-    finish_seq<BF16, mode>(a, blockIdx.x, sm);
+// H = sum of the S partials, in slice order; one thread per four floats.
+__global__ __launch_bounds__(kWG) void k_gate_sum(const float* __restrict__ part, int S,
+                                                  int64_t n4, float* __restrict__ H) {
+    const int64_t i = (int64_t)blockIdx.x * kWG + threadIdx.x;
+    if (i >= n4) return;
+    const float4* src = reinterpret_cast<const float4*>(part);
+    float4 acc = src[i];
+    for (int s = 1; s < S; ++s) {
+        const float4 v = src[(int64_t)s * n4 + i];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(H)[i] = acc;
+}
+
+// Pair scores alone: one workgroup per (sequence, position).
+struct PairArgs {
+    const int32_t* cand;
+    const float* cval;
+    const float* H;
+    const void* A;
+    const void* Bt;
+    const int32_t* prev;
+    float* out_S;
+    uint32_t* err;
+    int B, P, V, r, K;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kWG) void k_pairs(PairArgs a) {
+    __shared__ PairLds sm;
+    const int tid = threadIdx.x, K = a.K;
+    const int b = (int)(blockIdx.x / a.P), e = (int)(blockIdx.x % a.P);
+    const int64_t rb = (int64_t)b * a.P;
+    if (tid < K) {
+        sm.ids[0][tid] = (e > 0) ? checked_id(a.cand[(rb + e - 1) * K + tid], a.V, a.err, 2u)
+                                 : checked_id(a.prev[b], a.V, a.err, 1u);
+    } else if (tid >= 64 && tid < 64 + K) {
+        const int k = tid - 64;
+        sm.ids[1][k] = checked_id(a.cand[(rb + e) * K + k], a.V, a.err, 2u);
+        sm.u[0][k] = a.cval[(rb + e) * K + k];
+    }
+    __syncthreads();
+    pair_tiles<BF16>(a.A, a.Bt, K, a.r, e, 1, a.out_S + (rb + e) * K * K, sm, [&]() {
+        pair_sum_gate(a.H, 1, (int64_t)a.B * a.P, a.r, rb + e, 1, sm);
+    });
+}
+
+// The walk alone: one workgroup per sequence.
+struct WalkArgs {
+    const float* S;
+    const int32_t* cand;
+    int32_t* out_path;
+    float* out_score;
+    int P, K;
+};
+
+__global__ __launch_bounds__(kWG) void k_walk(WalkArgs a) {
+    __shared__ WalkLds sm;
+    const int64_t b = blockIdx.x;
+    walk_seq(a.S + b * a.P * a.K * a.K, a.cand + b * a.P * a.K, a.P, a.K, a.out_path + b * a.P,
+             a.out_score + b, sm);
 }
 
 // ----------------------------------------------------------------------------
@@ -253,6 +352,7 @@ struct Scratch {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::map<int, int> g_capacity;         // device -> resident select workgroups
 
 // Scratch of at least `bytes`, whose first `counter_bytes` are zero when the
 // stream reaches the next launch.
@@ -305,22 +405,44 @@ int env_int(const char* name, int dflt) {
     return (v && *v) ? atoi(v) : dflt;
 }
 
+// Workgroups of the select kernel that are resident at once on the current
+// device (CUs x workgroups per CU).
+int select_capacity() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1024;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_capacity.find(dev);
+        if (it != g_capacity.end()) return it->second;
+    }
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, reinterpret_cast<const void*>(&k_select<true, 4, 4>), kWG, 0) != hipSuccess)
+        per = 4;
+    const int cap = std::max(1, cus * std::max(1, per));
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_capacity[dev] = cap;
+    return cap;
+}
+
 struct Plan {
     Params p;
-    int nv = 1, nq = 1;
+    int nv = 1;
+    int mb = 4;                 // gate tile: 16*mb rows x 16*(mb == 1 ? 4 : 2) columns
     bool bf16 = true;
     int64_t n_chunk_blocks = 0;
     size_t counter_bytes = 0, total_bytes = 0;
-    size_t off_part = 0, off_cand = 0, off_cval = 0, off_ppart = 0, off_H = 0;
+    size_t off_part = 0, off_cand = 0, off_cval = 0, off_ppart = 0, off_S = 0;
 };
 
 // Chunk size (16-byte vectors per thread) and segmentation of the rows.
 // Chunks of 256 x 4 vectors keep two register buffers per thread cheap;
 // smaller chunks are used when there are too few rows to give every CU a
 // workgroup.  Rows are then cut into segments so that about `target`
-// workgroups stream in total, each pays one hand-off per segment, and the
-// row merge stays within one workgroup's registers.
-void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits) {
+// workgroups stream in total; a row's segment lists must fit one merge.
+void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits,
+               int64_t target) {
     Params& p = pl.p;
     pl.bf16 = bf16;
     const int pv = bf16 ? 8 : 4;
@@ -333,67 +455,49 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     if (forced == 1 || forced == 2 || forced == 4) nv = forced;
     pl.nv = nv;
     p.C = chunks(nv);
-    const int64_t target = std::max(1, env_int("DF2_WGS", 1024));
-    int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, (target + rows - 1) / rows));
-    int cps = (p.C + nseg - 1) / nseg;
-    nseg = (p.C + cps - 1) / cps;
-    while ((int64_t)nseg * K > kMergeMax) {
-        ++cps;
-        nseg = (p.C + cps - 1) / cps;
-    }
-    p.nseg = nseg;
-    p.cps = cps;
+    target = std::max<int64_t>(1, env_int("DF2_WGS", (int)std::min<int64_t>(target, 1 << 30)));
+    // at most kMergeMax words per row merge; fewer lists also make the merge
+    // bound sharper
+    const int max_lists = std::max(1, std::min(kMergeMax, env_int("DF2_MWORDS", 256)) / K);
+    int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, target / rows));
+    p.nseg = std::min(nseg, max_lists);
     p.rows = rows;
     p.V = V;
     p.K = K;
     p.aligned = (aligned16(logits) && (V % pv) == 0) ? 1 : 0;
-    pl.n_chunk_blocks = rows * nseg;
+    pl.n_chunk_blocks = rows * p.nseg;
     p.n_chunk = pl.n_chunk_blocks;
 }
 
-// H tiles of 16 rows x 16*NQ columns, each cut into S slices of d (at most
-// eight; eight puts slice s of every tile on XCD s).  Preferred: every wave
-// issues all loads of its slice at once (one round trip), then the fewest
-// slices; and, inside a select launch, no more slices than segment
-// workgroups to host them.
-void plan_proj(Plan& pl, int64_t M, int d, int r, int64_t hosts) {
+// Gate tiles and slices of d.  Tiles are 16 x 64 for a single tile row of
+// at most 16 rows, else 64 x 32.  A slice is at least one round of loads
+// (4 waves x gate_kb k steps); S is the largest count of such slices that
+// stays within kMaxFusedSlices (the pair scores sum the partials): many
+// short slices finish early, beside the streaming segments.  The standalone
+// projection uses the same slices, so both paths round alike.
+void plan_gate(Plan& pl, int64_t M, int d, int r) {
     Params& p = pl.p;
+    pl.mb = (M <= 16) ? 1 : 4;
+    const int nb = (pl.mb == 1) ? 4 : 2;
+    p.gm_rows = 16 * pl.mb;
+    p.mtiles = (int)((M + p.gm_rows - 1) / p.gm_rows);
+    p.ntiles = r / (16 * nb);
     const int KS = d / 32;
-    p.mtiles = (int)((M + 15) / 16);
-    int best_nq = 1, best_S = 1;
-    int64_t best_key = -1;
-    for (int nq : {4, 2, 1}) {
-        const int kb = proj_kb(pl.bf16, nq);
-        int S = std::min(kMaxSlices, std::max(1, (KS + 4 * kb - 1) / (4 * kb)));
-        S = std::min(S, KS);
-        const int per_wave = ((KS + S - 1) / S + kWaves - 1) / kWaves;
-        const int64_t batches = (per_wave + kb - 1) / kb;
-        const int64_t n = (int64_t)p.mtiles * (r / (16 * nq)) * S;
-        const bool fits = hosts <= 0 || n <= std::max<int64_t>(hosts, 256);
-        const int64_t key = (fits ? 0 : (int64_t)1 << 40) + (batches << 24) + n;
-        if (best_key < 0 || key < best_key) {
-            best_key = key;
-            best_nq = nq;
-            best_S = S;
-        }
-    }
-    int forced_nq = env_int("DF2_NQ", 0);
-    if (forced_nq == 1 || forced_nq == 2 || forced_nq == 4) best_nq = forced_nq;
-    int forced_s = env_int("DF2_S", 0);
-    if (forced_s >= 1 && forced_s <= std::min(KS, kMaxSlices)) best_S = forced_s;
-    pl.nq = best_nq;
-    p.qtiles = r / (16 * pl.nq);
-    p.S = best_S;
-    p.n_proj = p.mtiles * p.qtiles * p.S;
+    const int per_round = kWaves * gate_kb(pl.bf16);
+    int S = std::max(1, std::min(kMaxFusedSlices, (KS + per_round - 1) / per_round));
+    const int forced = env_int("DF2_S", 0);
+    if (forced >= 1 && forced <= std::min(KS, kMaxFusedSlices)) S = forced;
+    p.S = S;
+    p.n_gate = p.mtiles * p.ntiles * S;
     p.d = d;
     p.r = r;
 }
 
-// Scratch layout: counters first (err, row arrivals, tiles, sequences), then
-// data.
-void plan_layout(Plan& pl, int64_t rows, int64_t M, int B) {
+// Scratch layout: counters first (err, rows, transitions, sequences, gate
+// tile rows, gate readers), then data.
+void plan_layout(Plan& pl, int64_t rows, int64_t M, int B, bool pairs) {
     Params& p = pl.p;
-    const size_t ncnt = 1 + (size_t)rows + (size_t)p.mtiles * p.qtiles + (size_t)B;
+    const size_t ncnt = 1 + 2 * (size_t)rows + (size_t)B + 2 * (size_t)p.mtiles;
     pl.counter_bytes = align_up(ncnt * 4, 256);
     size_t off = pl.counter_bytes;
     pl.off_part = off;
@@ -403,9 +507,9 @@ void plan_layout(Plan& pl, int64_t rows, int64_t M, int B) {
     pl.off_cval = off;
     off = align_up(off + (size_t)rows * p.K * 4, 256);
     pl.off_ppart = off;
-    off = align_up(off + (size_t)p.S * M * p.r * 4, 256);
-    pl.off_H = off;
-    off = align_up(off + (size_t)M * p.r * 4, 256);
+    off = align_up(off + (p.S > 1 || pairs ? (size_t)p.S * M * p.r * 4 : 0), 256);
+    pl.off_S = off;
+    off = align_up(off + (pairs ? (size_t)rows * p.K * p.K * 4 : 0), 256);
     pl.total_bytes = off;
 }
 
@@ -415,14 +519,15 @@ void bind_scratch(Plan& pl, void* base, int64_t rows, int B) {
     uint32_t* cnt = reinterpret_cast<uint32_t*>(c);
     p.err = cnt;
     p.row_cnt = cnt + 1;
-    p.tile_cnt = cnt + 1 + rows;
-    p.seq_cnt = cnt + 1 + rows + (size_t)p.mtiles * p.qtiles;
-    (void)B;
+    p.edge_cnt = p.row_cnt + rows;
+    p.seq_cnt = p.edge_cnt + rows;
+    p.gate_cnt = p.seq_cnt + B;
+    p.rd_cnt = p.gate_cnt + p.mtiles;
     p.part = reinterpret_cast<uint64_t*>(c + pl.off_part);
     p.cand = reinterpret_cast<int32_t*>(c + pl.off_cand);
     p.cval = reinterpret_cast<float*>(c + pl.off_cval);
     p.ppart = reinterpret_cast<float*>(c + pl.off_ppart);
-    p.H = reinterpret_cast<float*>(c + pl.off_H);
+    p.Sb = reinterpret_cast<float*>(c + pl.off_S);
 }
 
 df2_status check_dims(const df2_dims* dims, bool need_d) {
@@ -451,24 +556,34 @@ df2_status launch_checked(F&& f, const char* what) {
     return DF2_OK;
 }
 
-#define DF2_NV_CASES(BF, NQ_)                                                        \
-    switch (pl.nv) {                                                                 \
-        case 1: hipLaunchKernelGGL((k_select<BF, 1, NQ_>), grid, block, 0, stream, pl.p); break; \
-        case 2: hipLaunchKernelGGL((k_select<BF, 2, NQ_>), grid, block, 0, stream, pl.p); break; \
-        default: hipLaunchKernelGGL((k_select<BF, 4, NQ_>), grid, block, 0, stream, pl.p); break; \
-    }
-
+// The gate can run as a launch of its own, before the segments (every pair
+// job then finds H complete), or inside the same launch.
 void launch_select(const Plan& pl, hipStream_t stream) {
-    dim3 grid((unsigned)std::max<int64_t>(pl.p.n_proj, pl.n_chunk_blocks)), block(kWG);
-    if (pl.bf16) {
-        if (pl.nq == 4) { DF2_NV_CASES(true, 4) }
-        else if (pl.nq == 2) { DF2_NV_CASES(true, 2) }
-        else { DF2_NV_CASES(true, 1) }
-    } else {
-        if (pl.nq == 4) { DF2_NV_CASES(false, 4) }
-        else if (pl.nq == 2) { DF2_NV_CASES(false, 2) }
-        else { DF2_NV_CASES(false, 1) }
+    const bool split = env_int("DF2_GSEP", 0) != 0;
+    Params p1 = pl.p, p2 = pl.p;
+    p2.base = split ? pl.p.n_gate : 0;
+    const int64_t n2 = split ? pl.n_chunk_blocks : pl.p.n_gate + pl.n_chunk_blocks;
+    dim3 block(kWG);
+#define DF2_SEL(BF, NV_, MB_)                                                                  \
+    do {                                                                                       \
+        if (split)                                                                             \
+            hipLaunchKernelGGL((k_select<BF, NV_, MB_>), dim3((unsigned)pl.p.n_gate), block, 0, \
+                               stream, p1);                                                    \
+        hipLaunchKernelGGL((k_select<BF, NV_, MB_>), dim3((unsigned)n2), block, 0, stream, p2); \
+    } while (0)
+#define DF2_SEL_NV(BF, MB_)                  \
+    switch (pl.nv) {                         \
+        case 1: DF2_SEL(BF, 1, MB_); break;  \
+        case 2: DF2_SEL(BF, 2, MB_); break;  \
+        default: DF2_SEL(BF, 4, MB_); break; \
     }
+    if (pl.bf16) {
+        if (pl.mb == 1) { DF2_SEL_NV(true, 1) } else { DF2_SEL_NV(true, 4) }
+    } else {
+        if (pl.mb == 1) { DF2_SEL_NV(false, 1) } else { DF2_SEL_NV(false, 4) }
+    }
+#undef DF2_SEL_NV
+#undef DF2_SEL
 }
 
 void launch_topk(const Plan& pl, hipStream_t stream) {
@@ -483,16 +598,20 @@ void launch_topk(const Plan& pl, hipStream_t stream) {
 #undef DF2_TOPK
 }
 
-void launch_project(const Plan& pl, hipStream_t stream) {
-    dim3 grid((unsigned)pl.p.n_proj), block(kWG);
-#define DF2_PROJ(BF)                                                                            \
-    switch (pl.nq) {                                                                            \
-        case 4: hipLaunchKernelGGL((k_project<BF, 4>), grid, block, 0, stream, pl.p); break;   \
-        case 2: hipLaunchKernelGGL((k_project<BF, 2>), grid, block, 0, stream, pl.p); break;   \
-        default: hipLaunchKernelGGL((k_project<BF, 1>), grid, block, 0, stream, pl.p); break;  \
+void launch_gate(const Plan& pl, hipStream_t stream) {
+    dim3 grid((unsigned)pl.p.n_gate), block(kWG);
+    if (pl.bf16) {
+        if (pl.mb == 1) hipLaunchKernelGGL((k_gate<true, 1>), grid, block, 0, stream, pl.p);
+        else hipLaunchKernelGGL((k_gate<true, 4>), grid, block, 0, stream, pl.p);
+    } else {
+        if (pl.mb == 1) hipLaunchKernelGGL((k_gate<false, 1>), grid, block, 0, stream, pl.p);
+        else hipLaunchKernelGGL((k_gate<false, 4>), grid, block, 0, stream, pl.p);
     }
-    if (pl.bf16) { DF2_PROJ(true) } else { DF2_PROJ(false) }
-#undef DF2_PROJ
+    if (pl.p.S > 1) {
+        const int64_t n4 = pl.p.rows * pl.p.r / 4;
+        dim3 g2((unsigned)((n4 + kWG - 1) / kWG));
+        hipLaunchKernelGGL(k_gate_sum, g2, block, 0, stream, pl.p.ppart, pl.p.S, n4, pl.p.H);
+    }
 }
 
 }  // namespace
@@ -538,9 +657,13 @@ df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* 
     const int64_t rows = (int64_t)dims->B * dims->P;
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
-    plan_topk(pl, rows, dims->V, K, bf16, logits);
-    plan_proj(pl, rows, dims->d, dims->r, pl.n_chunk_blocks);
-    plan_layout(pl, rows, rows, dims->B);
+    pl.bf16 = bf16;
+    plan_gate(pl, rows, dims->d, dims->r);
+    // segments fill what the gate leaves of one resident wave of workgroups
+    const int64_t cap = select_capacity();
+    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, cap - pl.p.n_gate));
+    if (pl.p.n_gate + pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "problem too large");
+    plan_layout(pl, rows, rows, dims->B, true);
     Params& p = pl.p;
     p.logits = logits;
     p.hidden = hidden;
@@ -576,13 +699,10 @@ df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V, df2_dtype d
         return fail(DF2_EINVAL, "logits misaligned for its dtype");
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
-    plan_topk(pl, rows, V, K, bf16, logits);
+    plan_topk(pl, rows, V, K, bf16, logits, select_capacity());
     if (pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "too many rows");
-    pl.p.mtiles = 0;
-    pl.p.qtiles = 0;
     pl.p.S = 1;
-    pl.p.r = 0;
-    plan_layout(pl, rows, 0, 0);
+    plan_layout(pl, rows, 0, 0, false);
     Params& p = pl.p;
     p.logits = logits;
     p.P = 1;
@@ -607,15 +727,15 @@ df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M, int32
     if (M == 0) return DF2_OK;
     if (M > (1 << 24)) return fail(DF2_EUNSUPPORTED, "M too large");
     if (!hidden || !W_H || !out_H) return fail(DF2_EINVAL, "NULL pointer argument");
-    if (!aligned16(hidden) || !aligned16(W_H) || ((uintptr_t)out_H & 3u))
-        return fail(DF2_EINVAL, "hidden and W_H must be 16-byte aligned, out_H 4-byte");
+    if (!aligned16(hidden) || !aligned16(W_H) || ((uintptr_t)out_H & 15u))
+        return fail(DF2_EINVAL, "hidden, W_H and out_H must be 16-byte aligned");
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = dtype == DF2_BF16;
-    plan_proj(pl, M, d, r, 0);
+    plan_gate(pl, M, d, r);
     pl.p.C = 0;
     pl.p.K = 0;
-    plan_layout(pl, 0, M, 0);
+    plan_layout(pl, 0, M, 0, false);
     Params& p = pl.p;
     p.rows = M;
     p.hidden = hidden;
@@ -626,7 +746,7 @@ df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M, int32
     note_layout(stream, pl.counter_bytes);
     bind_scratch(pl, base, 0, 0);
     p.H = out_H;
-    return launch_checked([&] { launch_project(pl, stream); }, "dflash2_project launch");
+    return launch_checked([&] { launch_gate(pl, stream); }, "dflash2_project launch");
 }
 
 df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
@@ -642,9 +762,10 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
         return fail(DF2_EINVAL, "NULL pointer argument");
     if (!aligned16(H) || !aligned16(A_tab) || !aligned16(B_tab))
         return fail(DF2_EINVAL, "H, A_tab and B_tab must be 16-byte aligned");
+    if ((int64_t)dims->B * dims->P > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "too many rows");
     void* base = nullptr;
     if ((st = get_scratch(stream, 256, 4, &base)) != DF2_OK) return st;
-    FinArgs a;
+    PairArgs a;
     std::memset(&a, 0, sizeof(a));
     a.cand = cand_idx;
     a.cval = cand_val;
@@ -654,17 +775,17 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
     a.prev = prev_tok;
     a.out_S = out_S;
     a.err = reinterpret_cast<uint32_t*>(base);
+    a.B = dims->B;
     a.P = dims->P;
     a.V = dims->V;
     a.r = dims->r;
     a.K = K;
-    a.nseg = 1;
-    dim3 grid((unsigned)dims->B), block(kWG);
+    dim3 grid((unsigned)((int64_t)dims->B * dims->P)), block(kWG);
     return launch_checked([&] {
         if (dims->dtype == DF2_BF16)
-            hipLaunchKernelGGL((k_finish<true, kFinScores>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((k_pairs<true>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((k_finish<false, kFinScores>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((k_pairs<false>), grid, block, 0, stream, a);
     }, "dflash2_pair_scores launch");
 }
 
@@ -676,21 +797,19 @@ df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, i
     if (K < 1 || K > kMaxK) return fail(DF2_EINVAL, "K must be in [1, 64]");
     if (B == 0) return DF2_OK;
     if (!S || !cand_idx || !out_path || !out_score) return fail(DF2_EINVAL, "NULL pointer argument");
-    FinArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.in_cand = cand_idx;
-    a.in_S = S;
+    if (((uintptr_t)S & 3u) || ((uintptr_t)cand_idx & 3u) || ((uintptr_t)out_path & 3u) ||
+        ((uintptr_t)out_score & 3u))
+        return fail(DF2_EINVAL, "arguments must be 4-byte aligned");
+    WalkArgs a;
+    a.S = S;
+    a.cand = cand_idx;
     a.out_path = out_path;
     a.out_score = out_score;
     a.P = P;
     a.K = K;
-    a.r = 64;
-    a.nseg = 1;
-    a.V = 0x7FFFFFFF;
     dim3 grid((unsigned)B), block(kWG);
-    return launch_checked([&] {
-        hipLaunchKernelGGL((k_finish<true, kFinWalk>), grid, block, 0, stream, a);
-    }, "dflash2_viterbi launch");
+    return launch_checked([&] { hipLaunchKernelGGL(k_walk, grid, block, 0, stream, a); },
+                          "dflash2_viterbi launch");
 }
 
 df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {

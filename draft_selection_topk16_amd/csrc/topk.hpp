@@ -25,9 +25,10 @@
 // needs a workgroup barrier.
 // At the end of the segment the four waves' lists are merged the same way.
 //
-// Stage 2 (merge): the segments' sorted lists of K candidate words are merged
-// by one wave (wave_merge_lists): a bound (the best K-th word of any list),
-// in-place compaction of the words that reach it, and ranks by counting.
+// Stage 2 (merge): the last segment of a row to finish merges the segments'
+// sorted lists with the whole workgroup (block_merge_lists): a bound (the
+// best K-th word of any list), compaction of the words that reach it, and
+// ranks by counting.
 //
 // Candidate words (key << 32 | ~index) are distinct within a row, so every
 // selection is exact and independent of arrival order: results are
@@ -41,10 +42,9 @@
 namespace df2 {
 
 constexpr int kMaxNV = 4;           // 16-byte vectors per lane per chunk
-constexpr int kMergeMax = 128;      // words merged per row (segment lists * K)
+constexpr int kMergeMax = 1024;     // words merged per row (segment lists * K)
 constexpr int kListWords = 256;     // words one wave merge takes (the four waves' lists, K <= 64)
-static_assert(kMergeMax <= kWG, "one word per thread when a row is loaded");
-static_assert(kMergeMax <= kListWords, "a row merge fits one wave merge");
+static_assert(kMergeMax % kWG == 0, "whole words per thread when a row is loaded");
 
 constexpr int kWCand = 256;         // candidate words buffered per wave
 constexpr int kWPend = 64;          // pending vectors per wave before a flush
@@ -63,7 +63,12 @@ struct ChunkLds {
     uint32_t bound;                     // a key at least K values of the segment reach
     uint32_t qkey[kWaves];              // each wave's ceil(K/4)-th kept key
     uint64_t top[64];                   // merge output
-    uint64_t rowlist[kMergeMax];        // a row's segment lists (row merge)
+};
+
+struct MergeLds {
+    uint64_t surv[kMergeMax];           // words that reach the bound
+    uint64_t tk, tc;                    // bound candidates
+    uint32_t m;                         // survivors
 };
 
 template <bool BF16>
@@ -398,14 +403,17 @@ __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV
     return tk;
 }
 
-// Stage 1: best K candidate words of chunks [c0, c1) of one row; chunk c is
-// 4 x 64 x NV vectors, wave w streams its quarter of every chunk.
+// Stage 1: best K candidate words of the chunks of one row that belong to
+// this segment: the i-th (i < nc) is (c0 + (i / split) * cs) * split +
+// i % split.  A chunk is 4 x 64 x NV vectors; wave w streams its quarter of
+// every chunk.  The segments of a row interleave (cs = segments per row), so
+// the workgroups of a row read neighbouring chunks at any one time.
 //   row: first element of the row; V: row length; K <= 64.
-//   aligned: the row start is 16-byte aligned and V is a multiple of kPerVec.
+//   ALIGNED: the row start is 16-byte aligned and V is a multiple of kPerVec.
 //   out: K hand-off words (0 for empty slots).
 template <bool BF16, int NV, bool ALIGNED>
-__device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, int c1, int K,
-                                  uint64_t* __restrict__ out, ChunkLds& sm) {
+__device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, int cs, int nc,
+                                  int split, int K, uint64_t* __restrict__ out, ChunkLds& sm) {
     static_assert(NV >= 1 && NV <= kMaxNV, "chunk vectors per lane");
     constexpr int PV = Elem<BF16>::kPerVec;
     constexpr int WE = 64 * PV * NV;           // elements per wave chunk
@@ -413,7 +421,10 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     uint64_t tk = 0;
     int npend = 0;                             // pending vectors of this wave
     const int kq = (K + kWaves - 1) / kWaves;
-    auto eb_of = [&](int c) { return ((int64_t)c * kWaves + w) * WE; };
+    auto eb_of = [&](int i) {
+        const int c = (c0 + (i / split) * cs) * split + i % split;
+        return ((int64_t)c * kWaves + w) * WE;
+    };
     // Publishes two bounds that at least K values of the segment reach: the
     // wave's own K-th kept key (raises sm.bound), and its ceil(K/4)-th kept
     // key -- the four waves hold disjoint values, so the smallest of their
@@ -448,17 +459,17 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     // processed the next one's loads are in flight.  Past the segment end a
     // prefetch re-reads the last chunk (in bounds, never consumed).
     u32x4_t b0[NV], b1[NV];
-    const int clast = c1 - 1;
+    const int clast = nc - 1;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(c0) + (int64_t)(j * 64 + lane) * PV);
+        b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(0) + (int64_t)(j * 64 + lane) * PV);
     {
         // Initial bound: the K-th largest of the workgroup's 256 lane maxima
         // over its first chunk (one barrier per segment).
         u32x4_t v[NV];
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-            v[j] = mask_vec<ALIGNED>(b0[j], eb_of(c0) + (int64_t)(j * 64 + lane) * PV, V);
+            v[j] = mask_vec<ALIGNED>(b0[j], eb_of(0) + (int64_t)(j * 64 + lane) * PV, V);
         sm.lkey[tid] = lane_max_key<BF16, NV>(v);
         if (tid < kWaves) sm.qkey[tid] = 0;
         __syncthreads();
@@ -475,7 +486,7 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
         if (tid == 0) sm.bound = T;
         __syncthreads();
     }
-    for (int c = c0; c < c1; c += 2) {
+    for (int c = 0; c < nc; c += 2) {
         const int cn = min(c + 1, clast);
 #pragma unroll
         for (int j = 0; j < NV; ++j)
@@ -485,7 +496,7 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
         // Keep the next half's uses of its loads below this point: hoisting
         // one would wait on every load in flight, prefetch included.
         __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 >= c1) break;
+        if (c + 1 >= nc) break;
         const int cnn = min(c + 2, clast);
 #pragma unroll
         for (int j = 0; j < NV; ++j)
@@ -504,37 +515,100 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     }
 }
 
+// Segment seg of nseg of a row of C chunks (chunks seg, seg + nseg, ...).
 template <bool BF16, int NV>
-__device__ void segment_topk(const void* __restrict__ row, int V, int c0, int c1, int K,
+__device__ void segment_topk(const void* __restrict__ row, int V, int C, int seg, int nseg, int K,
                              bool aligned, uint64_t* __restrict__ out, ChunkLds& sm) {
+    const int nc = (C - seg + nseg - 1) / nseg;
     // Rows that are not 16-byte aligned load element by element; they use
-    // one-vector chunks (the same elements, NV times as many chunks) so that
-    // this rare path stays small in registers.
+    // one-vector chunks (each chunk split in NV) so that this rare path stays
+    // small in registers.
     if (aligned)
-        segment_topk_impl<BF16, NV, true>(row, V, c0, c1, K, out, sm);
+        segment_topk_impl<BF16, NV, true>(row, V, seg, nseg, nc, 1, K, out, sm);
     else
-        segment_topk_impl<BF16, 1, false>(row, V, c0 * NV, c1 * NV, K, out, sm);
+        segment_topk_impl<BF16, 1, false>(row, V, seg, nseg, nc * NV, NV, K, out, sm);
 }
 
-// Stage 2: merge the nseg sorted segment lists of a row (K words each,
-// nseg * K <= kMergeMax) into the row's top-K, written as (index, value).
+// Stage 2: top K of one row from its nl sorted segment lists (K words each,
+// descending, zero padded; written by other workgroups, read with xload);
+// nl * K <= kMergeMax.  emit(rank, word) runs once for every rank < K, in
+// the thread that holds the word.  Every thread of the workgroup calls.
+// The bound is the larger of the best K-th word of any list and the
+// smallest c-th word over all lists (c = ceil(K / nl)): at least K words
+// reach either.
+template <typename Emit>
+__device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, int K,
+                                  MergeLds& sm, Emit&& emit) {
+    constexpr int Q = kMergeMax / kWG;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int n = nl * K;
+    const int c = (K + nl - 1) / nl;
+    uint64_t x[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) x[q] = (q * kWG < n) ? xload(lists + min(q * kWG + tid, n - 1)) : 0ull;
+    if (tid == 0) {
+        sm.tk = 0ull;
+        sm.tc = ~0ull;
+        sm.m = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = q * kWG + tid;
+        if (e < n) {
+            const int k = e % K;
+            if (k == K - 1)
+                __hip_atomic_fetch_max(&sm.tk, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (k == c - 1)
+                __hip_atomic_fetch_min(&sm.tc, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    __syncthreads();
+    uint64_t T = sm.tk > sm.tc ? sm.tk : sm.tc;
+    T = T ? T : 1ull;
+    // compaction: one LDS add per wave and round reserves the wave's slots
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if (q * kWG < n) {
+            const bool sv = (q * kWG + tid < n) && x[q] >= T;
+            const uint64_t bal = __ballot(sv);
+            uint32_t base = 0;
+            if (lane == 0 && bal)
+                base = __hip_atomic_fetch_add(&sm.m, (uint32_t)__popcll(bal), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_WORKGROUP);
+            base = __builtin_amdgcn_readfirstlane(base);
+            if (sv) sm.surv[base + __popcll(bal & ((1ull << lane) - 1ull))] = x[q];
+        }
+    }
+    __syncthreads();
+    const int m = (int)sm.m;
+    for (int s0 = 0; s0 < m; s0 += kWG) {
+        const int si = s0 + tid;
+        const uint64_t y = (si < m) ? sm.surv[si] : 0ull;
+        int rank = 0;
+        for (int u0 = 0; u0 < m; u0 += 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = sm.surv[min(u0 + j, m - 1)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rank += (u0 + j < m && v[j] > y) ? 1 : 0;
+        }
+        if (si < m && rank < K) emit(rank, y);
+    }
+    __syncthreads();
+}
+
+// Row merge to (index, value) pairs; a row always has K real values
+// (K <= V), so every rank is written.
 template <bool BF16>
 __device__ void merge_row(const uint64_t* __restrict__ part, int nseg, int K,
                           int32_t* __restrict__ out_idx, float* __restrict__ out_val,
-                          ChunkLds& sm) {
+                          MergeLds& sm) {
     using E = Elem<BF16>;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int n = nseg * K;     // <= kMergeMax <= kWG
-    const uint64_t x = xload(part + min(tid, n - 1));
-    if (tid < n) sm.rowlist[tid] = x;
-    __syncthreads();
-    if (tid < 64) {
-        const uint64_t y = wave_merge_lists(sm.rowlist, nseg, K, sm.top);
-        if (lane < K) {
-            out_idx[lane] = y ? (int32_t)cand_index(y) : 0;
-            out_val[lane] = y ? E::value((uint32_t)(y >> 32)) : -INFINITY;
-        }
-    }
+    block_merge_lists(part, nseg, K, sm, [&](int rank, uint64_t y) {
+        xstore(out_idx + rank, (int32_t)cand_index(y));
+        xstore(out_val + rank, E::value((uint32_t)(y >> 32)));
+    });
 }
 
 }  // namespace df2

@@ -1,0 +1,232 @@
+// The walk over precomputed pair scores.
+//
+// "DFlash 2: Keep Drafting Parallel", section "A Lightweight Path Selector":
+// the only sequential work of the selector is one walk over the scores,
+// starting from the last verified token.  The walk is read as a max-sum
+// (Viterbi) pass with backtrack:
+//     delta_0(j) = S_0(prev, j)
+//     delta_t(j) = max_i delta_{t-1}(i) + S_t(i, j),  psi_t(j) = its argmax
+// then the best final state and psi backwards.  Ties keep the smaller
+// predecessor rank and the smaller final rank.  Sums are fp32.
+//
+// One wave walks; lane j owns candidate j and reads the whole previous delta
+// from scalar registers (no LDS round trip per step).  Scores enter LDS
+// transposed (column j contiguous, padded to Kp = K rounded up to 16, 32 or
+// 64), a group of positions at a time.
+#pragma once
+
+#include <math.h>
+
+#include "common.hpp"
+#include "pairs.hpp"
+
+namespace df2 {
+
+constexpr int kWalkS = 4096;        // floats of scores per group of positions
+constexpr int kWalkIds = 1024;      // candidate ids kept in LDS (P * K at most)
+
+struct WalkLds {
+    float ST[kWalkS];               // [t][j][i] over Kp x Kp, zero padded
+    uint8_t psi[kMaxP * kMaxK];
+    int32_t ids[kWalkIds];
+    int32_t rank[kMaxP];
+};
+
+// Best of one lane's values v[0..16) (predecessors i0 .. i0 + 15): the
+// largest value and its smallest index, both by trees (the value by max,
+// the index by min over the positions that hold the maximum).
+__device__ __forceinline__ void best_of16(const float (&v)[16], int i0, float& best, int& arg) {
+    float m8[8], m4[4], m2[2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m8[u] = fmaxf(v[2 * u], v[2 * u + 1]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m4[u] = fmaxf(m8[2 * u], m8[2 * u + 1]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) m2[u] = fmaxf(m4[2 * u], m4[2 * u + 1]);
+    best = fmaxf(m2[0], m2[1]);
+    uint32_t e[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) e[u] = (v[u] == best) ? (uint32_t)u : 15u;
+    uint32_t e5[6];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) e5[u] = min(min(e[3 * u], e[3 * u + 1]), e[3 * u + 2]);
+    e5[5] = e[15];
+    const uint32_t e2a = min(min(e5[0], e5[1]), e5[2]), e2b = min(min(e5[3], e5[4]), e5[5]);
+    arg = i0 + (int)min(e2a, e2b);
+}
+
+// psi_t(j) of lane j for t < 16, eight bits each (four positions a word).
+struct PsiRegs {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ uint32_t psi_word(const PsiRegs& pk, int t) {
+    switch (t >> 2) {
+        case 0: return pk.w[0];
+        case 1: return pk.w[1];
+        case 2: return pk.w[2];
+        default: return pk.w[3];
+    }
+}
+
+// Wave 0: delta over positions [t0, t1) of a group held in sm.ST.  Lane j
+// owns candidate j; delta_{t-1} reaches every lane through readlane (scalar
+// registers), 16 predecessors at a time, and the column S_t(., j) comes from
+// LDS with 16-byte reads.  Lanes j >= K carry -inf.  psi goes to registers
+// (P <= 16) or to LDS.
+template <int KP>
+__device__ float walk_steps(int t0, int t1, int K, float delta, bool psi_regs, PsiRegs& pk,
+                            WalkLds& sm) {
+    const int lane = lane_id();
+    const int j = lane % KP;
+    const bool jv = lane < K;
+    const uint32_t keep = jv ? ~0u : 0u;
+    const uint32_t ninf = (uint32_t)__float_as_int(-INFINITY);
+#pragma unroll 1
+    for (int t = t0; t < t1; ++t) {
+        const float* col = sm.ST + (t - t0) * KP * KP + j * KP;
+        if (t == 0) {
+            delta = jv ? col[0] : -INFINITY;
+            continue;
+        }
+        float sv[KP];
+#pragma unroll
+        for (int q = 0; q < KP / 4; ++q) {
+            const float4 x = *reinterpret_cast<const float4*>(col + 4 * q);
+            sv[4 * q] = x.x;
+            sv[4 * q + 1] = x.y;
+            sv[4 * q + 2] = x.z;
+            sv[4 * q + 3] = x.w;
+        }
+        float best = -INFINITY;
+        int arg = 0;
+#pragma unroll
+        for (int c = 0; c < KP; c += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = sv[c + u] + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), c + u));
+            float cb;
+            int ca;
+            best_of16(v, c, cb, ca);
+            if (c == 0 || cb > best) {
+                best = cb;
+                arg = ca;
+            }
+        }
+        delta = __int_as_float((int)((__float_as_int(best) & keep) | (ninf & ~keep)));
+        // arg < K for finite scores; the clamp keeps NaN inputs in bounds
+        const uint32_t a = (uint32_t)min(arg, K - 1);
+        if (psi_regs) {
+            const uint32_t v = a << (8 * (t & 3));
+            switch (t >> 2) {
+                case 0: pk.w[0] |= v; break;
+                case 1: pk.w[1] |= v; break;
+                case 2: pk.w[2] |= v; break;
+                default: pk.w[3] |= v; break;
+            }
+        } else if (jv) {
+            sm.psi[t * K + j] = (uint8_t)a;
+        }
+    }
+    return delta;
+}
+
+// The walk of one sequence.  S: [P, K, K] scores (row i = predecessor rank,
+// column j = candidate rank; row 0 is used at t = 0), ids: [P, K] candidate
+// ids; both read with xload.  Writes out_path[0 .. P) and *out_score.
+// Every thread of the workgroup calls.
+__device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int32_t* __restrict__ ids, int P,
+                         int K, int32_t* __restrict__ out_path, float* __restrict__ out_score,
+                         WalkLds& sm) {
+    constexpr int U = 8;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int KP = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
+    const int KK = K * K, KP2 = KP * KP;
+    const int G = kWalkS / KP2;
+    const bool ids_lds = P * K <= kWalkIds;
+    const bool psi_regs = P <= 16;
+    PsiRegs pk = {{0u, 0u, 0u, 0u}};
+    float delta = -INFINITY;
+    for (int t0 = 0; t0 < P; t0 += G) {
+        const int t1 = min(P, t0 + G);
+        if (KP != K) {
+            for (int x = tid; x < (t1 - t0) * KP2; x += kWG) sm.ST[x] = 0.f;
+            __syncthreads();
+        }
+        // candidate ids (first group) and the group's scores, all loads of a
+        // thread issued before any is stored
+        const int nt = t1 - t0;
+        const bool load_ids = t0 == 0 && ids_lds;
+        constexpr int QI = kWalkIds / kWG;
+        int32_t idv[QI];
+#pragma unroll
+        for (int q = 0; q < QI; ++q)
+            idv[q] = load_ids ? xload(ids + min(q * kWG + tid, P * K - 1)) : 0;
+        for (int e = tid; e < KK; e += kWG) {
+            const int i = e / K, j = e % K;
+            const float* src = S + (int64_t)t0 * KK + e;
+            float* dst = sm.ST + j * KP + i;
+            for (int tb = 0; tb < nt; tb += U) {
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = xload(src + (int64_t)min(tb + u, nt - 1) * KK);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (tb + u < nt) dst[(tb + u) * KP2] = v[u];
+            }
+        }
+        if (load_ids) {
+#pragma unroll
+            for (int q = 0; q < QI; ++q)
+                if (q * kWG + tid < P * K) sm.ids[q * kWG + tid] = idv[q];
+        }
+        __syncthreads();
+        if (w == 0) {
+            if (KP == 16) delta = walk_steps<16>(t0, t1, K, delta, psi_regs, pk, sm);
+            else if (KP == 32) delta = walk_steps<32>(t0, t1, K, delta, psi_regs, pk, sm);
+            else delta = walk_steps<64>(t0, t1, K, delta, psi_regs, pk, sm);
+        }
+        __syncthreads();
+    }
+    if (w != 0) return;
+    // final pick (smaller rank on ties): every lane reduces the broadcast
+    // deltas, then backtracks through psi
+    float m = -INFINITY;
+    int jb = 0;
+    for (int c = 0; c < K; c += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            v[u] = (c + u < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), min(c + u, 63)))
+                               : -INFINITY;
+        float cb;
+        int ca;
+        best_of16(v, c, cb, ca);
+        if (c == 0 || cb > m) {
+            m = cb;
+            jb = ca;
+        }
+    }
+    // backtrack: jj is uniform; psi_t(jj) comes from lane jj's register
+    // (readlane) or from LDS
+    int jj = min(jb, K - 1);
+    for (int t = P - 1; t > 0; --t) {
+        if (lane == 0) sm.rank[t] = jj;
+        if (psi_regs)
+            jj = (int)((__builtin_amdgcn_readlane(psi_word(pk, t), jj) >> (8 * (t & 3))) & 63u);
+        else
+            jj = sm.psi[t * K + jj];
+    }
+    if (lane == 0) {
+        sm.rank[0] = jj;
+        *out_score = m;
+    }
+    wave_sync();
+    for (int t = lane; t < P; t += 64) {
+        const int rk = sm.rank[t];
+        out_path[t] = ids_lds ? sm.ids[t * K + rk] : xload(ids + (int64_t)t * K + rk);
+    }
+}
+
+}  // namespace df2

@@ -21,10 +21,10 @@
  *    pointer after the call returns and never frees caller memory.
  *  - Every tensor is dense row-major (C order), last dimension contiguous.
  *  - Work is enqueued on `stream` and the call returns without waiting.
- *  - Scratch memory (top-K partials, gate partials, arrival counters) comes
- *    from a cache owned by the library, one buffer per (device, stream); it
- *    grows with hipMalloc outside the launch and is zero-initialised when
- *    allocated.  Calls on the same stream are ordered; calls on different
+ *  - Scratch memory (top-K partials, gate partials, pair scores, arrival
+ *    counters) comes from a cache owned by the library, one buffer per
+ *    (device, stream); it grows with hipMalloc outside the launch and is
+ *    zero-initialised when allocated.  Calls on the same stream are ordered; calls on different
  *    streams use different scratch.  Warm the cache with one call before
  *    capturing a stream into a HIP graph.
  *  - Argument errors are found on the host, before any launch: the call
@@ -110,7 +110,9 @@ df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V,
 /*
  * Gate projection H = W_H h for M rows (the reading of H(h_t)).
  *   hidden [M, d] (dtype), W_H [r, d] (dtype), out_H [M, r] float
- * d multiple of 32, r multiple of 64 and <= 1024.
+ * d multiple of 32, r multiple of 64 and <= 1024; hidden, W_H and out_H
+ * 16-byte aligned.  H is rounded exactly as inside dflash2_select (the same
+ * slices of d, summed in the same order).
  */
 df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M,
                            int32_t d, int32_t r, df2_dtype dtype, float* out_H,
@@ -143,10 +145,12 @@ df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B,
                            float* out_score, hipStream_t stream);
 
 /*
- * Waits for `stream`, then reports and clears the device-side input flag of
- * its scratch buffer: *flags receives a bit mask (bit 0: a prev_tok outside
+ * Waits for `stream`, then reports and clears the device-side flags of its
+ * scratch buffer: *flags receives a bit mask (bit 0: a prev_tok outside
  * [0, V) was replaced by 0; bit 1: a cand_idx entry outside [0, V) was
- * replaced by 0).  Returns DF2_OK, or DF2_EHIP.
+ * replaced by 0; bit 2: a pair-score job of dflash2_select gave up waiting
+ * for its gate rows, which only a fault elsewhere can cause, and its scores
+ * are then unreliable).  Returns DF2_OK, or DF2_EHIP.
  */
 df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags);
 
