@@ -68,6 +68,7 @@ struct Params {
     float* cval;          // [rows, K]
     float* ppart;         // [S, M, r] gate partials
     float* Sb;            // [rows, K, K] pair scores
+    float* Hb;            // [rows, r] gate rows, summed by the row merges
     uint32_t* err;        // device input-error flags
     uint32_t* row_cnt;    // [rows] segments done
     uint32_t* edge_cnt;   // [rows] rows ready of transition t - 1 -> t
@@ -132,9 +133,12 @@ __device__ __forceinline__ int32_t checked_id(int32_t id, int V, uint32_t* err, 
 }
 
 // Pair scores of positions e0 .. e0 + ne - 1 of sequence b (fused launch).
+// own: the row this workgroup merged; hown: its gate row (floats tid and
+// tid + 256 of this thread).  The other position's gate row comes from Hb.
 template <bool BF16>
-__device__ void pairs_fused(const Params& p, int b, int e0, int ne, PairLds& sm) {
-    const int tid = threadIdx.x, K = p.K;
+__device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
+                            const float (&hown)[2], PairLds& sm) {
+    const int tid = threadIdx.x, K = p.K, r = p.r;
     const int64_t rb = (int64_t)b * p.P;
     // Candidate ids come from the row merges and are always in [0, V); they
     // are still checked, so that no gather can leave the tables.
@@ -154,31 +158,26 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, PairLds& sm)
         const int x = tid - 64, q = x / K, k = x % K;
         sm.ids[1 + q][k] = checked_id(xload(p.cand + (rb + e0 + q) * K + k), p.V, p.err, 2u);
         sm.u[q][k] = xload(p.cval + (rb + e0 + q) * K + k);
-    } else if (tid >= 192 && tid < 192 + ne) {
-        // the gate tile row of the position's row must be complete
-        const int64_t grow = rb + e0 + (tid - 192);
-        const int mt = (int)(grow / p.gm_rows);
-        const uint32_t need = (uint32_t)(p.ntiles * p.S);
-        uint32_t it = 0;
-        while (xload(&p.gate_cnt[mt]) < need) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++it > (1u << 20)) {
-                atomicOr(p.err, 4u);
-                break;
-            }
-        }
-        // the last of the tile row's pair jobs resets its counters
-        const int64_t lo = (int64_t)mt * p.gm_rows;
-        const uint32_t rows_in = (uint32_t)(std::min<int64_t>(p.rows, lo + p.gm_rows) - lo);
-        if (arrive(&p.rd_cnt[mt]) == rows_in - 1u) {
-            reset_counter(&p.gate_cnt[mt]);
-            reset_counter(&p.rd_cnt[mt]);
+    }
+    // gate rows of the positions, in the same round of loads
+    float hv[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int64_t grow = rb + e0 + q;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int k = tid + u * kWG;
+            hv[q][u] = (grow == own) ? hown[u]
+                                     : ((q < ne && k < r) ? xload(p.Hb + grow * r + k) : 0.f);
         }
     }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            if (q < ne && tid + u * kWG < r) sm.H[q][tid + u * kWG] = hv[q][u];
     __syncthreads();
-    pair_tiles<BF16>(p.A, p.Bt, K, p.r, e0, ne, p.Sb + (rb + e0) * K * K, sm, [&]() {
-        pair_sum_gate(p.ppart, p.S, p.rows, p.r, rb + e0, ne, sm);
-    });
+    pair_tiles<BF16>(p.A, p.Bt, K, r, e0, ne, p.Sb + (rb + e0) * K * K, sm, [] {});
 }
 
 // The whole selector in one launch.
@@ -201,17 +200,78 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
     __builtin_amdgcn_s_setprio(3);
     if (tid == 0) reset_counter(&p.row_cnt[row]);
-    const int K = p.K, P = p.P;
-    merge_row<BF16>(p.part + (size_t)row * p.nseg * K, p.nseg, K, p.cand + row * K,
-                    p.cval + row * K, sm.m);
+    const int K = p.K, P = p.P, r = p.r;
+    // The row's gate H_t: once the gate tile row is complete (its workgroups
+    // were dispatched first and never wait; this is almost always so by
+    // now), its S partials are loaded while the merge runs and summed in
+    // slice order.
+    const int mt = (int)(row / p.gm_rows);
+    const uint32_t need = (uint32_t)(p.ntiles * p.S);
+    const int S = p.S;
+    uint32_t hp[kMaxFusedSlices];
+    auto issue_h = [&](int k) {
+#pragma unroll
+        for (int s = 0; s < kMaxFusedSlices; ++s)
+            hp[s] = xload(reinterpret_cast<const uint32_t*>(p.ppart) +
+                          ((int64_t)min(s, S - 1) * p.rows + row) * r + min(k, r - 1));
+    };
+    auto sum_h = [&]() {
+        float h = 0.f;
+#pragma unroll
+        for (int s = 0; s < kMaxFusedSlices; ++s)
+            if (s < S) h += __uint_as_float(hp[s]);
+        return h;
+    };
+    merge_row<BF16>(
+        p.part + (size_t)row * p.nseg * K, p.nseg, K, p.cand + row * K, p.cval + row * K, sm.m,
+        [&] {
+            if (tid == 0) sm.m.aux = xload(&p.gate_cnt[mt]);
+        },
+        [&] {
+            if (sm.m.aux < need) {
+                if (tid == 0) {
+                    uint32_t it = 0;
+                    while (xload(&p.gate_cnt[mt]) < need) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++it > (1u << 20)) {
+                            atomicOr(p.err, 4u);
+                            break;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+            issue_h(tid);
+        });
+    float hown[2];
+    hown[0] = sum_h();
+    hown[1] = 0.f;
+    if (r > kWG) {
+        issue_h(tid + kWG);
+        hown[1] = sum_h();
+    }
+    // publish H_t for the pair job of the next position
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        if (tid + u * kWG < r) xstore(p.Hb + row * r + tid + u * kWG, hown[u]);
     // arrive on the transitions into and out of this row
     const int b = (int)(row / P), t = (int)(row % P);
     drain_stores();
     __syncthreads();
     if (tid < 64) {
-        bool mine = false;
-        if (tid == 0) mine = (t == 0) || arrive(&p.edge_cnt[row]) == 1u;
-        if (tid == 1 && t + 1 < P) mine = arrive(&p.edge_cnt[row + 1]) == 1u;
+        // one atomic instruction: lane 0 on the transition into this row,
+        // lane 1 on the one out of it, lane 2 on the gate tile row's readers
+        const int64_t lo = (int64_t)mt * p.gm_rows;
+        const uint32_t rows_in = (uint32_t)(std::min<int64_t>(p.rows, lo + p.gm_rows) - lo);
+        const bool act = (tid == 0 && t > 0) || (tid == 1 && t + 1 < P) || tid == 2;
+        uint32_t* cnt = (tid == 2) ? &p.rd_cnt[mt] : &p.edge_cnt[row + tid];
+        const uint32_t old = act ? arrive(cnt) : 0u;
+        const bool mine = (tid == 0 && (t == 0 || old == 1u)) || (tid == 1 && act && old == 1u);
+        if (tid == 2 && old == rows_in - 1u) {
+            // the last row of the gate tile row to be read resets its counters
+            reset_counter(&p.gate_cnt[mt]);
+            reset_counter(&p.rd_cnt[mt]);
+        }
         const uint64_t bal = __ballot(mine);
         if (tid == 0) flag = (uint32_t)bal & 3u;
     }
@@ -222,7 +282,7 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     if (tid == 1 && (em & 2u)) reset_counter(&p.edge_cnt[row + 1]);
     const int e0 = (em & 1u) ? t : t + 1;
     const int ne = (em == 3u) ? 2 : 1;
-    pairs_fused<BF16>(p, b, e0, ne, sm.pr);
+    pairs_fused<BF16>(p, b, e0, ne, row, hown, sm.pr);
     drain_stores();
     __syncthreads();
     if (tid == 0) {
@@ -433,7 +493,7 @@ struct Plan {
     bool bf16 = true;
     int64_t n_chunk_blocks = 0;
     size_t counter_bytes = 0, total_bytes = 0;
-    size_t off_part = 0, off_cand = 0, off_cval = 0, off_ppart = 0, off_S = 0;
+    size_t off_part = 0, off_cand = 0, off_cval = 0, off_ppart = 0, off_S = 0, off_Hb = 0;
 };
 
 // Chunk size (16-byte vectors per thread) and segmentation of the rows.
@@ -510,6 +570,8 @@ void plan_layout(Plan& pl, int64_t rows, int64_t M, int B, bool pairs) {
     off = align_up(off + (p.S > 1 || pairs ? (size_t)p.S * M * p.r * 4 : 0), 256);
     pl.off_S = off;
     off = align_up(off + (pairs ? (size_t)rows * p.K * p.K * 4 : 0), 256);
+    pl.off_Hb = off;
+    off = align_up(off + (pairs ? (size_t)rows * p.r * 4 : 0), 256);
     pl.total_bytes = off;
 }
 
@@ -528,6 +590,7 @@ void bind_scratch(Plan& pl, void* base, int64_t rows, int B) {
     p.cval = reinterpret_cast<float*>(c + pl.off_cval);
     p.ppart = reinterpret_cast<float*>(c + pl.off_ppart);
     p.Sb = reinterpret_cast<float*>(c + pl.off_S);
+    p.Hb = reinterpret_cast<float*>(c + pl.off_Hb);
 }
 
 df2_status check_dims(const df2_dims* dims, bool need_d) {

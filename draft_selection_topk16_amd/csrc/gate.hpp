@@ -10,9 +10,10 @@
 // fp32 inputs use the fp32 matrix instruction).
 //
 // A workgroup computes one slice s of d for one output tile of MB x NB
-// 16 x 16 blocks.  Its four waves take interleaved 32-wide k steps and issue
-// the loads of KB steps each before the first product, so a slice of
-// 4 * KB steps costs one memory round trip.  The four waves' tiles are summed
+// 16 x 16 blocks.  Its four waves take turns at groups of KB adjacent
+// 32-wide k steps (adjacent steps of a row share cache lines) and issue the
+// loads of a group before its first product, so a slice of 4 * KB steps
+// costs one memory round trip.  The four waves' tiles are summed
 // in LDS in wave order and the slice is written as a partial [S, M, r]
 // (or straight into H when S == 1).  Whoever needs H_t sums the S partials of
 // its row in slice order, so results never depend on timing.
@@ -42,8 +43,11 @@ __device__ void gate_slice(const void* __restrict__ hidden, const void* __restri
     constexpr int KB = gate_kb(BF16);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int row = lane & 15, g = lane >> 4;
-    const int KS = d / 32;
-    const int ks0 = (int)((int64_t)KS * s / S), ks1 = (int)((int64_t)KS * (s + 1) / S);
+    // slices start on even k steps, so that the two adjacent steps a wave
+    // loads together share their 128-byte lines
+    const int KS = d / 32, KP = (KS + 1) / 2;
+    const int ks0 = 2 * (int)((int64_t)KP * s / S);
+    const int ks1 = min(KS, 2 * (int)((int64_t)KP * (s + 1) / S));
 
     f32x4_t acc[MB][NB];
 #pragma unroll
@@ -58,14 +62,15 @@ __device__ void gate_slice(const void* __restrict__ hidden, const void* __restri
 #pragma unroll
     for (int j = 0; j < NB; ++j) brow[j] = (int64_t)(nt * 16 * NB + 16 * j + row) * d;
 
-    for (int kb = ks0 + w; kb < ks1; kb += kWaves * KB) {
+    // wave w takes steps kb .. kb + KB - 1, kb = ks0 + KB * (w + 4 i)
+    for (int kb = ks0 + KB * w; kb < ks1; kb += kWaves * KB) {
         if constexpr (BF16) {
             const uint16_t* h16 = reinterpret_cast<const uint16_t*>(hidden);
             const uint16_t* w16 = reinterpret_cast<const uint16_t*>(W);
             u32x4_t a[KB][MB], b[KB][NB];
 #pragma unroll
             for (int q = 0; q < KB; ++q) {
-                const int kq = kb + q * kWaves;
+                const int kq = kb + q;
                 const int k0 = ((kq < ks1) ? kq : kb) * 32 + g * 8;
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
@@ -76,7 +81,7 @@ __device__ void gate_slice(const void* __restrict__ hidden, const void* __restri
             }
 #pragma unroll
             for (int q = 0; q < KB; ++q) {
-                if (kb + q * kWaves < ks1) {
+                if (kb + q < ks1) {
 #pragma unroll
                     for (int i = 0; i < MB; ++i)
 #pragma unroll

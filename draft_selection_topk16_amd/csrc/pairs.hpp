@@ -12,7 +12,8 @@
 //
 // One workgroup scores one or two consecutive positions.  The 16 x 16 tiles
 // are taken a batch at a time; inside a batch the four waves split the k
-// steps (wave w takes steps w, w + 4, ...), each wave gathers its embedding
+// steps (wave w takes adjacent steps 2w, 2w + 1, then 2w + 8, ...: adjacent
+// steps of an embedding row share cache lines), each wave gathers its embedding
 // slices straight into operand registers with all loads of the batch in
 // flight, and the four partial tiles are summed in LDS in wave order.
 #pragma once
@@ -72,7 +73,7 @@ __device__ void pair_tiles(const void* __restrict__ A, const void* __restrict__ 
         f32x4_t acc[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int kr = w; kr < nks || !h_loaded; kr += kWaves * KSW) {
+        for (int kr = KSW * w; kr < nks || !h_loaded; kr += kWaves * KSW) {
             if constexpr (BF16) {
                 const uint16_t* A16 = reinterpret_cast<const uint16_t*>(A);
                 const uint16_t* B16 = reinterpret_cast<const uint16_t*>(Bt);
@@ -81,7 +82,7 @@ __device__ void pair_tiles(const void* __restrict__ A, const void* __restrict__ 
                 for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
                     for (int q = 0; q < KSW; ++q) {
-                        const int ks = min(kr + q * kWaves, nks - 1);
+                        const int ks = min(kr + q, nks - 1);
                         const int k0 = ks * 32 + g * 8;
                         av[tb][q] = *reinterpret_cast<const u32x4_t*>(A16 + (int64_t)atok[tb] * r + k0);
                         bv[tb][q] = *reinterpret_cast<const u32x4_t*>(B16 + (int64_t)btok[tb] * r + k0);
@@ -97,7 +98,7 @@ __device__ void pair_tiles(const void* __restrict__ A, const void* __restrict__ 
                     const float* Hs = sm.H[tq[tb]];
 #pragma unroll
                     for (int q = 0; q < KSW; ++q) {
-                        const int ks = kr + q * kWaves;
+                        const int ks = kr + q;
                         if (ks >= nks) continue;
                         const int k0 = ks * 32 + g * 8;
                         const float4 h0 = *reinterpret_cast<const float4*>(Hs + k0);
@@ -124,7 +125,7 @@ __device__ void pair_tiles(const void* __restrict__ A, const void* __restrict__ 
                 float4 av[KSW][2], bv[KSW][2];
 #pragma unroll
                 for (int q = 0; q < KSW; ++q) {
-                    const int ks = min(kr + q * kWaves, nks - 1);
+                    const int ks = min(kr + q, nks - 1);
                     const int k0 = ks * 32 + g * 8;
                     const float* ap = A32 + (int64_t)atok[0] * r + k0;
                     const float* bp = B32 + (int64_t)btok[0] * r + k0;
@@ -141,7 +142,7 @@ __device__ void pair_tiles(const void* __restrict__ A, const void* __restrict__ 
                 const float* Hs = sm.H[tq[0]];
 #pragma unroll
                 for (int q = 0; q < KSW; ++q) {
-                    const int ks = kr + q * kWaves;
+                    const int ks = kr + q;
                     if (ks >= nks) continue;
                     const int k0 = ks * 32 + g * 8;
                     const float4 h0 = *reinterpret_cast<const float4*>(Hs + k0);

@@ -69,6 +69,7 @@ struct MergeLds {
     uint64_t surv[kMergeMax];           // words that reach the bound
     uint64_t tk, tc;                    // bound candidates
     uint32_t m;                         // survivors
+    uint32_t aux;                       // for the caller's hooks
 };
 
 template <bool BF16>
@@ -536,9 +537,11 @@ __device__ void segment_topk(const void* __restrict__ row, int V, int C, int seg
 // The bound is the larger of the best K-th word of any list and the
 // smallest c-th word over all lists (c = ceil(K / nl)): at least K words
 // reach either.
-template <typename Emit>
+// pre() runs right after the list loads are issued and mid() right after the
+// first barrier, so that a caller can overlap loads of its own with the merge.
+template <typename Emit, typename Pre, typename Mid>
 __device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, int K,
-                                  MergeLds& sm, Emit&& emit) {
+                                  MergeLds& sm, Emit&& emit, Pre&& pre, Mid&& mid) {
     constexpr int Q = kMergeMax / kWG;
     const int tid = threadIdx.x, lane = tid & 63;
     const int n = nl * K;
@@ -551,7 +554,9 @@ __device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, in
         sm.tc = ~0ull;
         sm.m = 0u;
     }
+    pre();
     __syncthreads();
+    mid();
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int e = q * kWG + tid;
@@ -599,16 +604,26 @@ __device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, in
 }
 
 // Row merge to (index, value) pairs; a row always has K real values
-// (K <= V), so every rank is written.
+// (K <= V), so every rank is written.  pre / mid: see block_merge_lists.
+template <bool BF16, typename Pre, typename Mid>
+__device__ void merge_row(const uint64_t* __restrict__ part, int nseg, int K,
+                          int32_t* __restrict__ out_idx, float* __restrict__ out_val,
+                          MergeLds& sm, Pre&& pre, Mid&& mid) {
+    using E = Elem<BF16>;
+    block_merge_lists(
+        part, nseg, K, sm,
+        [&](int rank, uint64_t y) {
+            xstore(out_idx + rank, (int32_t)cand_index(y));
+            xstore(out_val + rank, E::value((uint32_t)(y >> 32)));
+        },
+        pre, mid);
+}
+
 template <bool BF16>
 __device__ void merge_row(const uint64_t* __restrict__ part, int nseg, int K,
                           int32_t* __restrict__ out_idx, float* __restrict__ out_val,
                           MergeLds& sm) {
-    using E = Elem<BF16>;
-    block_merge_lists(part, nseg, K, sm, [&](int rank, uint64_t y) {
-        xstore(out_idx + rank, (int32_t)cand_index(y));
-        xstore(out_val + rank, E::value((uint32_t)(y >> 32)));
-    });
+    merge_row<BF16>(part, nseg, K, out_idx, out_val, sm, [] {}, [] {});
 }
 
 }  // namespace df2

@@ -33,8 +33,7 @@ struct WalkLds {
 };
 
 // Best of one lane's values v[0..16) (predecessors i0 .. i0 + 15): the
-// largest value and its smallest index, both by trees (the value by max,
-// the index by min over the positions that hold the maximum).
+// largest value by a max tree, then its smallest index.
 __device__ __forceinline__ void best_of16(const float (&v)[16], int i0, float& best, int& arg) {
     float m8[8], m4[4], m2[2];
 #pragma unroll
@@ -44,39 +43,17 @@ __device__ __forceinline__ void best_of16(const float (&v)[16], int i0, float& b
 #pragma unroll
     for (int u = 0; u < 2; ++u) m2[u] = fmaxf(m4[2 * u], m4[2 * u + 1]);
     best = fmaxf(m2[0], m2[1]);
-    uint32_t e[16];
+    arg = i0 + 15;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) e[u] = (v[u] == best) ? (uint32_t)u : 15u;
-    uint32_t e5[6];
-#pragma unroll
-    for (int u = 0; u < 5; ++u) e5[u] = min(min(e[3 * u], e[3 * u + 1]), e[3 * u + 2]);
-    e5[5] = e[15];
-    const uint32_t e2a = min(min(e5[0], e5[1]), e5[2]), e2b = min(min(e5[3], e5[4]), e5[5]);
-    arg = i0 + (int)min(e2a, e2b);
-}
-
-// psi_t(j) of lane j for t < 16, eight bits each (four positions a word).
-struct PsiRegs {
-    uint32_t w[4];
-};
-
-__device__ __forceinline__ uint32_t psi_word(const PsiRegs& pk, int t) {
-    switch (t >> 2) {
-        case 0: return pk.w[0];
-        case 1: return pk.w[1];
-        case 2: return pk.w[2];
-        default: return pk.w[3];
-    }
+    for (int u = 14; u >= 0; --u) arg = (v[u] == best) ? i0 + u : arg;
 }
 
 // Wave 0: delta over positions [t0, t1) of a group held in sm.ST.  Lane j
 // owns candidate j; delta_{t-1} reaches every lane through readlane (scalar
 // registers), 16 predecessors at a time, and the column S_t(., j) comes from
-// LDS with 16-byte reads.  Lanes j >= K carry -inf.  psi goes to registers
-// (P <= 16) or to LDS.
+// LDS with 16-byte reads.  Lanes j >= K carry -inf.
 template <int KP>
-__device__ float walk_steps(int t0, int t1, int K, float delta, bool psi_regs, PsiRegs& pk,
-                            WalkLds& sm) {
+__device__ float walk_steps(int t0, int t1, int K, float delta, WalkLds& sm) {
     const int lane = lane_id();
     const int j = lane % KP;
     const bool jv = lane < K;
@@ -116,18 +93,7 @@ __device__ float walk_steps(int t0, int t1, int K, float delta, bool psi_regs, P
         }
         delta = __int_as_float((int)((__float_as_int(best) & keep) | (ninf & ~keep)));
         // arg < K for finite scores; the clamp keeps NaN inputs in bounds
-        const uint32_t a = (uint32_t)min(arg, K - 1);
-        if (psi_regs) {
-            const uint32_t v = a << (8 * (t & 3));
-            switch (t >> 2) {
-                case 0: pk.w[0] |= v; break;
-                case 1: pk.w[1] |= v; break;
-                case 2: pk.w[2] |= v; break;
-                default: pk.w[3] |= v; break;
-            }
-        } else if (jv) {
-            sm.psi[t * K + j] = (uint8_t)a;
-        }
+        if (jv) sm.psi[t * K + j] = (uint8_t)min(arg, K - 1);
     }
     return delta;
 }
@@ -145,8 +111,6 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
     const int KK = K * K, KP2 = KP * KP;
     const int G = kWalkS / KP2;
     const bool ids_lds = P * K <= kWalkIds;
-    const bool psi_regs = P <= 16;
-    PsiRegs pk = {{0u, 0u, 0u, 0u}};
     float delta = -INFINITY;
     for (int t0 = 0; t0 < P; t0 += G) {
         const int t1 = min(P, t0 + G);
@@ -183,9 +147,9 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
         }
         __syncthreads();
         if (w == 0) {
-            if (KP == 16) delta = walk_steps<16>(t0, t1, K, delta, psi_regs, pk, sm);
-            else if (KP == 32) delta = walk_steps<32>(t0, t1, K, delta, psi_regs, pk, sm);
-            else delta = walk_steps<64>(t0, t1, K, delta, psi_regs, pk, sm);
+            if (KP == 16) delta = walk_steps<16>(t0, t1, K, delta, sm);
+            else if (KP == 32) delta = walk_steps<32>(t0, t1, K, delta, sm);
+            else delta = walk_steps<64>(t0, t1, K, delta, sm);
         }
         __syncthreads();
     }
@@ -208,15 +172,11 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
             jb = ca;
         }
     }
-    // backtrack: jj is uniform; psi_t(jj) comes from lane jj's register
-    // (readlane) or from LDS
+    // backtrack (jj is uniform)
     int jj = min(jb, K - 1);
     for (int t = P - 1; t > 0; --t) {
         if (lane == 0) sm.rank[t] = jj;
-        if (psi_regs)
-            jj = (int)((__builtin_amdgcn_readlane(psi_word(pk, t), jj) >> (8 * (t & 3))) & 63u);
-        else
-            jj = sm.psi[t * K + jj];
+        jj = sm.psi[t * K + jj];
     }
     if (lane == 0) {
         sm.rank[0] = jj;
