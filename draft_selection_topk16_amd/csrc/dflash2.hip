@@ -63,7 +63,7 @@ struct Params {
     float* out_score;
     float* H;             // standalone projection output [M, r]
     // scratch
-    uint64_t* part;       // [rows, nseg, K] candidate words
+    uint64_t* part;       // [rows, nseg, 4, K] candidate words (a sorted list per wave)
     int32_t* cand;        // [rows, K]
     float* cval;          // [rows, K]
     float* ppart;         // [S, M, r] gate partials
@@ -121,7 +121,7 @@ __device__ void segment_of(const Params& p, int64_t row, int seg, ChunkLds& sm) 
     const size_t esz = BF16 ? 2 : 4;
     const char* rowp = reinterpret_cast<const char*>(p.logits) + (size_t)row * p.V * esz;
     segment_topk<BF16, NV>(rowp, p.V, p.C, seg, p.nseg, p.K, p.aligned != 0,
-                           p.part + ((size_t)row * p.nseg + seg) * p.K, sm);
+                           p.part + ((size_t)row * p.nseg + seg) * kWaves * p.K, sm);
 }
 
 __device__ __forceinline__ int32_t checked_id(int32_t id, int V, uint32_t* err, uint32_t bit) {
@@ -223,7 +223,8 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
         return h;
     };
     merge_row<BF16>(
-        p.part + (size_t)row * p.nseg * K, p.nseg, K, p.cand + row * K, p.cval + row * K, sm.m,
+        p.part + (size_t)row * p.nseg * kWaves * K, p.nseg * kWaves, K, p.cand + row * K,
+        p.cval + row * K, sm.m,
         [&] {
             if (tid == 0) sm.m.aux = xload(&p.gate_cnt[mt]);
         },
@@ -306,8 +307,8 @@ __global__ __launch_bounds__(kWG, 5) void k_topk(Params p) {
     segment_of<BF16, NV>(p, row, (int)(blockIdx.x % p.nseg), sm.c);
     if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
     if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
-    merge_row<BF16>(p.part + (size_t)row * p.nseg * p.K, p.nseg, p.K, p.cand + row * p.K,
-                    p.cval + row * p.K, sm.m);
+    merge_row<BF16>(p.part + (size_t)row * p.nseg * kWaves * p.K, p.nseg * kWaves, p.K,
+                    p.cand + row * p.K, p.cval + row * p.K, sm.m);
 }
 
 // Gate projection alone: slices into H (S == 1) or into partials.
@@ -518,9 +519,9 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     target = std::max<int64_t>(1, env_int("DF2_WGS", (int)std::min<int64_t>(target, 1 << 30)));
     // at most kMergeMax words per row merge; fewer lists also make the merge
     // bound sharper
-    const int max_lists = std::max(1, std::min(kMergeMax, env_int("DF2_MWORDS", 256)) / K);
+    const int max_segs = std::max(1, std::min(kMergeMax, env_int("DF2_MWORDS", 1024)) / (kWaves * K));
     int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, target / rows));
-    p.nseg = std::min(nseg, max_lists);
+    p.nseg = std::min(nseg, max_segs);
     p.rows = rows;
     p.V = V;
     p.K = K;
@@ -561,7 +562,7 @@ void plan_layout(Plan& pl, int64_t rows, int64_t M, int B, bool pairs) {
     pl.counter_bytes = align_up(ncnt * 4, 256);
     size_t off = pl.counter_bytes;
     pl.off_part = off;
-    off = align_up(off + (size_t)rows * p.nseg * p.K * 8, 256);
+    off = align_up(off + (size_t)rows * p.nseg * kWaves * p.K * 8, 256);
     pl.off_cand = off;
     off = align_up(off + (size_t)rows * p.K * 4, 256);
     pl.off_cval = off;

@@ -2,8 +2,8 @@
 // section "A Lightweight Path Selector": keep the top 16 candidates at each
 // draft position).
 //
-// Stage 1 (segment): a workgroup streams a contiguous segment of one row.
-// Each of its four waves works on its own: it streams every fourth chunk of
+// Stage 1 (segment): a workgroup streams one segment of one row (every
+// nseg-th chunk of the row).  Each of its four waves works on its own: it streams every fourth chunk of
 // 64 lanes x NV 16-byte vectors, with the next chunk's loads issued before
 // the current chunk is processed (two register buffers), and keeps its best
 // K candidate words in registers, one word per lane, sorted.  Per chunk each
@@ -15,20 +15,20 @@
 // values of the row are known to reach: the wave's own K-th kept key, or the
 // best K-th kept key of the workgroup's four waves (an LDS word each wave
 // raises with an atomic max; any wave's K-th key bounds the row's K-th
-// largest value from below).  With nothing known yet, the K-th largest lane
-// maximum of the chunk is the bound.  Once a few chunks have been seen, most
+// largest value from below).  The first bound of each wave is the K-th
+// largest of its 64 lane maxima over its first chunk.  Once a few chunks have been seen, most
 // chunks have no lane that reaches the bound and cost a handful of
 // instructions.  Vectors that do reach it are keyed exactly from
 // registers; words that beat the K-th kept word are compacted (ballot) into
 // an LDS buffer, which is merged into the list (all ranks found in parallel)
 // once to establish it and then only when it fills.  No step of a chunk
-// needs a workgroup barrier.
-// At the end of the segment the four waves' lists are merged the same way.
+// needs a workgroup barrier.  At the end of the segment each wave's sorted
+// list is handed on as it is.
 //
-// Stage 2 (merge): the last segment of a row to finish merges the segments'
-// sorted lists with the whole workgroup (block_merge_lists): a bound (the
-// best K-th word of any list), compaction of the words that reach it, and
-// ranks by counting.
+// Stage 2 (merge): the last segment of a row to finish merges the row's
+// sorted lists (four per segment) with the whole workgroup
+// (block_merge_lists): a bound (the best K-th word of any list), compaction
+// of the words that reach it, and ranks by counting.
 //
 // Candidate words (key << 32 | ~index) are distinct within a row, so every
 // selection is exact and independent of arrival order: results are
@@ -43,7 +43,6 @@ namespace df2 {
 
 constexpr int kMaxNV = 4;           // 16-byte vectors per lane per chunk
 constexpr int kMergeMax = 1024;     // words merged per row (segment lists * K)
-constexpr int kListWords = 256;     // words one wave merge takes (the four waves' lists, K <= 64)
 static_assert(kMergeMax % kWG == 0, "whole words per thread when a row is loaded");
 
 constexpr int kWCand = 256;         // candidate words buffered per wave
@@ -58,11 +57,8 @@ struct WaveLds {
 
 struct ChunkLds {
     WaveLds wv[kWaves];
-    uint64_t fin[kWaves * 64];          // the waves' lists at the end of a segment
-    uint32_t lkey[kWG];                 // lane maxima of the first chunk
     uint32_t bound;                     // a key at least K values of the segment reach
     uint32_t qkey[kWaves];              // each wave's ceil(K/4)-th kept key
-    uint64_t top[64];                   // merge output
 };
 
 struct MergeLds {
@@ -70,6 +66,7 @@ struct MergeLds {
     uint64_t tk, tc;                    // bound candidates
     uint32_t m;                         // survivors
     uint32_t aux;                       // for the caller's hooks
+    uint32_t aux2;                      // head bound
 };
 
 template <bool BF16>
@@ -193,84 +190,6 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
     return ((uint64_t)hi << 32) | lo;
-}
-
-// Top K of nl sorted lists of K words (lists[l * K + k], descending, zero
-// padded), by one wave: emit(rank, word) is called once for every word of
-// rank < K.  Bound T: a word that at least K words reach, so every word of
-// the top K is >= T.  Two such words are known from the lists' order: the
-// largest K-th word of any list (that list alone holds K words that reach
-// it), and the smallest c-th word over all lists with c = ceil(K / nl)
-// (every list holds c words that reach it).  Words >= T are compacted in
-// place and ranked by counting.  nl * K <= kListWords.
-template <typename Emit>
-__device__ void wave_merge_lists_emit(uint64_t* lists, int nl, int K, Emit&& emit) {
-    const int lane = lane_id();
-    const int n = nl * K;
-    const int c = (K + nl - 1) / nl;
-    // LDS reads are issued eight at a time (indexes clamped into range) so
-    // that loops do not wait for each read in turn.
-    uint64_t Tk = 0, Tc = ~0ull;
-    for (int l0 = 0; l0 < nl; l0 += 8) {
-        uint64_t tk[8], tc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int l = min(l0 + j, nl - 1);
-            tk[j] = lists[l * K + K - 1];
-            tc[j] = lists[l * K + c - 1];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            Tk = tk[j] > Tk ? tk[j] : Tk;
-            Tc = tc[j] < Tc ? tc[j] : Tc;
-        }
-    }
-    uint64_t T = Tk > Tc ? Tk : Tc;
-    T = T ? T : 1ull;
-    uint64_t x[kListWords / 64];
-#pragma unroll
-    for (int q = 0; q < kListWords / 64; ++q) {
-        const int e = q * 64 + lane;
-        x[q] = (e < n) ? lists[e] : 0ull;
-    }
-    wave_sync();
-    int m = 0;
-#pragma unroll
-    for (int q = 0; q < kListWords / 64; ++q) {
-        if (q * 64 < n) {
-            const bool s = x[q] >= T;
-            const uint64_t bal = __ballot(s);
-            if (s) lists[m + __popcll(bal & ((1ull << lane) - 1ull))] = x[q];
-            m += __popcll(bal);
-        }
-    }
-    wave_sync();
-    for (int s0 = 0; s0 < m; s0 += 64) {
-        const int si = s0 + lane;
-        const uint64_t y = (si < m) ? lists[si] : 0ull;
-        int rank = 0;
-        for (int u0 = 0; u0 < m; u0 += 8) {
-            uint64_t v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = lists[min(u0 + j, m - 1)];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rank += (u0 + j < m && v[j] > y) ? 1 : 0;
-        }
-        if (si < m && rank < K) emit(rank, y);
-    }
-    wave_sync();
-}
-
-// The same, returning the k-th best word in lane k (0 where there is none);
-// top: K words of LDS.
-__device__ uint64_t wave_merge_lists(uint64_t* lists, int nl, int K, uint64_t* top) {
-    const int lane = lane_id();
-    if (lane < K) top[lane] = 0ull;
-    wave_sync();
-    wave_merge_lists_emit(lists, nl, K, [&](int rank, uint64_t y) { top[rank] = y; });
-    const uint64_t res = (lane < K) ? top[lane] : 0ull;
-    wave_sync();
-    return res;
 }
 
 // Merges m distinct candidate words c[0..m) (LDS, written by this wave) into
@@ -411,7 +330,7 @@ __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV
 // the workgroups of a row read neighbouring chunks at any one time.
 //   row: first element of the row; V: row length; K <= 64.
 //   ALIGNED: the row start is 16-byte aligned and V is a multiple of kPerVec.
-//   out: K hand-off words (0 for empty slots).
+//   out: 4 x K hand-off words, one sorted list per wave (0 for empty slots).
 template <bool BF16, int NV, bool ALIGNED>
 __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, int cs, int nc,
                                   int split, int K, uint64_t* __restrict__ out, ChunkLds& sm) {
@@ -461,31 +380,31 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     // prefetch re-reads the last chunk (in bounds, never consumed).
     u32x4_t b0[NV], b1[NV];
     const int clast = nc - 1;
+    // The shared bounds start at zero (one barrier, before any load is in
+    // flight).
+    if (tid == 0) sm.bound = 0;
+    if (tid < kWaves) sm.qkey[tid] = 0;
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(0) + (int64_t)(j * 64 + lane) * PV);
     {
-        // Initial bound: the K-th largest of the workgroup's 256 lane maxima
-        // over its first chunk (one barrier per segment).
+        // Initial bound, per wave: the K-th largest of its 64 lane maxima
+        // over its first chunk (K lane maxima reach it); published with an
+        // atomic max, no barrier.
         u32x4_t v[NV];
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             v[j] = mask_vec<ALIGNED>(b0[j], eb_of(0) + (int64_t)(j * 64 + lane) * PV, V);
-        sm.lkey[tid] = lane_max_key<BF16, NV>(v);
-        if (tid < kWaves) sm.qkey[tid] = 0;
-        __syncthreads();
-        const uint32_t q0 = sm.lkey[lane], q1 = sm.lkey[lane + 64];
-        const uint32_t q2 = sm.lkey[lane + 128], q3 = sm.lkey[lane + 192];
+        const uint32_t q0 = lane_max_key<BF16, NV>(v);
         uint32_t T = 0;
 #pragma unroll 1
         for (int bit = Elem<BF16>::kKeyBits - 1; bit >= 0; --bit) {
             const uint32_t c = T | (1u << bit);
-            const int cnt = ballot_count(q0 >= c) + ballot_count(q1 >= c) + ballot_count(q2 >= c) +
-                            ballot_count(q3 >= c);
-            if (cnt >= K) T = c;
+            if (ballot_count(q0 >= c) >= K) T = c;
         }
-        if (tid == 0) sm.bound = T;
-        __syncthreads();
+        if (lane == 0)
+            __hip_atomic_fetch_max(&sm.bound, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     for (int c = 0; c < nc; c += 2) {
         const int cn = min(c + 1, clast);
@@ -507,13 +426,9 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
         __builtin_amdgcn_sched_barrier(0);
     }
     settle(true);
-    // Merge the four waves' sorted lists; the best K leave in order.
-    if (lane < K) sm.fin[w * K + lane] = tk;
-    __syncthreads();
-    if (w == 0) {
-        const uint64_t x = wave_merge_lists(sm.fin, kWaves, K, sm.top);
-        if (lane < K) xstore(out + lane, x);
-    }
+    // Each wave's sorted list leaves as it is; the row merge takes the
+    // segments' four lists each.
+    if (lane < K) xstore(out + w * K + lane, tk);
 }
 
 // Segment seg of nseg of a row of C chunks (chunks seg, seg + nseg, ...).
@@ -540,7 +455,7 @@ __device__ void segment_topk(const void* __restrict__ row, int V, int C, int seg
 // pre() runs right after the list loads are issued and mid() right after the
 // first barrier, so that a caller can overlap loads of its own with the merge.
 template <typename Emit, typename Pre, typename Mid>
-__device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, int K,
+__device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, int K, int keybits,
                                   MergeLds& sm, Emit&& emit, Pre&& pre, Mid&& mid) {
     constexpr int Q = kMergeMax / kWG;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -557,33 +472,61 @@ __device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, in
     pre();
     __syncthreads();
     mid();
+    // Few lists: the best K-th word of any list and the smallest c-th word
+    // (LDS atomics, at most 2 nl of them).  Many lists (K <= nl <= 64): the
+    // K-th largest head key, which is much sharper and avoids contended
+    // atomics.
+    const bool heads = nl >= K && nl <= 64;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int e = q * kWG + tid;
         if (e < n) {
             const int k = e % K;
-            if (k == K - 1)
-                __hip_atomic_fetch_max(&sm.tk, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (k == c - 1)
-                __hip_atomic_fetch_min(&sm.tc, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (heads) {
+                if (k == 0) sm.surv[e / K] = x[q];
+            } else {
+                if (k == K - 1)
+                    __hip_atomic_fetch_max(&sm.tk, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (k == c - 1)
+                    __hip_atomic_fetch_min(&sm.tc, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         }
     }
     __syncthreads();
-    uint64_t T = sm.tk > sm.tc ? sm.tk : sm.tc;
+    uint64_t T = heads ? 0ull : (sm.tk > sm.tc ? sm.tk : sm.tc);
+    if (heads) {
+        // With many lists: the K-th largest value key among the lists'
+        // heads (K heads reach it), by a bitwise search over ballot counts.
+        if (tid < 64) {
+            const uint32_t hk = (lane < nl) ? (uint32_t)(sm.surv[lane] >> 32) : 0u;
+            uint32_t th = 0;
+            for (int bit = keybits - 1; bit >= 0; --bit) {
+                const uint32_t cb = th | (1u << bit);
+                if (ballot_count(hk >= cb) >= K) th = cb;
+            }
+            if (tid == 0) sm.aux2 = th;
+        }
+        __syncthreads();
+        const uint64_t Th = (uint64_t)sm.aux2 << 32;
+        T = T > Th ? T : Th;
+    }
     T = T ? T : 1ull;
-    // compaction: one LDS add per wave and round reserves the wave's slots
+    // compaction: one LDS add per wave reserves the wave's slots
+    uint64_t bal[Q];
+    uint32_t cnt = 0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        if (q * kWG < n) {
-            const bool sv = (q * kWG + tid < n) && x[q] >= T;
-            const uint64_t bal = __ballot(sv);
-            uint32_t base = 0;
-            if (lane == 0 && bal)
-                base = __hip_atomic_fetch_add(&sm.m, (uint32_t)__popcll(bal), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_WORKGROUP);
-            base = __builtin_amdgcn_readfirstlane(base);
-            if (sv) sm.surv[base + __popcll(bal & ((1ull << lane) - 1ull))] = x[q];
-        }
+        bal[q] = __ballot((q * kWG + tid < n) && x[q] >= T);
+        cnt += (uint32_t)__popcll(bal[q]);
+    }
+    uint32_t base = 0;
+    if (lane == 0 && cnt)
+        base = __hip_atomic_fetch_add(&sm.m, cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if ((bal[q] >> lane) & 1ull) sm.surv[base + __popcll(bal[q] & ((1ull << lane) - 1ull))] = x[q];
+        base += (uint32_t)__popcll(bal[q]);
     }
     __syncthreads();
     const int m = (int)sm.m;
@@ -611,7 +554,7 @@ __device__ void merge_row(const uint64_t* __restrict__ part, int nseg, int K,
                           MergeLds& sm, Pre&& pre, Mid&& mid) {
     using E = Elem<BF16>;
     block_merge_lists(
-        part, nseg, K, sm,
+        part, nseg, K, Elem<BF16>::kKeyBits, sm,
         [&](int rank, uint64_t y) {
             xstore(out_idx + rank, (int32_t)cand_index(y));
             xstore(out_val + rank, E::value((uint32_t)(y >> 32)));
