@@ -107,15 +107,22 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float):
     for i in range(warmup):
         calls[i % nsets]()
     torch.cuda.synchronize()
+    # whole-job throughput: the K timed launches back to back, nothing else
+    # on the stream, synchronised on both sides
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[(warmup + i) % nsets]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-launch duration for the roofline: the same launches again, each
+    # between two HIP events on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         calls[(warmup + i) % nsets]()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ks = sorted(a.elapsed_time(b) for a, b in ev)      # ms per launch
     res = dict(ms_per_step=wall * 1e3 / steps,
                kernel_ms_avg=statistics.fmean(ks),
