@@ -6,8 +6,9 @@ by bench.py's cpu_baseline leg.  The GPU product path never imports it.
 All arithmetic is float64 on inputs widened exactly from their storage type.
 The steps follow "DFlash 2: Keep Drafting Parallel", section "A Lightweight
 Path Selector" (top-16 candidates, the pair-score equation, one walk from the
-last verified token); the walk is read as max-sum Viterbi with backtrack and
-H(h_t) as a bias-free linear map d -> r (see the header of oracle.c).
+last verified token); the walk is read as max-sum Viterbi with backtrack, the
+literal greedy walk is a second mode, and H(h_t) is read as a bias-free
+linear map d -> r (see the header of oracle.c).
 
 Every function here is pinned by CPU tests against something other than
 itself (brute-force enumeration, closed forms, exact integer cases, an
@@ -55,6 +56,8 @@ def _load():
         lib.orc_pair_scores.restype = None
         lib.orc_viterbi.argtypes = [P, P, I, I, I, P, P, P]
         lib.orc_viterbi.restype = ctypes.c_int
+        lib.orc_greedy.argtypes = [P, P, I, I, I, P, P, P]
+        lib.orc_greedy.restype = None
         lib.orc_second_best.argtypes = [P, P, I, I, I, P]
         lib.orc_second_best.restype = ctypes.c_int
         _lib = lib
@@ -126,6 +129,28 @@ def viterbi(S, cand):
     return pr, pt, sc
 
 
+def greedy(S, cand):
+    """Greedy walk: (path_rank [B,P] int32, path_tok [B,P] int32, score [B] float64)."""
+    S = _f64(S)
+    cand = _i32(cand)
+    Bn, P, K = cand.shape
+    pr = np.empty((Bn, P), dtype=np.int32)
+    pt = np.empty((Bn, P), dtype=np.int32)
+    sc = np.empty(Bn, dtype=np.float64)
+    _load().orc_greedy(_p(S), _p(cand), Bn, P, K, _p(pr), _p(pt), _p(sc))
+    return pr, pt, sc
+
+
+def path_sigma(sig, path_rank) -> np.ndarray:
+    """Sum of the tolerance scale sigma along each rank path (row 0 at t = 0)."""
+    Bn, P = path_rank.shape
+    out = np.zeros(Bn, dtype=np.float64)
+    for b in range(Bn):
+        out[b] = sig[b, 0, 0, path_rank[b, 0]] + sum(
+            sig[b, t, path_rank[b, t - 1], path_rank[b, t]] for t in range(1, P))
+    return out
+
+
 def second_best(S, path_rank) -> np.ndarray:
     """Second-best path score per sequence (-inf when K == 1)."""
     S = _f64(S)
@@ -156,11 +181,9 @@ def select(logits, hidden, A, Bt, W, prev, K: int,
     S, sig = pair_scores(cand, U, H, A, Bt, prev)
     pr, pt, sc = viterbi(S, cand)
     sec = second_best(S, pr)
-    P = cand.shape[1]
-    # scale of the best path: sum of sigma along it (tolerance for scores)
-    sig_path = np.zeros(cand.shape[0], dtype=np.float64)
-    for b in range(cand.shape[0]):
-        sig_path[b] = sig[b, 0, 0, pr[b, 0]] + sum(
-            sig[b, t, pr[b, t - 1], pr[b, t]] for t in range(1, P))
+    gr, gt, gs = greedy(S, cand)
+    # scale of each path's score: sum of sigma along it (tolerance for scores)
     return dict(cand=cand, U=U, H=H, S=S, sigma=sig, path_rank=pr, path=pt,
-                score=sc, second=sec, margin=sc - sec, sigma_path=sig_path)
+                score=sc, second=sec, margin=sc - sec, sigma_path=path_sigma(sig, pr),
+                greedy_rank=gr, greedy_path=gt, greedy_score=gs,
+                sigma_greedy=path_sigma(sig, gr))

@@ -23,7 +23,8 @@
  *       H[q] = sum_m W_H[q][m] * h_t[m]           (W_H stored [r][d]).
  *   - The walk is a max-sum (Viterbi) pass plus backtrack over the
  *     candidate lattice; the predecessor of the first draft position is the
- *     last verified token prev_tok.
+ *     last verified token prev_tok.  The literal left-to-right greedy walk
+ *     (orc_greedy) is kept beside it as a second walk mode.
  *   - Top-K order is value descending; equal values (IEEE equality, so
  *     -0 == +0) go to the lower vocabulary index.
  *   - Viterbi ties go to the smaller predecessor rank; the final pick goes
@@ -198,6 +199,36 @@ int orc_viterbi(const double* S, const int32_t* cand, int64_t Bn, int64_t P,
     free(delta);
     free(psi);
     return 0;
+}
+
+/*
+ * The greedy walk: the literal reading of "greedy follows the best successor
+ * at each step" (same page and section).  Starting from the last verified
+ * token, each position keeps the candidate whose pair score, given the token
+ * just chosen, is largest:
+ *   j_0 = argmax_j S[b][0][0][j]             (t = 0 predecessor is prev_tok)
+ *   j_t = argmax_j S[b][t][j_{t-1}][j],      t >= 1
+ *   score[b] = sum_t S[b][t][j_{t-1}][j_t]   (j_{-1} = row 0), summed from t = 0
+ * Ties go to the smaller rank.  Outputs as for orc_viterbi.
+ */
+void orc_greedy(const double* S, const int32_t* cand, int64_t Bn, int64_t P,
+                int64_t K, int32_t* path_rank, int32_t* path_tok, double* score) {
+    for (int64_t b = 0; b < Bn; ++b) {
+        const double* Sb = S + b * P * K * K;
+        int64_t i = 0;                  /* rank of the predecessor */
+        double total = 0.0;
+        for (int64_t t = 0; t < P; ++t) {
+            const double* row = Sb + (t * K + i) * K;
+            int64_t jb = 0;
+            for (int64_t j = 1; j < K; ++j)
+                if (row[j] > row[jb]) jb = j;
+            total += row[jb];
+            path_rank[b * P + t] = (int32_t)jb;
+            path_tok[b * P + t] = cand[(b * P + t) * K + jb];
+            i = jb;
+        }
+        score[b] = total;
+    }
 }
 
 /*

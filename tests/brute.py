@@ -64,3 +64,34 @@ def enumerate_paths(logits, hidden, A, Bt, W, prev, K):
             path=np.array([cand[b, t, best_ranks[t]] for t in range(P)], dtype=np.int64),
             score=best, second=second, all=scored, cand=cand[b], U=U[b], H=H[b]))
     return out
+
+
+def greedy_from_ids(logits, hidden, A, Bt, W, prev, K):
+    """Left-to-right greedy walk scored straight from token ids.
+
+    At each position, every candidate is scored with the pair-score equation
+    against the token chosen one step earlier (prev_tok before the first
+    position); the largest step score wins, the lower rank on ties.  Returns
+    per sequence (ranks, tokens, score), the score summed from t = 0."""
+    logits = np.asarray(logits, dtype=np.float64)
+    B, P, _ = logits.shape
+    cand, U = topk_lexsort(logits, K)
+    H = np.matmul(np.asarray(hidden, dtype=np.float64), np.asarray(W, dtype=np.float64).T)
+    A = np.asarray(A, dtype=np.float64)
+    Bt = np.asarray(Bt, dtype=np.float64)
+    out = []
+    for b in range(B):
+        pred = int(prev[b])
+        ranks, toks, total = [], [], 0.0
+        for t in range(P):
+            steps = [U[b, t, j] + float(np.sum(A[pred] * H[b, t] * Bt[int(cand[b, t, j])]))
+                     for j in range(K)]
+            best = max(steps)
+            j = steps.index(best)          # first (lowest-rank) maximiser
+            ranks.append(j)
+            toks.append(int(cand[b, t, j]))
+            total += best
+            pred = toks[-1]
+        out.append(dict(ranks=np.array(ranks, dtype=np.int64),
+                        path=np.array(toks, dtype=np.int64), score=total))
+    return out

@@ -36,6 +36,9 @@ def main():
         lines.append("path_rank " + fmt(o["path_rank"].ravel()))
         lines.append("score " + fmt(o["score"].ravel()))
         lines.append("second " + fmt(o["second"].ravel()))
+        lines.append("greedy_path " + fmt(o["greedy_path"].ravel()))
+        lines.append("greedy_rank " + fmt(o["greedy_rank"].ravel()))
+        lines.append("greedy_score " + fmt(o["greedy_score"].ravel()))
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
         print("wrote", os.path.basename(path))

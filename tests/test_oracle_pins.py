@@ -5,7 +5,8 @@ independent sort, or hand-worked fixtures under tests/golden/.
 Method: "DFlash 2: Keep Drafting Parallel", section "A Lightweight Path
 Selector": top-16 candidates per position, pair score
 S_t(a,b) = U_t(b) + <A(a) * H(h_t), B(b)>, one walk from the last verified
-token (read as max-sum Viterbi with backtrack).
+token (read as max-sum Viterbi with backtrack; the literal greedy walk is a
+second mode).
 """
 import glob
 import os
@@ -14,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from brute import enumerate_paths, topk_lexsort
+from brute import enumerate_paths, greedy_from_ids, topk_lexsort
 from golden.golden_io import read_fixture
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -58,6 +59,15 @@ def test_golden_fixture(path):
     assert bf[0]["path"].tolist() == [int(x) for x in exp["path"]]
     assert bf[0]["score"] == exp["score"][0]
     assert bf[0]["second"] == exp["second"][0]
+    # the greedy walk, where the fixture derives it by hand
+    if "greedy_path" in exp:
+        assert o["greedy_path"].ravel().tolist() == [int(x) for x in exp["greedy_path"]]
+        assert o["greedy_rank"].ravel().tolist() == [int(x) for x in exp["greedy_rank"]]
+        assert o["greedy_score"][0] == exp["greedy_score"][0]
+        gb = greedy_from_ids(fx["logits"], fx["hidden"], fx["A"], fx["Bt"], fx["W"], fx["prev"],
+                             fx["K"])
+        assert gb[0]["path"].tolist() == [int(x) for x in exp["greedy_path"]]
+        assert gb[0]["score"] == exp["greedy_score"][0]
 
 
 # ---------------------------------------------------------- brute force: paths
@@ -267,3 +277,75 @@ def test_margin_zero_on_exact_tie():
                       np.array([0], dtype=np.int32), K)
     assert o["path"][0].tolist() == [4, 4, 4]
     assert o["margin"][0] == 0.0
+
+
+# ------------------------------------------------------------------ greedy walk
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("K,P", [(2, 5), (4, 3), (5, 6), (16, 4), (1, 3), (3, 1)])
+def test_greedy_matches_step_scores_from_ids(seed, K, P):
+    """The oracle's greedy walk (over its S table) against a walk that scores
+    each step straight from token ids."""
+    rng = np.random.default_rng(3000 * seed + 10 * K + P)
+    c = rand_case(rng, B=3, P=P, V=61, d=12, r=8, K=K, pair=1.5)
+    o = run_oracle(c, K)
+    gb = greedy_from_ids(c["logits"], c["hidden"], c["A"], c["Bt"], c["W"], c["prev"], K)
+    for b in range(3):
+        assert o["greedy_rank"][b].tolist() == gb[b]["ranks"].tolist()
+        assert o["greedy_path"][b].tolist() == gb[b]["path"].tolist()
+        assert o["greedy_score"][b] == pytest.approx(gb[b]["score"], rel=1e-12, abs=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_greedy_integer_ties(seed):
+    """Exact integer scores with many ties: the lower rank must win each step."""
+    rng = np.random.default_rng(500 + seed)
+    K, P = 4, 5
+    c = rand_case(rng, B=3, P=P, V=9, d=4, r=4, K=K, integer=True)
+    o = run_oracle(c, K)
+    gb = greedy_from_ids(c["logits"], c["hidden"], c["A"], c["Bt"], c["W"], c["prev"], K)
+    for b in range(3):
+        assert o["greedy_rank"][b].tolist() == gb[b]["ranks"].tolist()
+        assert o["greedy_score"][b] == gb[b]["score"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_greedy_is_one_of_the_enumerated_paths_and_never_beats_viterbi(seed):
+    """Greedy's score is the enumerated score of its own path, and no greater
+    than the best path's."""
+    rng = np.random.default_rng(40 + seed)
+    K, P = 3, 4
+    c = rand_case(rng, B=2, P=P, V=23, d=8, r=6, K=K, pair=2.0)
+    o = run_oracle(c, K)
+    bf = enumerate_paths(c["logits"], c["hidden"], c["A"], c["Bt"], c["W"], c["prev"], K)
+    for b in range(2):
+        table = {tuple(rk): sc for rk, sc in bf[b]["all"]}
+        own = table[tuple(int(x) for x in o["greedy_rank"][b])]
+        assert o["greedy_score"][b] == pytest.approx(own, rel=1e-12, abs=1e-12)
+        assert o["greedy_score"][b] <= bf[b]["score"] + 1e-12
+
+
+@pytest.mark.parametrize("zero", ["A", "Bt", "W"])
+def test_greedy_zero_pair_term_is_top1(zero):
+    """Without the pair term each step is the top-1 candidate, as for Viterbi."""
+    rng = np.random.default_rng(21)
+    K, P = 16, 7
+    c = rand_case(rng, B=3, P=P, V=500, d=32, r=16, K=K)
+    c[zero] = np.zeros_like(c[zero])
+    o = run_oracle(c, K)
+    top1 = np.argmax(c["logits"], axis=-1)
+    assert np.array_equal(o["greedy_path"], top1)
+    assert np.array_equal(o["greedy_path"], o["path"])
+    assert np.allclose(o["greedy_score"], c["logits"].max(axis=-1).sum(axis=-1), rtol=0, atol=1e-12)
+
+
+def test_greedy_k1_and_p1():
+    """K = 1 leaves one path; P = 1 makes greedy and Viterbi the same argmax."""
+    rng = np.random.default_rng(22)
+    c = rand_case(rng, B=2, P=5, V=300, d=16, r=8, K=1, pair=3.0)
+    o = run_oracle(c, 1)
+    assert np.array_equal(o["greedy_path"], np.argmax(c["logits"], axis=-1))
+    assert np.array_equal(o["greedy_score"], o["score"])
+    c = rand_case(rng, B=4, P=1, V=200, d=16, r=8, K=8, pair=3.0)
+    o = run_oracle(c, 8)
+    assert np.array_equal(o["greedy_path"], o["path"])
+    assert np.array_equal(o["greedy_score"], o["score"])
