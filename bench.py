@@ -16,6 +16,9 @@ Prints ONE JSON line:
               draft-verify cycle;
   roofline    algorithmic bytes per launch / average launch time (HIP events on
               the launch stream) against the 8 TB/s HBM peak;
+  greedy      the same workloads with the greedy walk in place of the max-sum
+              walk, and how often the two walks' paths differ (on the timed
+              workload and on its pair-dominant variant);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -78,7 +81,9 @@ def traffic_for(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def time_workload(wl, steps: int, warmup: int, rotate_mb: float):
+def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi",)):
+    """Times dflash2_select_walk on `wl` for each walk in `walks` (same inputs);
+    returns (inputs, {walk: timings}, {walk: path of the first input set})."""
     import torch
     import draft_selection_topk16_amd as df2
     from draft_selection_topk16_amd import synth
@@ -101,9 +106,24 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float):
     per_set = logits.nbytes + hidden.nbytes
     nsets = max(1, int(math.ceil(rotate_mb * 1e6 / per_set)))
     sets = [(logits, hidden)] + [(logits.clone(), hidden.clone()) for _ in range(nsets - 1)]
-    calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K) for (l, h) in sets]
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    results, paths = {}, {}
+    for walk in walks:
+        calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K, walk=walk) for (l, h) in sets]
+        torch.cuda.synchronize()
+        results[walk] = _time_calls(calls, nsets, steps, warmup, stream)
+        results[walk].update(rotation_sets=nsets, rotation_mb=nsets * per_set / 1e6)
+        calls[0]()
+        torch.cuda.synchronize()
+        paths[walk] = calls[0].out_path.cpu().numpy().copy()
+        del calls
+    del sets
+    torch.cuda.empty_cache()
+    return x, results, paths
+
+
+def _time_calls(calls, nsets: int, steps: int, warmup: int, stream):
+    import torch
     for i in range(warmup):
         calls[i % nsets]()
     torch.cuda.synchronize()
@@ -127,8 +147,7 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float):
     res = dict(ms_per_step=wall * 1e3 / steps,
                kernel_ms_avg=statistics.fmean(ks),
                kernel_ms_p10=ks[len(ks) // 10], kernel_ms_p50=ks[len(ks) // 2],
-               kernel_ms_p90=ks[(9 * len(ks)) // 10],
-               rotation_sets=nsets, rotation_mb=nsets * per_set / 1e6)
+               kernel_ms_p90=ks[(9 * len(ks)) // 10])
     # warm (same buffers every step) for reference only
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -136,9 +155,17 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float):
         calls[0]()
     torch.cuda.synchronize()
     res["warm_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
-    del calls, sets
-    torch.cuda.empty_cache()
-    return x, res
+    return res
+
+
+def _differ(paths):
+    """Sequences whose greedy path differs from the Viterbi path."""
+    import numpy as np
+    g, v = paths["greedy"], paths["viterbi"]
+    n = int(np.sum(np.any(g != v, axis=1)))
+    pos = int(np.sum(g != v))
+    return {"sequences": n, "of_sequences": int(g.shape[0]), "positions": pos,
+            "of_positions": int(g.size)}
 
 
 def cpu_baseline(x, seconds: float):
@@ -184,6 +211,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b1", action="store_true")
+    ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
     args = ap.parse_args()
 
@@ -208,7 +236,9 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
-    x, res = time_workload(wl, args.steps, args.warmup, args.rotate_mb)
+    walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy")
+    x, allres, paths = time_workload(wl, args.steps, args.warmup, args.rotate_mb, walks)
+    res = allres["viterbi"]
     pos_per_s = wl.B * wl.P / (res["ms_per_step"] * 1e-3)
     abytes = algorithmic_bytes(wl)
     achieved = abytes / (res["kernel_ms_avg"] * 1e-3) / 1e9
@@ -240,10 +270,21 @@ def main():
                      "kernel": "k_select (fused selector)",
                      "algorithmic_bytes_per_launch": abytes},
     }
+    if not args.no_greedy:
+        g = allres["greedy"]
+        out["greedy"] = {"walk": "greedy (best successor of the token just chosen)",
+                         "workload": wl.name,
+                         "us_per_cycle": g["ms_per_step"] * 1e3,
+                         "kernel_us_avg": g["kernel_ms_avg"] * 1e3,
+                         "positions_per_s": wl.B * wl.P / (g["ms_per_step"] * 1e-3),
+                         "paths_differ_from_viterbi": _differ(paths),
+                         "timing": g}
+    r1 = None
     if not args.no_b1:
         wl1 = synth.WORKLOADS[args.b1_workload]
         log("timing %s" % wl1.name)
-        _, r1 = time_workload(wl1, args.steps, args.warmup, args.rotate_mb)
+        _, allr1, _ = time_workload(wl1, args.steps, args.warmup, args.rotate_mb, walks)
+        r1 = allr1["viterbi"]
         ab1 = algorithmic_bytes(wl1)
         out["b1"] = {"workload": "%s: B=%d P=%d V=%d d=%d K=%d" % (wl1.name, wl1.B, wl1.P, wl1.V, wl1.d, wl1.K),
                      "us_per_cycle": r1["ms_per_step"] * 1e3,
@@ -251,6 +292,17 @@ def main():
                      "positions_per_s": wl1.B * wl1.P / (r1["ms_per_step"] * 1e-3),
                      "hbm_frac": ab1 / (r1["kernel_ms_avg"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "timing": r1}
+        if not args.no_greedy:
+            g1 = allr1["greedy"]
+            out["greedy"]["b1"] = {"workload": wl1.name,
+                                   "us_per_cycle": g1["ms_per_step"] * 1e3,
+                                   "kernel_us_avg": g1["kernel_ms_avg"] * 1e3}
+    if not args.no_greedy:
+        wlp = wl.with_(pair_scale=8.0)
+        log("greedy vs Viterbi on the pair-dominant variant of %s" % wl.name)
+        _, _, pp = time_workload(wlp, 3, 1, 0.0, walks)
+        out["greedy"]["pair_dominant"] = {"workload": "%s with A and B scaled by 8" % wl.name,
+                                          "paths_differ_from_viterbi": _differ(pp)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle for %.0f s" % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

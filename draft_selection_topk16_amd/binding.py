@@ -18,10 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libdflash2.so")
 DF2_F32 = 0
 DF2_BF16 = 1
 
+# df2_walk
+WALKS = {"viterbi": 0, "greedy": 1}
+
 EXPORTED = (
-    "dflash2_select", "dflash2_topk", "dflash2_project", "dflash2_pair_scores",
-    "dflash2_viterbi", "dflash2_device_error", "dflash2_release",
-    "dflash2_status_string", "dflash2_last_error", "dflash2_version",
+    "dflash2_select", "dflash2_select_walk", "dflash2_topk", "dflash2_project",
+    "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk", "dflash2_device_error",
+    "dflash2_release", "dflash2_status_string", "dflash2_last_error", "dflash2_version",
 )
 
 
@@ -55,10 +58,12 @@ def load() -> ctypes.CDLL:
     dp = ctypes.POINTER(Dims)
     sig = {
         "dflash2_select": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
+        "dflash2_select_walk": [dp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp, vp],
         "dflash2_topk": [vp, i64, i32, ctypes.c_int, i32, vp, vp, vp],
         "dflash2_project": [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp],
         "dflash2_pair_scores": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp],
         "dflash2_viterbi": [vp, vp, i32, i32, i32, vp, vp, vp],
+        "dflash2_walk": [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp],
         "dflash2_device_error": [vp, u32p],
         "dflash2_release": [],
     }
@@ -104,17 +109,24 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _walk_code(walk: str) -> int:
+    if walk not in WALKS:
+        raise ValueError("walk must be one of %s" % sorted(WALKS))
+    return WALKS[walk]
+
+
 class PreparedSelect:
-    """The checked arguments of one dflash2_select call, for repeated
+    """The checked arguments of one dflash2_select_walk call, for repeated
     launches with little host overhead (the tensors are kept alive and must
     not be reallocated).  Calling it enqueues one launch on the stream that
-    was current when it was prepared."""
+    was current when it was prepared.  walk: "viterbi" or "greedy"."""
 
     def __init__(self, logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor,
                  Bt: torch.Tensor, W: torch.Tensor, prev: torch.Tensor, K: int,
                  out_path: Optional[torch.Tensor] = None,
-                 out_score: Optional[torch.Tensor] = None):
+                 out_score: Optional[torch.Tensor] = None, walk: str = "viterbi"):
         lib = load()
+        wcode = _walk_code(walk)
         B, P, V = logits.shape
         d = hidden.shape[-1]
         r = A.shape[-1]
@@ -134,10 +146,10 @@ class PreparedSelect:
         self.out_path, self.out_score = out_path, out_score
         self._keep = (logits, hidden, A, Bt, W, prev)
         self._dims = Dims(B, P, V, d, r, dt)
-        self._fn = lib.dflash2_select
+        self._fn = lib.dflash2_select_walk
         self._args = (ctypes.byref(self._dims), _dev(logits, "logits"), _dev(hidden, "hidden"),
                       _dev(A, "A"), _dev(Bt, "Bt"), _dev(W, "W"), _dev(prev, "prev"), int(K),
-                      _dev(out_path, "out_path"), _dev(out_score, "out_score"),
+                      wcode, _dev(out_path, "out_path"), _dev(out_score, "out_score"),
                       _stream(logits.device))
 
     def __call__(self) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -148,9 +160,11 @@ class PreparedSelect:
 def select(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torch.Tensor,
            W: torch.Tensor, prev: torch.Tensor, K: int,
            out_path: Optional[torch.Tensor] = None,
-           out_score: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Selected path [B, P] int32 and its score [B] float32 (one launch)."""
-    return PreparedSelect(logits, hidden, A, Bt, W, prev, K, out_path, out_score)()
+           out_score: Optional[torch.Tensor] = None,
+           walk: str = "viterbi") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Selected path [B, P] int32 and its score [B] float32 (one launch);
+    walk: "viterbi" (max-sum with backtrack) or "greedy"."""
+    return PreparedSelect(logits, hidden, A, Bt, W, prev, K, out_path, out_score, walk)()
 
 
 def topk(logits: torch.Tensor, K: int) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -200,6 +214,18 @@ def viterbi(S: torch.Tensor, cand: torch.Tensor) -> Tuple[torch.Tensor, torch.Te
     score = torch.empty((B,), dtype=torch.float32, device=S.device)
     _check(lib.dflash2_viterbi(_dev(S, "S"), _dev(cand, "cand"), B, P, K, _dev(path, "path"),
                                _dev(score, "score"), _stream(S.device)))
+    return path, score
+
+
+def walk(S: torch.Tensor, cand: torch.Tensor, mode: str = "viterbi") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Walk over S [B, P, K, K] in either mode: (path [B, P] int32, score [B] float32)."""
+    lib = load()
+    wcode = _walk_code(mode)
+    B, P, K = cand.shape
+    path = torch.empty((B, P), dtype=torch.int32, device=S.device)
+    score = torch.empty((B,), dtype=torch.float32, device=S.device)
+    _check(lib.dflash2_walk(_dev(S, "S"), _dev(cand, "cand"), B, P, K, wcode, _dev(path, "path"),
+                            _dev(score, "score"), _stream(S.device)))
     return path, score
 
 

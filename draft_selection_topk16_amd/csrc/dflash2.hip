@@ -85,6 +85,7 @@ struct Params {
     int mtiles, ntiles, S, n_gate;
     int64_t n_chunk;      // segment workgroups (rows * nseg)
     int64_t base;         // index of the launch's first workgroup
+    int walk;             // df2_walk: max-sum pass with backtrack, or greedy
 };
 
 union SharedAll {
@@ -295,7 +296,10 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     if (!flag) return;
     if (tid == 0) reset_counter(&p.seq_cnt[b]);
     const int64_t rb = (int64_t)b * P;
-    walk_seq(p.Sb + rb * K * K, p.cand + rb * K, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+    if (p.walk == DF2_WALK_GREEDY)
+        greedy_seq(p.Sb + rb * K * K, p.cand + rb * K, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+    else
+        walk_seq(p.Sb + rb * K * K, p.cand + rb * K, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
 // Top-K alone: segments, then the row merge on last arrival.
@@ -378,13 +382,18 @@ struct WalkArgs {
     int32_t* out_path;
     float* out_score;
     int P, K;
+    int walk;             // df2_walk
 };
 
 __global__ __launch_bounds__(kWG) void k_walk(WalkArgs a) {
     __shared__ WalkLds sm;
     const int64_t b = blockIdx.x;
-    walk_seq(a.S + b * a.P * a.K * a.K, a.cand + b * a.P * a.K, a.P, a.K, a.out_path + b * a.P,
-             a.out_score + b, sm);
+    const float* S = a.S + b * a.P * a.K * a.K;
+    const int32_t* ids = a.cand + b * a.P * a.K;
+    if (a.walk == DF2_WALK_GREEDY)
+        greedy_seq(S, ids, a.P, a.K, a.out_path + b * a.P, a.out_score + b, sm);
+    else
+        walk_seq(S, ids, a.P, a.K, a.out_path + b * a.P, a.out_score + b, sm);
 }
 
 // ----------------------------------------------------------------------------
@@ -700,11 +709,13 @@ const char* dflash2_status_string(df2_status s) {
 
 const char* dflash2_last_error(void) { return g_last_error.c_str(); }
 
-df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* hidden,
-                          const void* A_tab, const void* B_tab, const void* W_H,
-                          const int32_t* prev_tok, int32_t K, int32_t* out_path,
-                          float* out_score, hipStream_t stream) {
+df2_status dflash2_select_walk(const df2_dims* dims, const void* logits, const void* hidden,
+                               const void* A_tab, const void* B_tab, const void* W_H,
+                               const int32_t* prev_tok, int32_t K, df2_walk walk,
+                               int32_t* out_path, float* out_score, hipStream_t stream) {
     g_last_error.clear();
+    if (walk != DF2_WALK_VITERBI && walk != DF2_WALK_GREEDY)
+        return fail(DF2_EINVAL, "unknown walk mode");
     df2_status st = check_dims(dims, true);
     if (st != DF2_OK) return st;
     if ((st = check_k(K, dims->V)) != DF2_OK) return st;
@@ -739,11 +750,20 @@ df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* 
     p.out_score = out_score;
     p.B = dims->B;
     p.P = dims->P;
+    p.walk = (int)walk;
     void* base = nullptr;
     if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
     note_layout(stream, pl.counter_bytes);
     bind_scratch(pl, base, rows, dims->B);
     return launch_checked([&] { launch_select(pl, stream); }, "dflash2_select launch");
+}
+
+df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* hidden,
+                          const void* A_tab, const void* B_tab, const void* W_H,
+                          const int32_t* prev_tok, int32_t K, int32_t* out_path,
+                          float* out_score, hipStream_t stream) {
+    return dflash2_select_walk(dims, logits, hidden, A_tab, B_tab, W_H, prev_tok, K,
+                               DF2_WALK_VITERBI, out_path, out_score, stream);
 }
 
 df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V, df2_dtype dtype, int32_t K,
@@ -853,9 +873,11 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
     }, "dflash2_pair_scores launch");
 }
 
-df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,
-                           int32_t K, int32_t* out_path, float* out_score, hipStream_t stream) {
+df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B, int32_t P, int32_t K,
+                        df2_walk walk, int32_t* out_path, float* out_score, hipStream_t stream) {
     g_last_error.clear();
+    if (walk != DF2_WALK_VITERBI && walk != DF2_WALK_GREEDY)
+        return fail(DF2_EINVAL, "unknown walk mode");
     if (B < 0) return fail(DF2_EINVAL, "B < 0");
     if (P < 1 || P > kMaxP) return fail(DF2_EINVAL, "P must be in [1, 64]");
     if (K < 1 || K > kMaxK) return fail(DF2_EINVAL, "K must be in [1, 64]");
@@ -871,9 +893,15 @@ df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, i
     a.out_score = out_score;
     a.P = P;
     a.K = K;
+    a.walk = (int)walk;
     dim3 grid((unsigned)B), block(kWG);
     return launch_checked([&] { hipLaunchKernelGGL(k_walk, grid, block, 0, stream, a); },
-                          "dflash2_viterbi launch");
+                          "dflash2_walk launch");
+}
+
+df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,
+                           int32_t K, int32_t* out_path, float* out_score, hipStream_t stream) {
+    return dflash2_walk(S, cand_idx, B, P, K, DF2_WALK_VITERBI, out_path, out_score, stream);
 }
 
 df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {

@@ -13,6 +13,12 @@
 // from scalar registers (no LDS round trip per step).  Scores enter LDS
 // transposed (column j contiguous, padded to Kp = K rounded up to 16, 32 or
 // 64), a group of positions at a time.
+//
+// The same section also describes the walk literally as greedy: from the
+// last verified token, each position takes the best successor of the token
+// chosen one step earlier.  greedy_seq does that: every thread of the
+// workgroup finds the best successor of one (position, predecessor) pair at
+// once, and the chain through those choices is then a few register reads.
 #pragma once
 
 #include <math.h>
@@ -182,6 +188,86 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
         sm.rank[0] = jj;
         *out_score = m;
     }
+    wave_sync();
+    for (int t = lane; t < P; t += 64) {
+        const int rk = sm.rank[t];
+        out_path[t] = ids_lds ? sm.ids[t * K + rk] : xload(ids + (int64_t)t * K + rk);
+    }
+}
+
+// The greedy walk of one sequence; arguments, outputs and tie rule as for
+// walk_seq:
+//     j_0 = argmax_j S_0(0, j),  j_t = argmax_j S_t(j_{t-1}, j),
+//     score = S_0(0, j_0) + S_1(j_0, j_1) + ... in fp32, in order of t.
+// Step 1, every thread: for each row (t, i) it owns, the best successor
+// nx(t, i) and its score; both go to LDS (sm.psi, sm.ST as [P, K]).
+// Step 2, wave 0: lane i holds nx(t, i) and its score for a few positions
+// at a time, and the chain j_t = nx(t, j_{t-1}) runs through readlane.
+// Every thread of the workgroup calls.
+__device__ __forceinline__ void greedy_seq(const float* __restrict__ S, const int32_t* __restrict__ ids,
+                                           int P, int K, int32_t* __restrict__ out_path,
+                                           float* __restrict__ out_score, WalkLds& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int PK = P * K;
+    const bool ids_lds = PK <= kWalkIds;
+    constexpr int QI = kWalkIds / kWG;
+    int32_t idv[QI];
+#pragma unroll
+    for (int q = 0; q < QI; ++q) idv[q] = ids_lds ? xload(ids + min(q * kWG + tid, PK - 1)) : 0;
+    for (int e = tid; e < PK; e += kWG) {
+        // row (t, i) = (e / K, e % K) starts at S + e * K
+        const float* row = S + (int64_t)e * K;
+        float best = -INFINITY;
+        int arg = 0;
+        for (int c = 0; c < K; c += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = xload(row + min(c + u, K - 1));
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                // strictly greater: the lower rank keeps a tie
+                if (c + u < K && (c + u == 0 || v[u] > best)) {
+                    best = v[u];
+                    arg = c + u;
+                }
+            }
+        }
+        sm.psi[e] = (uint8_t)arg;
+        sm.ST[e] = best;
+    }
+    if (ids_lds) {
+#pragma unroll
+        for (int q = 0; q < QI; ++q)
+            if (q * kWG + tid < PK) sm.ids[q * kWG + tid] = idv[q];
+    }
+    __syncthreads();
+    if (w != 0) return;
+    // eight positions at a time: their LDS reads go out together, then the
+    // chain runs through readlane (more at once costs registers elsewhere)
+    constexpr int G = 8;
+    const int li = min(lane, K - 1);
+    int j = 0;
+    float score = 0.f;
+#pragma unroll 1
+    for (int t0 = 0; t0 < P; t0 += G) {
+        int nx[G];
+        float sv[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const int e = min(t0 + u, P - 1) * K + li;
+            nx[u] = sm.psi[e];
+            sv[u] = sm.ST[e];
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            if (t0 + u < P) {
+                score += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv[u]), j));
+                j = __builtin_amdgcn_readlane(nx[u], j);
+                if (lane == 0) sm.rank[t0 + u] = j;
+            }
+        }
+    }
+    if (lane == 0) *out_score = score;
     wave_sync();
     for (int t = lane; t < P; t += 64) {
         const int rk = sm.rank[t];

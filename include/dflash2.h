@@ -12,7 +12,8 @@
  * embeddings, H(h_t) a gate computed from the drafter hidden state), and make
  * one walk over the precomputed scores, starting from the last verified
  * token.  This library reads H as a bias-free linear map d -> r,
- * H_t = W_H h_t, and the walk as a max-sum (Viterbi) pass with backtrack.
+ * H_t = W_H h_t, and the walk as a max-sum (Viterbi) pass with backtrack;
+ * the section's literal greedy walk is available as a second walk mode.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -50,6 +51,20 @@ extern "C" {
 
 /* Element type of logits, hidden, A_tab, B_tab and W_H (all the same). */
 typedef enum { DF2_F32 = 0, DF2_BF16 = 1 } df2_dtype;
+
+/*
+ * The walk over the pair scores.
+ *   DF2_WALK_VITERBI  max-sum pass plus backtrack: the path with the largest
+ *                     total score (ties: smaller predecessor rank, then
+ *                     smaller final rank).
+ *   DF2_WALK_GREEDY   the greedy walk of the same section: from the last
+ *                     verified token, each position takes the best successor
+ *                     of the token chosen one step earlier,
+ *                     j_0 = argmax_j S_0(prev, j), j_t = argmax_j S_t(j_{t-1}, j)
+ *                     (ties: smaller rank); the score is the sum of the chosen
+ *                     S_t, added in order of t.
+ */
+typedef enum { DF2_WALK_VITERBI = 0, DF2_WALK_GREEDY = 1 } df2_walk;
 
 typedef enum {
     DF2_OK = 0,
@@ -94,6 +109,18 @@ df2_status dflash2_select(const df2_dims* dims, const void* logits,
                           const int32_t* prev_tok, int32_t K,
                           int32_t* out_path, float* out_score,
                           hipStream_t stream);
+
+/*
+ * dflash2_select with a choice of walk (same section; see df2_walk).
+ * Arguments as for dflash2_select; `walk` outside df2_walk is DF2_EINVAL.
+ * dflash2_select is this call with DF2_WALK_VITERBI.
+ */
+df2_status dflash2_select_walk(const df2_dims* dims, const void* logits,
+                               const void* hidden, const void* A_tab,
+                               const void* B_tab, const void* W_H,
+                               const int32_t* prev_tok, int32_t K,
+                               df2_walk walk, int32_t* out_path,
+                               float* out_score, hipStream_t stream);
 
 /*
  * Top-K of each row ("keep the top 16 candidates at each position").
@@ -143,6 +170,15 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
 df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B,
                            int32_t P, int32_t K, int32_t* out_path,
                            float* out_score, hipStream_t stream);
+
+/*
+ * The walk alone, either mode (see df2_walk).  Arguments as for
+ * dflash2_viterbi, which is this call with DF2_WALK_VITERBI; 1 <= P <= 64,
+ * 1 <= K <= 64; S, cand_idx, out_path and out_score 4-byte aligned.
+ */
+df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B,
+                        int32_t P, int32_t K, df2_walk walk, int32_t* out_path,
+                        float* out_score, hipStream_t stream);
 
 /*
  * Waits for `stream`, then reports and clears the device-side flags of its

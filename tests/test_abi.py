@@ -98,6 +98,9 @@ def test_empty_batch_is_a_noop(lib):
     assert lib.dflash2_topk(FAKE, 0, 100, 1, 16, FAKE, FAKE, None) == DF2_OK
     assert lib.dflash2_project(FAKE, FAKE, 0, 64, 64, 1, FAKE, None) == DF2_OK
     assert lib.dflash2_viterbi(FAKE, FAKE, 0, 3, 4, FAKE, FAKE, None) == DF2_OK
+    assert lib.dflash2_walk(FAKE, FAKE, 0, 3, 4, 1, FAKE, FAKE, None) == DF2_OK
+    assert lib.dflash2_select_walk(ctypes.byref(Dims(0, 7, 32000, 1024, 256, 1)), FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, FAKE, None) == DF2_OK
 
 
 def test_stage_entry_points_reject_bad_arguments(lib):
@@ -113,12 +116,32 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     assert lib.dflash2_viterbi(FAKE, FAKE, 2, 0, 4, FAKE, FAKE, None) == DF2_EINVAL
     assert lib.dflash2_viterbi(FAKE, FAKE, 2, 3, 65, FAKE, FAKE, None) == DF2_EINVAL
     assert lib.dflash2_viterbi(None, FAKE, 2, 3, 4, FAKE, FAKE, None) == DF2_EINVAL
+    for mode in (0, 1):
+        assert lib.dflash2_walk(FAKE, FAKE, 2, 0, 4, mode, FAKE, FAKE, None) == DF2_EINVAL
+        assert lib.dflash2_walk(FAKE, FAKE, 2, 3, 65, mode, FAKE, FAKE, None) == DF2_EINVAL
+        assert lib.dflash2_walk(FAKE + 2, FAKE, 2, 3, 4, mode, FAKE, FAKE, None) == DF2_EINVAL
+    # an unknown walk mode is refused before anything else is looked at
+    assert lib.dflash2_walk(FAKE, FAKE, 2, 3, 4, 2, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_walk(FAKE, FAKE, 2, 3, 4, -1, FAKE, FAKE, None) == DF2_EINVAL
+    assert b"walk" in lib.dflash2_last_error()
+    dsel = Dims(1, 7, 32000, 1024, 256, 1)
+    assert lib.dflash2_select_walk(ctypes.byref(dsel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2,
+                                   FAKE, FAKE, None) == DF2_EINVAL
+    assert b"walk" in lib.dflash2_last_error()
     d = Dims(2, 3, 100, 32, 64, 1)
     assert lib.dflash2_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 4,
                                    FAKE, None) == DF2_EINVAL
     assert lib.dflash2_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 101,
                                    FAKE, None) == DF2_EINVAL
     assert lib.dflash2_device_error(None, None) == DF2_EINVAL
+
+
+def test_binding_rejects_unknown_walk_name():
+    import torch
+    S = torch.zeros(1, 2, 3, 3)
+    cand = torch.zeros(1, 2, 3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        df2.walk(S, cand, "beam")
 
 
 def test_binding_raises_without_gpu_tensors():

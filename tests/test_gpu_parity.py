@@ -12,7 +12,8 @@ import torch
 import oracle
 import draft_selection_topk16_amd as df2
 from draft_selection_topk16_amd import synth
-from gpu_util import (TOL, check_scores, check_select, dev_tensor, run_oracle, say, to_device)
+from gpu_util import (TOL, check_greedy, check_scores, check_select, dev_tensor, run_oracle, say,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,10 +203,56 @@ def test_viterbi_integer_ties_exact():
     assert np.array_equal(score.cpu().numpy().astype(np.float64), sc)
 
 
+@pytest.mark.parametrize("K,P", [(16, 7), (32, 15), (5, 3), (1, 4), (64, 2), (16, 64), (64, 64),
+                                 (3, 17)])
+def test_greedy_stage(K, P):
+    """Greedy decisions compare the same fp32 scores on both sides, so the
+    path must match exactly; the score is an fp32 sum in order of t."""
+    say("greedy walk K=%d P=%d" % (K, P))
+    rng = np.random.default_rng(K * 100 + P + 7)
+    B = 9
+    S = rng.standard_normal((B, P, K, K)).astype(np.float32)
+    S[:, 0, 1:, :] = S[:, 0, :1, :]
+    cand = rng.integers(0, 1 << 20, size=(B, P, K)).astype(np.int32)
+    path, score = df2.walk(torch.from_numpy(S).cuda(), torch.from_numpy(cand).cuda(), "greedy")
+    pr, pt, sc = oracle.greedy(S.astype(np.float64), cand)
+    assert np.array_equal(path.cpu().numpy(), pt)
+    score = score.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        mag = abs(S[b, 0, 0, pr[b, 0]]) + sum(abs(S[b, t, pr[b, t - 1], pr[b, t]]) for t in range(1, P))
+        assert abs(score[b] - sc[b]) <= 2.0 ** -23 * P * mag, (b, score[b], sc[b])
+
+
+def test_greedy_integer_ties_exact():
+    """Small integers: many exact ties, all sums exact; the lower rank wins."""
+    say("greedy walk integer ties")
+    rng = np.random.default_rng(43)
+    B, P, K = 16, 9, 8
+    S = rng.integers(-2, 3, size=(B, P, K, K)).astype(np.float32)
+    S[:, 0, 1:, :] = S[:, 0, :1, :]
+    cand = np.tile(np.arange(K, dtype=np.int32), (B, P, 1)) + 1000
+    path, score = df2.walk(torch.from_numpy(S).cuda(), torch.from_numpy(cand).cuda(), "greedy")
+    _, pt, sc = oracle.greedy(S.astype(np.float64), cand)
+    assert np.array_equal(path.cpu().numpy(), pt)
+    assert np.array_equal(score.cpu().numpy().astype(np.float64), sc)
+
+
+def test_walk_viterbi_mode_matches_viterbi_entry():
+    say("walk(viterbi) equals viterbi")
+    rng = np.random.default_rng(44)
+    B, P, K = 5, 11, 16
+    S = torch.from_numpy(rng.standard_normal((B, P, K, K)).astype(np.float32)).cuda()
+    cand = torch.from_numpy(rng.integers(0, 5000, size=(B, P, K)).astype(np.int32)).cuda()
+    p1, s1 = df2.viterbi(S, cand)
+    p2, s2 = df2.walk(S, cand, "viterbi")
+    assert torch.equal(p1, p2) and torch.equal(s1, s2)
+
+
 # ------------------------------------------------------------ whole select
-def gpu_select(x):
+def gpu_select(x, walk="viterbi"):
     t = to_device(x)
-    path, score = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K)
+    path, score = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K,
+                             walk=walk)
     torch.cuda.synchronize()
     return path.cpu().numpy(), score.cpu().numpy()
 
@@ -335,5 +382,88 @@ def test_stages_compose_to_select():
     S = df2.pair_scores(idx, val, H, t["A"], t["Bt"], t["prev"])
     p1, s1 = df2.viterbi(S, idx)
     p2, s2 = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], 16)
+    assert torch.equal(p1, p2)
+    assert torch.allclose(s1, s2, rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------ whole select, greedy
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_4b_b1", "t27b_b32", "stress_b256"])
+def test_select_greedy_workloads(name):
+    x = inputs(name)
+    say("select greedy %s B=%d P=%d V=%d K=%d" % (name, x.wl.B, x.wl.P, x.wl.V, x.wl.K))
+    path, score = gpu_select(x, "greedy")
+    seqs = STRESS_SEQS if name == "stress_b256" else None
+    o = run_oracle(x, seqs=seqs)
+    if seqs is not None:
+        path, score = path[seqs], score[seqs]
+    check_greedy(path, score, o, TOL[x.wl.dtype], name)
+    assert flags_clear()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {"pair_scale": 8.0, "V": 4000}),
+    ("qwen3_4b_b1", {"pair_scale": 8.0}),
+    ("t27b_b8", {"pair_scale": 8.0, "V": 30000, "d": 512}),
+])
+def test_select_greedy_pair_dominant(name, kw):
+    """Pair-dominant inputs: greedy and Viterbi part ways; both walks of the
+    GPU follow their oracle, and the share of sequences where the two walks'
+    paths differ is reported."""
+    x = inputs(name, **kw)
+    say("select greedy pair-dominant %s %s" % (name, kw))
+    gp, gs = gpu_select(x, "greedy")
+    vp, vs = gpu_select(x, "viterbi")
+    o = run_oracle(x)
+    check_greedy(gp, gs, o, TOL[x.wl.dtype], name + " greedy")
+    check_select(vp, vs, o, TOL[x.wl.dtype], name + " viterbi")
+    differ = int(np.sum(np.any(o["greedy_path"] != o["path"], axis=1)))
+    say("  greedy and Viterbi paths differ in %d of %d sequences (oracle); GPU: %d"
+        % (differ, o["path"].shape[0], int(np.sum(np.any(gp != vp, axis=1)))))
+    # the best path never scores below the greedy one
+    assert np.all(o["score"] >= o["greedy_score"] - 1e-9 * np.maximum(1.0, np.abs(o["score"])))
+
+
+@pytest.mark.parametrize("B,P,V,K,d", [(1, 1, 5000, 16, 64), (3, 64, 3000, 16, 64),
+                                       (2, 5, 64, 64, 64), (2, 4, 300, 1, 64),
+                                       (4, 7, 9999, 3, 96), (33, 7, 2048, 16, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_greedy_edge_shapes(B, P, V, K, d, dtype):
+    say("select greedy edge %s B=%d P=%d V=%d K=%d d=%d" % (dtype, B, P, V, K, d))
+    wl = synth.Workload("edge", 1, B=B, P=P, V=V, d=d, K=K, r=64, dtype=dtype, pair_scale=4.0)
+    x = synth.make_inputs(wl, seed=B * 1000 + P * 10 + K + 5)
+    path, score = gpu_select(x, "greedy")
+    check_greedy(path, score, run_oracle(x), TOL[dtype], "greedy edge")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_greedy_integer_exact(dtype):
+    """Small-integer inputs keep every step exact: the greedy path and score
+    match the oracle bit for bit, ties included."""
+    say("select greedy integer-exact %s" % dtype)
+    rng = np.random.default_rng(8)
+    B, P, V, d, r, K = 6, 9, 3000, 64, 64, 16
+    wl = synth.Workload("int", 0, B=B, P=P, V=V, d=d, K=K, r=r, dtype=dtype)
+    logits = rng.integers(-6, 7, size=(B, P, V)).astype(np.float32)
+    x = synth.make_inputs(wl, seed=124, logits_override=logits)
+    for k, shape in (("hidden", (B, P, d)), ("A", (V, r)), ("Bt", (V, r)), ("W", (r, d))):
+        v = rng.integers(-2, 3, size=shape).astype(np.float32)
+        setattr(x, k, synth.f32_to_bf16_bits(v) if dtype == "bf16" else v)
+    path, score = gpu_select(x, "greedy")
+    o = run_oracle(x)
+    assert np.array_equal(path, o["greedy_path"])
+    assert np.array_equal(score.astype(np.float64), o["greedy_score"])
+
+
+def test_greedy_stages_compose_to_select():
+    """topk -> project -> pair_scores -> walk(greedy) gives the fused greedy result."""
+    x = inputs("qwen3_4b_b1")
+    say("greedy stages compose")
+    t = to_device(x)
+    idx, val = df2.topk(t["logits"], 16)
+    H = df2.project(t["hidden"], t["W"])
+    S = df2.pair_scores(idx, val, H, t["A"], t["Bt"], t["prev"])
+    p1, s1 = df2.walk(S, idx, "greedy")
+    p2, s2 = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], 16,
+                        walk="greedy")
     assert torch.equal(p1, p2)
     assert torch.allclose(s1, s2, rtol=1e-6, atol=1e-6)
