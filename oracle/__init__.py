@@ -7,8 +7,8 @@ All arithmetic is float64 on inputs widened exactly from their storage type.
 The steps follow "DFlash 2: Keep Drafting Parallel", section "A Lightweight
 Path Selector" (top-16 candidates, the pair-score equation, one walk from the
 last verified token); the walk is read as max-sum Viterbi with backtrack, the
-literal greedy walk is a second mode, and H(h_t) is read as a bias-free
-linear map d -> r (see the header of oracle.c).
+literal greedy walk and the sampling walk are further modes, and H(h_t) is
+read as a bias-free linear map d -> r (see the header of oracle.c).
 
 Every function here is pinned by CPU tests against something other than
 itself (brute-force enumeration, closed forms, exact integer cases, an
@@ -58,6 +58,8 @@ def _load():
         lib.orc_viterbi.restype = ctypes.c_int
         lib.orc_greedy.argtypes = [P, P, I, I, I, P, P, P]
         lib.orc_greedy.restype = None
+        lib.orc_sample.argtypes = [P, P, P, I, I, I, ctypes.c_double, P, P, P, P]
+        lib.orc_sample.restype = ctypes.c_int
         lib.orc_second_best.argtypes = [P, P, I, I, I, P]
         lib.orc_second_best.restype = ctypes.c_int
         _lib = lib
@@ -141,6 +143,28 @@ def greedy(S, cand):
     return pr, pt, sc
 
 
+def sample(S, cand, u, tau: float):
+    """Sampling walk with uniforms u [B,P] in [0, 1) at temperature tau:
+    (path_rank [B,P] int32, path_tok [B,P] int32, prob [B,P] float64 = the
+    chosen candidate's step probability, score [B] float64)."""
+    S = _f64(S)
+    cand = _i32(cand)
+    u = _f64(u)
+    Bn, P, K = cand.shape
+    if u.shape != (Bn, P):
+        raise ValueError("u must be [B, P]")
+    if not (tau > 0 and np.isfinite(tau)):
+        raise ValueError("tau must be positive and finite")
+    pr = np.empty((Bn, P), dtype=np.int32)
+    pt = np.empty((Bn, P), dtype=np.int32)
+    q = np.empty((Bn, P), dtype=np.float64)
+    sc = np.empty(Bn, dtype=np.float64)
+    if _load().orc_sample(_p(S), _p(cand), _p(u), Bn, P, K, float(tau), _p(pr), _p(pt), _p(q),
+                          _p(sc)) != 0:
+        raise MemoryError("orc_sample")
+    return pr, pt, q, sc
+
+
 def path_sigma(sig, path_rank) -> np.ndarray:
     """Sum of the tolerance scale sigma along each rank path (row 0 at t = 0)."""
     Bn, P = path_rank.shape
@@ -164,18 +188,21 @@ def second_best(S, path_rank) -> np.ndarray:
 
 
 def select(logits, hidden, A, Bt, W, prev, K: int,
-           seqs: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+           seqs: Optional[np.ndarray] = None, u=None, tau: float = 1.0) -> Dict[str, np.ndarray]:
     """The whole selector on float64 inputs; returns every intermediate.
 
     logits [B,P,V], hidden [B,P,d], A/Bt [V,r], W [r,d], prev [B].
     `seqs` restricts the work to a subset of sequences (sampled checks on
-    large workloads); outputs then follow the order of `seqs`.
+    large workloads); outputs then follow the order of `seqs`.  With
+    uniforms u [B,P] the sampling walk at temperature tau is added.
     """
     if seqs is not None:
         seqs = np.asarray(seqs, dtype=np.int64)
         logits = np.asarray(logits)[seqs]
         hidden = np.asarray(hidden)[seqs]
         prev = np.asarray(prev)[seqs]
+        if u is not None:
+            u = np.asarray(u)[seqs]
     cand, U = topk(logits, K)
     H = project(hidden, W)
     S, sig = pair_scores(cand, U, H, A, Bt, prev)
@@ -183,7 +210,12 @@ def select(logits, hidden, A, Bt, W, prev, K: int,
     sec = second_best(S, pr)
     gr, gt, gs = greedy(S, cand)
     # scale of each path's score: sum of sigma along it (tolerance for scores)
-    return dict(cand=cand, U=U, H=H, S=S, sigma=sig, path_rank=pr, path=pt,
-                score=sc, second=sec, margin=sc - sec, sigma_path=path_sigma(sig, pr),
-                greedy_rank=gr, greedy_path=gt, greedy_score=gs,
-                sigma_greedy=path_sigma(sig, gr))
+    out = dict(cand=cand, U=U, H=H, S=S, sigma=sig, path_rank=pr, path=pt,
+               score=sc, second=sec, margin=sc - sec, sigma_path=path_sigma(sig, pr),
+               greedy_rank=gr, greedy_path=gt, greedy_score=gs,
+               sigma_greedy=path_sigma(sig, gr))
+    if u is not None:
+        sr, st, sq, ss = sample(S, cand, u, tau)
+        out.update(sample_rank=sr, sample_path=st, sample_prob=sq, sample_score=ss, u=np.asarray(u),
+                   tau=tau)
+    return out

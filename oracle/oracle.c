@@ -24,7 +24,9 @@
  *   - The walk is a max-sum (Viterbi) pass plus backtrack over the
  *     candidate lattice; the predecessor of the first draft position is the
  *     last verified token prev_tok.  The literal left-to-right greedy walk
- *     (orc_greedy) is kept beside it as a second walk mode.
+ *     (orc_greedy) and the sampling walk (orc_sample: inverse-CDF draws from
+ *     the softmax of each step's scores, uniforms supplied by the caller)
+ *     are kept beside it as further walk modes.
  *   - Top-K order is value descending; equal values (IEEE equality, so
  *     -0 == +0) go to the lower vocabulary index.
  *   - Viterbi ties go to the smaller predecessor rank; the final pick goes
@@ -229,6 +231,61 @@ void orc_greedy(const double* S, const int32_t* cand, int64_t Bn, int64_t P,
         }
         score[b] = total;
     }
+}
+
+/*
+ * The sampling walk: "sampling draws from the same scores" (same page and
+ * section), read as: from the last verified token, each position draws its
+ * candidate from the softmax of the pair scores of the token just chosen,
+ * at temperature tau, with the caller's uniform u[b][t] in [0, 1):
+ *   q_t(j) = exp((S_t(i, j) - m) / tau) / sum_k exp((S_t(i, k) - m) / tau),
+ *            m = max_k S_t(i, k), i = j_{t-1} (row 0 at t = 0)
+ *   j_t    = the smallest j with u[b][t] < q_t(0) + ... + q_t(j)
+ *            (if rounding leaves u above the last sum: the last j with
+ *            q_t(j) > 0)
+ * Outputs: ranks, tokens, prob[b][t] = q_t(j_t) (the draft probability that
+ * rejection sampling needs), score[b] = sum_t S_t(j_{t-1}, j_t) from t = 0.
+ * Returns 0, or -1 on allocation failure.
+ */
+int orc_sample(const double* S, const int32_t* cand, const double* u, int64_t Bn,
+               int64_t P, int64_t K, double tau, int32_t* path_rank,
+               int32_t* path_tok, double* prob, double* score) {
+    double* q = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!q) return -1;
+    for (int64_t b = 0; b < Bn; ++b) {
+        const double* Sb = S + b * P * K * K;
+        int64_t i = 0;
+        double total = 0.0;
+        for (int64_t t = 0; t < P; ++t) {
+            const double* row = Sb + (t * K + i) * K;
+            double m = row[0];
+            for (int64_t j = 1; j < K; ++j)
+                if (row[j] > m) m = row[j];
+            double z = 0.0;
+            for (int64_t j = 0; j < K; ++j) {
+                q[j] = exp((row[j] - m) / tau);
+                z += q[j];
+            }
+            for (int64_t j = 0; j < K; ++j) q[j] /= z;
+            const double ub = u[b * P + t];
+            int64_t pick = -1, last = 0;
+            double cdf = 0.0;
+            for (int64_t j = 0; j < K; ++j) {
+                cdf += q[j];
+                if (q[j] > 0.0) last = j;
+                if (pick < 0 && ub < cdf) pick = j;
+            }
+            if (pick < 0) pick = last;
+            total += row[pick];
+            path_rank[b * P + t] = (int32_t)pick;
+            path_tok[b * P + t] = cand[(b * P + t) * K + pick];
+            prob[b * P + t] = q[pick];
+            i = pick;
+        }
+        score[b] = total;
+    }
+    free(q);
+    return 0;
 }
 
 /*

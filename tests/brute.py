@@ -95,3 +95,37 @@ def greedy_from_ids(logits, hidden, A, Bt, W, prev, K):
         out.append(dict(ranks=np.array(ranks, dtype=np.int64),
                         path=np.array(toks, dtype=np.int64), score=total))
     return out
+
+
+def sample_from_ids(logits, hidden, A, Bt, W, prev, K, u, tau):
+    """Sampling walk scored straight from token ids: at each position the
+    step scores of every candidate (pair-score equation against the token
+    chosen one step earlier) go through scipy's softmax at temperature tau,
+    and u[b, t] picks by inverse CDF (numpy searchsorted on the cumulative
+    sum: the first j whose cumulative probability exceeds u)."""
+    from scipy.special import softmax
+    logits = np.asarray(logits, dtype=np.float64)
+    B, P, _ = logits.shape
+    cand, U = topk_lexsort(logits, K)
+    H = np.matmul(np.asarray(hidden, dtype=np.float64), np.asarray(W, dtype=np.float64).T)
+    A = np.asarray(A, dtype=np.float64)
+    Bt = np.asarray(Bt, dtype=np.float64)
+    out = []
+    for b in range(B):
+        pred = int(prev[b])
+        ranks, toks, probs, total = [], [], [], 0.0
+        for t in range(P):
+            steps = np.array([U[b, t, j] + float(np.sum(A[pred] * H[b, t] * Bt[int(cand[b, t, j])]))
+                              for j in range(K)])
+            q = softmax(steps / tau)
+            j = int(np.searchsorted(np.cumsum(q), u[b, t], side="right"))
+            if j >= K:
+                j = int(np.nonzero(q > 0)[0][-1])
+            ranks.append(j)
+            toks.append(int(cand[b, t, j]))
+            probs.append(float(q[j]))
+            total += steps[j]
+            pred = toks[-1]
+        out.append(dict(ranks=np.array(ranks, dtype=np.int64), path=np.array(toks, dtype=np.int64),
+                        prob=np.array(probs), score=total))
+    return out

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from brute import enumerate_paths, greedy_from_ids, topk_lexsort
+from brute import enumerate_paths, greedy_from_ids, sample_from_ids, topk_lexsort
 from golden.golden_io import read_fixture
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -349,3 +349,100 @@ def test_greedy_k1_and_p1():
     o = run_oracle(c, 8)
     assert np.array_equal(o["greedy_path"], o["path"])
     assert np.array_equal(o["greedy_score"], o["score"])
+
+
+# ---------------------------------------------------------------- sampling walk
+def run_sample(c, K, u, tau):
+    return oracle.select(c["logits"], c["hidden"], c["A"], c["Bt"], c["W"], c["prev"], K,
+                         u=u, tau=tau)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("K,P,tau", [(2, 5, 1.0), (4, 3, 0.5), (5, 6, 2.0), (16, 4, 1.0), (1, 3, 1.0),
+                                     (3, 1, 0.7)])
+def test_sample_matches_softmax_walk_from_ids(seed, K, P, tau):
+    rng = np.random.default_rng(7000 * seed + 10 * K + P)
+    c = rand_case(rng, B=3, P=P, V=61, d=12, r=8, K=K, pair=1.5)
+    u = rng.random((3, P))
+    o = run_sample(c, K, u, tau)
+    sb = sample_from_ids(c["logits"], c["hidden"], c["A"], c["Bt"], c["W"], c["prev"], K, u, tau)
+    for b in range(3):
+        assert o["sample_rank"][b].tolist() == sb[b]["ranks"].tolist()
+        assert o["sample_path"][b].tolist() == sb[b]["path"].tolist()
+        np.testing.assert_allclose(o["sample_prob"][b], sb[b]["prob"], rtol=1e-12, atol=1e-15)
+        assert o["sample_score"][b] == pytest.approx(sb[b]["score"], rel=1e-12, abs=1e-12)
+
+
+def test_sample_frequencies_on_a_grid_of_uniforms():
+    """One position, N evenly spaced uniforms: rank j is drawn by
+    N * q_j (+-1) of them, q from numpy's exp of the step scores."""
+    rng = np.random.default_rng(17)
+    K, N, tau = 6, 5000, 0.8
+    c = rand_case(rng, B=1, P=1, V=40, d=8, r=8, K=K, pair=1.0)
+    rep = {k: (np.repeat(v, N, axis=0) if k in ("logits", "hidden", "prev") else v) for k, v in c.items()}
+    u = ((np.arange(N) + 0.5) / N).reshape(N, 1)
+    o = run_sample(rep, K, u, tau)
+    cand, U = topk_lexsort(c["logits"], K)
+    H = c["hidden"][0, 0] @ c["W"].T
+    s = np.array([U[0, 0, j] + np.dot(c["A"][c["prev"][0]] * H, c["Bt"][cand[0, 0, j]]) for j in range(K)])
+    e = np.exp((s - s.max()) / tau)
+    q = e / e.sum()
+    counts = np.bincount(o["sample_rank"][:, 0], minlength=K)
+    assert np.all(np.abs(counts - N * q) <= 1.0), (counts, N * q)
+    np.testing.assert_allclose(o["sample_prob"][:, 0], q[o["sample_rank"][:, 0]], rtol=1e-12)
+
+
+def test_sample_zero_uniform_takes_rank0():
+    """u = 0 draws the first candidate with positive probability: rank 0."""
+    rng = np.random.default_rng(18)
+    K, P = 8, 6
+    c = rand_case(rng, B=2, P=P, V=100, d=8, r=8, K=K, pair=2.0)
+    o = run_sample(c, K, np.zeros((2, P)), 1.0)
+    assert np.all(o["sample_rank"] == 0)
+    for b in range(2):
+        assert o["sample_score"][b] == pytest.approx(sum(o["S"][b, t, 0, 0] for t in range(P)), rel=1e-14)
+
+
+def test_sample_small_temperature_is_greedy():
+    rng = np.random.default_rng(19)
+    K, P = 16, 7
+    c = rand_case(rng, B=4, P=P, V=300, d=16, r=8, K=K, pair=2.0)
+    o = run_sample(c, K, rng.random((4, P)), 1e-9)
+    assert np.array_equal(o["sample_rank"], o["greedy_rank"])
+    assert np.all(o["sample_prob"] == 1.0)
+    np.testing.assert_allclose(o["sample_score"], o["greedy_score"], rtol=1e-14)
+
+
+def test_sample_large_temperature_is_uniform():
+    """tau -> infinity: every candidate has probability 1/K, so u picks
+    rank floor(u * K) (uniforms kept away from the k / K boundaries)."""
+    rng = np.random.default_rng(20)
+    K, P = 5, 6
+    c = rand_case(rng, B=4, P=P, V=100, d=8, r=8, K=K, pair=2.0)
+    u = (rng.integers(0, K, size=(4, P)) + rng.uniform(0.05, 0.95, size=(4, P))) / K
+    o = run_sample(c, K, u, 1e15)
+    assert np.array_equal(o["sample_rank"], np.floor(u * K).astype(np.int32))
+    np.testing.assert_allclose(o["sample_prob"], 1.0 / K, rtol=1e-9)
+
+
+def test_sample_hand_lattice():
+    """greedy_trap_k2_p2.txt worked by hand at tau = 1 with u = (0.8, 0.5):
+    S_0 = (5, 4): q = (1/(1+e^-1), 1/(1+e)); 0.8 > 0.731 -> rank 1 (token 1);
+    row 1 of S_1 = (10, 5): q_0 = 1/(1+e^-5) = 0.9933 > 0.5 -> rank 0 (token 2);
+    score 4 + 10 = 14."""
+    fx, _ = read_fixture(os.path.join(GOLDEN, "greedy_trap_k2_p2.txt"))
+    o = oracle.select(fx["logits"], fx["hidden"], fx["A"], fx["Bt"], fx["W"], fx["prev"], fx["K"],
+                      u=np.array([[0.8, 0.5]]), tau=1.0)
+    assert o["sample_rank"][0].tolist() == [1, 0]
+    assert o["sample_path"][0].tolist() == [1, 2]
+    assert o["sample_prob"][0][0] == pytest.approx(1.0 / (1.0 + np.e), rel=1e-14)
+    assert o["sample_prob"][0][1] == pytest.approx(1.0 / (1.0 + np.exp(-5.0)), rel=1e-14)
+    assert o["sample_score"][0] == 14.0
+
+
+def test_sample_k1_probability_one():
+    rng = np.random.default_rng(21)
+    c = rand_case(rng, B=2, P=4, V=50, d=8, r=8, K=1)
+    o = run_sample(c, 1, rng.random((2, 4)), 1.0)
+    assert np.array_equal(o["sample_path"], np.argmax(c["logits"], axis=-1))
+    assert np.all(o["sample_prob"] == 1.0)
