@@ -19,6 +19,8 @@ Prints ONE JSON line:
   greedy      the same workloads with the greedy walk in place of the max-sum
               walk, and how often the two walks' paths differ (on the timed
               workload and on its pair-dominant variant);
+  sample      the same workloads with the sampling walk (temperature 1,
+              seeded uniforms resident on the device);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -108,8 +110,11 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi
     sets = [(logits, hidden)] + [(logits.clone(), hidden.clone()) for _ in range(nsets - 1)]
     stream = torch.cuda.current_stream()
     results, paths = {}, {}
+    g = torch.Generator().manual_seed(0xDF2)
+    u = torch.rand((wl.B, wl.P), generator=g, dtype=torch.float32).cuda()
     for walk in walks:
-        calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K, walk=walk) for (l, h) in sets]
+        calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K, walk=walk, u=u, temperature=1.0)
+                 for (l, h) in sets]
         torch.cuda.synchronize()
         results[walk] = _time_calls(calls, nsets, steps, warmup, stream)
         results[walk].update(rotation_sets=nsets, rotation_mb=nsets * per_set / 1e6)
@@ -236,7 +241,7 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
-    walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy")
+    walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy", "sample")
     x, allres, paths = time_workload(wl, args.steps, args.warmup, args.rotate_mb, walks)
     res = allres["viterbi"]
     pos_per_s = wl.B * wl.P / (res["ms_per_step"] * 1e-3)
@@ -279,6 +284,13 @@ def main():
                          "positions_per_s": wl.B * wl.P / (g["ms_per_step"] * 1e-3),
                          "paths_differ_from_viterbi": _differ(paths),
                          "timing": g}
+        sm = allres["sample"]
+        out["sample"] = {"walk": "sampling (softmax of the step's scores, temperature 1)",
+                         "workload": wl.name,
+                         "us_per_cycle": sm["ms_per_step"] * 1e3,
+                         "kernel_us_avg": sm["kernel_ms_avg"] * 1e3,
+                         "positions_per_s": wl.B * wl.P / (sm["ms_per_step"] * 1e-3),
+                         "timing": sm}
     r1 = None
     if not args.no_b1:
         wl1 = synth.WORKLOADS[args.b1_workload]
@@ -297,10 +309,14 @@ def main():
             out["greedy"]["b1"] = {"workload": wl1.name,
                                    "us_per_cycle": g1["ms_per_step"] * 1e3,
                                    "kernel_us_avg": g1["kernel_ms_avg"] * 1e3}
+            s1 = allr1["sample"]
+            out["sample"]["b1"] = {"workload": wl1.name,
+                                   "us_per_cycle": s1["ms_per_step"] * 1e3,
+                                   "kernel_us_avg": s1["kernel_ms_avg"] * 1e3}
     if not args.no_greedy:
         wlp = wl.with_(pair_scale=8.0)
         log("greedy vs Viterbi on the pair-dominant variant of %s" % wl.name)
-        _, _, pp = time_workload(wlp, 3, 1, 0.0, walks)
+        _, _, pp = time_workload(wlp, 3, 1, 0.0, ("viterbi", "greedy"))
         out["greedy"]["pair_dominant"] = {"workload": "%s with A and B scaled by 8" % wl.name,
                                           "paths_differ_from_viterbi": _differ(pp)}
     if not args.no_cpu_baseline:

@@ -6,7 +6,7 @@ inputs.  Importing the package does not load the library: the first call
 does, and raises if it has not been built.
 """
 from .binding import (PreparedSelect, SelectorError, device_error, load, pair_scores, project,
-                      release, select, topk, version, viterbi, walk)
+                      release, sample_walk, select, select_sample, topk, version, viterbi, walk)
 
 __all__ = ["PreparedSelect", "SelectorError", "device_error", "load", "pair_scores", "project", "release",
-           "select", "topk", "version", "viterbi", "walk"]
+           "sample_walk", "select", "select_sample", "topk", "version", "viterbi", "walk"]

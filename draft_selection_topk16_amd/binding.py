@@ -22,9 +22,10 @@ DF2_BF16 = 1
 WALKS = {"viterbi": 0, "greedy": 1}
 
 EXPORTED = (
-    "dflash2_select", "dflash2_select_walk", "dflash2_topk", "dflash2_project",
-    "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk", "dflash2_device_error",
-    "dflash2_release", "dflash2_status_string", "dflash2_last_error", "dflash2_version",
+    "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_topk",
+    "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
+    "dflash2_sample_walk", "dflash2_device_error", "dflash2_release", "dflash2_status_string",
+    "dflash2_last_error", "dflash2_version",
 )
 
 
@@ -59,11 +60,14 @@ def load() -> ctypes.CDLL:
     sig = {
         "dflash2_select": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
         "dflash2_select_walk": [dp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp, vp],
+        "dflash2_select_sample": [dp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp,
+                                  vp],
         "dflash2_topk": [vp, i64, i32, ctypes.c_int, i32, vp, vp, vp],
         "dflash2_project": [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp],
         "dflash2_pair_scores": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp],
         "dflash2_viterbi": [vp, vp, i32, i32, i32, vp, vp, vp],
         "dflash2_walk": [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp],
+        "dflash2_sample_walk": [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp],
         "dflash2_device_error": [vp, u32p],
         "dflash2_release": [],
     }
@@ -115,18 +119,31 @@ def _walk_code(walk: str) -> int:
     return WALKS[walk]
 
 
+def _uniforms(u: Optional[torch.Tensor], B: int, P: int) -> torch.Tensor:
+    if u is None:
+        raise ValueError("the sampling walk needs uniforms u [B, P]")
+    if u.dtype != torch.float32 or tuple(u.shape) != (B, P):
+        raise ValueError("u must be float32 [B, P]")
+    return u
+
+
 class PreparedSelect:
-    """The checked arguments of one dflash2_select_walk call, for repeated
-    launches with little host overhead (the tensors are kept alive and must
-    not be reallocated).  Calling it enqueues one launch on the stream that
-    was current when it was prepared.  walk: "viterbi" or "greedy"."""
+    """The checked arguments of one dflash2_select_walk (or, for walk="sample",
+    dflash2_select_sample) call, for repeated launches with little host
+    overhead (the tensors are kept alive and must not be reallocated; refill
+    `u` in place between launches to draw again).  Calling it enqueues one
+    launch on the stream that was current when it was prepared.
+    walk: "viterbi", "greedy" or "sample" (then u [B, P] float32 uniforms and
+    the temperature; the draws' probabilities land in self.out_q)."""
 
     def __init__(self, logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor,
                  Bt: torch.Tensor, W: torch.Tensor, prev: torch.Tensor, K: int,
                  out_path: Optional[torch.Tensor] = None,
-                 out_score: Optional[torch.Tensor] = None, walk: str = "viterbi"):
+                 out_score: Optional[torch.Tensor] = None, walk: str = "viterbi",
+                 u: Optional[torch.Tensor] = None, temperature: float = 1.0):
         lib = load()
-        wcode = _walk_code(walk)
+        sample = walk == "sample"
+        wcode = 0 if sample else _walk_code(walk)
         B, P, V = logits.shape
         d = hidden.shape[-1]
         r = A.shape[-1]
@@ -144,13 +161,23 @@ class PreparedSelect:
         if out_score is None:
             out_score = torch.empty((B,), dtype=torch.float32, device=logits.device)
         self.out_path, self.out_score = out_path, out_score
+        self.out_q = None
         self._keep = (logits, hidden, A, Bt, W, prev)
         self._dims = Dims(B, P, V, d, r, dt)
-        self._fn = lib.dflash2_select_walk
-        self._args = (ctypes.byref(self._dims), _dev(logits, "logits"), _dev(hidden, "hidden"),
-                      _dev(A, "A"), _dev(Bt, "Bt"), _dev(W, "W"), _dev(prev, "prev"), int(K),
-                      wcode, _dev(out_path, "out_path"), _dev(out_score, "out_score"),
-                      _stream(logits.device))
+        head = (ctypes.byref(self._dims), _dev(logits, "logits"), _dev(hidden, "hidden"),
+                _dev(A, "A"), _dev(Bt, "Bt"), _dev(W, "W"), _dev(prev, "prev"), int(K))
+        if sample:
+            u = _uniforms(u, B, P)
+            self.out_q = torch.empty((B, P), dtype=torch.float32, device=logits.device)
+            self._keep += (u,)
+            self._fn = lib.dflash2_select_sample
+            self._args = head + (float(temperature), _dev(u, "u"), _dev(out_path, "out_path"),
+                                 _dev(self.out_q, "out_q"), _dev(out_score, "out_score"),
+                                 _stream(logits.device))
+        else:
+            self._fn = lib.dflash2_select_walk
+            self._args = head + (wcode, _dev(out_path, "out_path"), _dev(out_score, "out_score"),
+                                 _stream(logits.device))
 
     def __call__(self) -> Tuple[torch.Tensor, torch.Tensor]:
         _check(self._fn(*self._args))
@@ -165,6 +192,18 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torc
     """Selected path [B, P] int32 and its score [B] float32 (one launch);
     walk: "viterbi" (max-sum with backtrack) or "greedy"."""
     return PreparedSelect(logits, hidden, A, Bt, W, prev, K, out_path, out_score, walk)()
+
+
+def select_sample(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torch.Tensor,
+                  W: torch.Tensor, prev: torch.Tensor, K: int, u: torch.Tensor,
+                  temperature: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Sampling walk in one launch: (path [B, P] int32, q [B, P] float32 =
+    each drawn token's probability, score [B] float32); u [B, P] float32
+    uniforms in [0, 1)."""
+    call = PreparedSelect(logits, hidden, A, Bt, W, prev, K, walk="sample", u=u,
+                          temperature=temperature)
+    path, score = call()
+    return path, call.out_q, score
 
 
 def topk(logits: torch.Tensor, K: int) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -227,6 +266,21 @@ def walk(S: torch.Tensor, cand: torch.Tensor, mode: str = "viterbi") -> Tuple[to
     _check(lib.dflash2_walk(_dev(S, "S"), _dev(cand, "cand"), B, P, K, wcode, _dev(path, "path"),
                             _dev(score, "score"), _stream(S.device)))
     return path, score
+
+
+def sample_walk(S: torch.Tensor, cand: torch.Tensor, u: torch.Tensor,
+                temperature: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Sampling walk over S [B, P, K, K]: (path, q, score) as select_sample."""
+    lib = load()
+    B, P, K = cand.shape
+    u = _uniforms(u, B, P)
+    path = torch.empty((B, P), dtype=torch.int32, device=S.device)
+    q = torch.empty((B, P), dtype=torch.float32, device=S.device)
+    score = torch.empty((B,), dtype=torch.float32, device=S.device)
+    _check(lib.dflash2_sample_walk(_dev(S, "S"), _dev(cand, "cand"), _dev(u, "u"), B, P, K,
+                                   float(temperature), _dev(path, "path"), _dev(q, "q"),
+                                   _dev(score, "score"), _stream(S.device)))
+    return path, q, score
 
 
 def device_error(device: Optional[torch.device] = None) -> int:

@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -85,8 +86,16 @@ struct Params {
     int mtiles, ntiles, S, n_gate;
     int64_t n_chunk;      // segment workgroups (rows * nseg)
     int64_t base;         // index of the launch's first workgroup
-    int walk;             // df2_walk: max-sum pass with backtrack, or greedy
+    int walk;             // kWalkViterbi, kWalkGreedy or kWalkSample
+    const float* u;       // [B, P] uniforms of the sampling walk
+    float* out_q;         // [B, P] probabilities of the sampled choices
+    float inv_tau;        // 1 / temperature of the sampling walk
 };
+
+// Walk modes inside the launch: the two of df2_walk, and the sampling walk.
+constexpr int kWalkViterbi = DF2_WALK_VITERBI;
+constexpr int kWalkGreedy = DF2_WALK_GREEDY;
+constexpr int kWalkSample = 2;
 
 union SharedAll {
     ChunkLds c;
@@ -182,7 +191,7 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
 }
 
 // The whole selector in one launch.
-template <bool BF16, int NV, int MB>
+template <bool BF16, int NV, int MB, bool SAMPLE>
 __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
@@ -296,10 +305,15 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     if (!flag) return;
     if (tid == 0) reset_counter(&p.seq_cnt[b]);
     const int64_t rb = (int64_t)b * P;
-    if (p.walk == DF2_WALK_GREEDY)
-        greedy_seq(p.Sb + rb * K * K, p.cand + rb * K, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+    const float* Sq = p.Sb + rb * K * K;
+    const int32_t* ids = p.cand + rb * K;
+    if constexpr (SAMPLE)
+        chain_seq<kChainSample>(Sq, ids, p.u + rb, p.inv_tau, P, K, p.out_path + rb, p.out_q + rb,
+                                p.out_score + b, sm.wk);
+    else if (p.walk == kWalkGreedy)
+        chain_seq<kChainGreedy>(Sq, ids, nullptr, 0.f, P, K, p.out_path + rb, nullptr, p.out_score + b, sm.wk);
     else
-        walk_seq(p.Sb + rb * K * K, p.cand + rb * K, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+        walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
 // Top-K alone: segments, then the row merge on last arrival.
@@ -379,21 +393,28 @@ __global__ __launch_bounds__(kWG) void k_pairs(PairArgs a) {
 struct WalkArgs {
     const float* S;
     const int32_t* cand;
+    const float* u;       // sampling walk: [B, P] uniforms
     int32_t* out_path;
+    float* out_q;         // sampling walk: [B, P] probabilities
     float* out_score;
     int P, K;
-    int walk;             // df2_walk
+    int walk;             // kWalkViterbi, kWalkGreedy or kWalkSample
+    float inv_tau;
 };
 
 __global__ __launch_bounds__(kWG) void k_walk(WalkArgs a) {
     __shared__ WalkLds sm;
     const int64_t b = blockIdx.x;
-    const float* S = a.S + b * a.P * a.K * a.K;
-    const int32_t* ids = a.cand + b * a.P * a.K;
-    if (a.walk == DF2_WALK_GREEDY)
-        greedy_seq(S, ids, a.P, a.K, a.out_path + b * a.P, a.out_score + b, sm);
+    const int64_t rb = b * a.P;
+    const float* S = a.S + rb * a.K * a.K;
+    const int32_t* ids = a.cand + rb * a.K;
+    if (a.walk == kWalkGreedy)
+        chain_seq<kChainGreedy>(S, ids, nullptr, 0.f, a.P, a.K, a.out_path + rb, nullptr, a.out_score + b, sm);
+    else if (a.walk == kWalkSample)
+        chain_seq<kChainSample>(S, ids, a.u + rb, a.inv_tau, a.P, a.K, a.out_path + rb, a.out_q + rb,
+                                a.out_score + b, sm);
     else
-        walk_seq(S, ids, a.P, a.K, a.out_path + b * a.P, a.out_score + b, sm);
+        walk_seq(S, ids, a.P, a.K, a.out_path + rb, a.out_score + b, sm);
 }
 
 // ----------------------------------------------------------------------------
@@ -488,7 +509,7 @@ int select_capacity() {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void*>(&k_select<true, 4, 4>), kWG, 0) != hipSuccess)
+            &per, reinterpret_cast<const void*>(&k_select<true, 4, 4, false>), kWG, 0) != hipSuccess)
         per = 4;
     const int cap = std::max(1, cus * std::max(1, per));
     std::lock_guard<std::mutex> lock(g_mu);
@@ -637,12 +658,18 @@ void launch_select(const Plan& pl, hipStream_t stream) {
     p2.base = split ? pl.p.n_gate : 0;
     const int64_t n2 = split ? pl.n_chunk_blocks : pl.p.n_gate + pl.n_chunk_blocks;
     dim3 block(kWG);
-#define DF2_SEL(BF, NV_, MB_)                                                                  \
+#define DF2_SEL_W(BF, NV_, MB_, SM)                                                            \
     do {                                                                                       \
         if (split)                                                                             \
-            hipLaunchKernelGGL((k_select<BF, NV_, MB_>), dim3((unsigned)pl.p.n_gate), block, 0, \
-                               stream, p1);                                                    \
-        hipLaunchKernelGGL((k_select<BF, NV_, MB_>), dim3((unsigned)n2), block, 0, stream, p2); \
+            hipLaunchKernelGGL((k_select<BF, NV_, MB_, SM>), dim3((unsigned)pl.p.n_gate), block, \
+                               0, stream, p1);                                                 \
+        hipLaunchKernelGGL((k_select<BF, NV_, MB_, SM>), dim3((unsigned)n2), block, 0, stream,  \
+                           p2);                                                                \
+    } while (0)
+#define DF2_SEL(BF, NV_, MB_)                                     \
+    do {                                                          \
+        if (pl.p.walk == kWalkSample) DF2_SEL_W(BF, NV_, MB_, true); \
+        else DF2_SEL_W(BF, NV_, MB_, false);                      \
     } while (0)
 #define DF2_SEL_NV(BF, MB_)                  \
     switch (pl.nv) {                         \
@@ -657,6 +684,7 @@ void launch_select(const Plan& pl, hipStream_t stream) {
     }
 #undef DF2_SEL_NV
 #undef DF2_SEL
+#undef DF2_SEL_W
 }
 
 void launch_topk(const Plan& pl, hipStream_t stream) {
@@ -709,13 +737,16 @@ const char* dflash2_status_string(df2_status s) {
 
 const char* dflash2_last_error(void) { return g_last_error.c_str(); }
 
-df2_status dflash2_select_walk(const df2_dims* dims, const void* logits, const void* hidden,
-                               const void* A_tab, const void* B_tab, const void* W_H,
-                               const int32_t* prev_tok, int32_t K, df2_walk walk,
-                               int32_t* out_path, float* out_score, hipStream_t stream) {
-    g_last_error.clear();
-    if (walk != DF2_WALK_VITERBI && walk != DF2_WALK_GREEDY)
-        return fail(DF2_EINVAL, "unknown walk mode");
+}  // extern "C"
+
+namespace {
+
+// The fused selector with any walk; the sampling walk also takes u, 1 / tau
+// and out_q (checked by the caller).
+df2_status select_common(const df2_dims* dims, const void* logits, const void* hidden,
+                         const void* A_tab, const void* B_tab, const void* W_H,
+                         const int32_t* prev_tok, int32_t K, int walk, const float* u, float inv_tau,
+                         int32_t* out_path, float* out_q, float* out_score, hipStream_t stream) {
     df2_status st = check_dims(dims, true);
     if (st != DF2_OK) return st;
     if ((st = check_k(K, dims->V)) != DF2_OK) return st;
@@ -750,12 +781,59 @@ df2_status dflash2_select_walk(const df2_dims* dims, const void* logits, const v
     p.out_score = out_score;
     p.B = dims->B;
     p.P = dims->P;
-    p.walk = (int)walk;
+    p.walk = walk;
+    p.u = u;
+    p.out_q = out_q;
+    p.inv_tau = inv_tau;
     void* base = nullptr;
     if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
     note_layout(stream, pl.counter_bytes);
     bind_scratch(pl, base, rows, dims->B);
     return launch_checked([&] { launch_select(pl, stream); }, "dflash2_select launch");
+}
+
+// 1 / tau for the sampling walk, or an error for a temperature that is not
+// positive and finite, or whose reciprocal overflows fp32.
+df2_status sample_inv_tau(float temperature, float* inv_tau) {
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(DF2_EINVAL, "temperature must be positive and finite");
+    const double it = 1.0 / (double)temperature;
+    if (it > 3.0e38) return fail(DF2_EINVAL, "temperature too small (1 / temperature overflows fp32)");
+    *inv_tau = (float)it;
+    return DF2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+df2_status dflash2_select_walk(const df2_dims* dims, const void* logits, const void* hidden,
+                               const void* A_tab, const void* B_tab, const void* W_H,
+                               const int32_t* prev_tok, int32_t K, df2_walk walk,
+                               int32_t* out_path, float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    if (walk != DF2_WALK_VITERBI && walk != DF2_WALK_GREEDY)
+        return fail(DF2_EINVAL, "unknown walk mode");
+    return select_common(dims, logits, hidden, A_tab, B_tab, W_H, prev_tok, K, (int)walk, nullptr,
+                         0.f, out_path, nullptr, out_score, stream);
+}
+
+df2_status dflash2_select_sample(const df2_dims* dims, const void* logits, const void* hidden,
+                                 const void* A_tab, const void* B_tab, const void* W_H,
+                                 const int32_t* prev_tok, int32_t K, float temperature,
+                                 const float* u, int32_t* out_path, float* out_q,
+                                 float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    float inv_tau = 0.f;
+    df2_status st = sample_inv_tau(temperature, &inv_tau);
+    if (st != DF2_OK) return st;
+    if (dims && dims->B > 0) {
+        if (!u || !out_q) return fail(DF2_EINVAL, "NULL pointer argument");
+        if (((uintptr_t)u & 3u) || ((uintptr_t)out_q & 3u))
+            return fail(DF2_EINVAL, "u and out_q must be 4-byte aligned");
+    }
+    return select_common(dims, logits, hidden, A_tab, B_tab, W_H, prev_tok, K, kWalkSample, u,
+                         inv_tau, out_path, out_q, out_score, stream);
 }
 
 df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* hidden,
@@ -873,11 +951,13 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
     }, "dflash2_pair_scores launch");
 }
 
-df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B, int32_t P, int32_t K,
-                        df2_walk walk, int32_t* out_path, float* out_score, hipStream_t stream) {
-    g_last_error.clear();
-    if (walk != DF2_WALK_VITERBI && walk != DF2_WALK_GREEDY)
-        return fail(DF2_EINVAL, "unknown walk mode");
+}  // extern "C"
+
+namespace {
+
+df2_status walk_common(const float* S, const int32_t* cand_idx, int32_t B, int32_t P, int32_t K,
+                       int walk, const float* u, float inv_tau, int32_t* out_path, float* out_q,
+                       float* out_score, hipStream_t stream) {
     if (B < 0) return fail(DF2_EINVAL, "B < 0");
     if (P < 1 || P > kMaxP) return fail(DF2_EINVAL, "P must be in [1, 64]");
     if (K < 1 || K > kMaxK) return fail(DF2_EINVAL, "K must be in [1, 64]");
@@ -893,10 +973,42 @@ df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B, int3
     a.out_score = out_score;
     a.P = P;
     a.K = K;
-    a.walk = (int)walk;
+    a.walk = walk;
+    a.u = u;
+    a.out_q = out_q;
+    a.inv_tau = inv_tau;
     dim3 grid((unsigned)B), block(kWG);
     return launch_checked([&] { hipLaunchKernelGGL(k_walk, grid, block, 0, stream, a); },
                           "dflash2_walk launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B, int32_t P, int32_t K,
+                        df2_walk walk, int32_t* out_path, float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    if (walk != DF2_WALK_VITERBI && walk != DF2_WALK_GREEDY)
+        return fail(DF2_EINVAL, "unknown walk mode");
+    return walk_common(S, cand_idx, B, P, K, (int)walk, nullptr, 0.f, out_path, nullptr, out_score,
+                       stream);
+}
+
+df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx, const float* u, int32_t B,
+                               int32_t P, int32_t K, float temperature, int32_t* out_path,
+                               float* out_q, float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    float inv_tau = 0.f;
+    df2_status st = sample_inv_tau(temperature, &inv_tau);
+    if (st != DF2_OK) return st;
+    if (B > 0) {
+        if (!u || !out_q) return fail(DF2_EINVAL, "NULL pointer argument");
+        if (((uintptr_t)u & 3u) || ((uintptr_t)out_q & 3u))
+            return fail(DF2_EINVAL, "u and out_q must be 4-byte aligned");
+    }
+    return walk_common(S, cand_idx, B, P, K, kWalkSample, u, inv_tau, out_path, out_q, out_score,
+                       stream);
 }
 
 df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,

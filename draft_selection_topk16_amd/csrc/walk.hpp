@@ -14,11 +14,12 @@
 // transposed (column j contiguous, padded to Kp = K rounded up to 16, 32 or
 // 64), a group of positions at a time.
 //
-// The same section also describes the walk literally as greedy: from the
+// The same section also describes the walk literally as greedy (from the
 // last verified token, each position takes the best successor of the token
-// chosen one step earlier.  greedy_seq does that: every thread of the
-// workgroup finds the best successor of one (position, predecessor) pair at
-// once, and the chain through those choices is then a few register reads.
+// chosen one step earlier) and as sampling from the same scores.  chain_seq
+// does both: every thread of the workgroup decides the successor of one
+// (position, predecessor) row at once, and the chain through those choices
+// is then a few register reads.
 #pragma once
 
 #include <math.h>
@@ -36,6 +37,7 @@ struct WalkLds {
     uint8_t psi[kMaxP * kMaxK];
     int32_t ids[kWalkIds];
     int32_t rank[kMaxP];
+    float qpick[kMaxP];             // sampling walk: probability of each choice
 };
 
 // Best of one lane's values v[0..16) (predecessors i0 .. i0 + 15): the
@@ -195,83 +197,216 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
     }
 }
 
-// The greedy walk of one sequence; arguments, outputs and tie rule as for
-// walk_seq:
-//     j_0 = argmax_j S_0(0, j),  j_t = argmax_j S_t(j_{t-1}, j),
-//     score = S_0(0, j_0) + S_1(j_0, j_1) + ... in fp32, in order of t.
-// Step 1, every thread: for each row (t, i) it owns, the best successor
-// nx(t, i) and its score; both go to LDS (sm.psi, sm.ST as [P, K]).
-// Step 2, wave 0: lane i holds nx(t, i) and its score for a few positions
-// at a time, and the chain j_t = nx(t, j_{t-1}) runs through readlane.
-// Every thread of the workgroup calls.
-__device__ __forceinline__ void greedy_seq(const float* __restrict__ S, const int32_t* __restrict__ ids,
-                                           int P, int K, int32_t* __restrict__ out_path,
-                                           float* __restrict__ out_score, WalkLds& sm) {
+// Walks whose choice at t depends only on the row of the token chosen at
+// t - 1 ("chain" walks: greedy and sampling).  Each row (t, i) has its own
+// successor nx(t, i), so all rows are decided at once and the walk is the
+// chain j_t = nx(t, j_{t-1}) from row 0 at t = 0.
+enum ChainRule { kChainGreedy = 0, kChainSample = 1 };
+
+constexpr int kChainRows = kWalkS / 2;  // rows (t, i) decided per group of positions
+
+// Greedy rule: the first maximiser of the row and its score.
+__device__ __forceinline__ void row_best(const float* __restrict__ row, int K, int& arg, float& best) {
+    best = -INFINITY;
+    arg = 0;
+    for (int c = 0; c < K; c += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = xload(row + min(c + u, K - 1));
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            // strictly greater: the lower rank keeps a tie
+            if (c + u < K && (c + u == 0 || v[u] > best)) {
+                best = v[u];
+                arg = c + u;
+            }
+        }
+    }
+}
+
+// Sampling rule (section "A Lightweight Path Selector": sampling draws from
+// the same scores): e_j = exp((s_j - max s) / tau), z = e_0 + ... + e_{K-1}
+// summed in rank order, and the draw is the first j whose running sum
+// exceeds uu * z (the running sum ends exactly at z: the same additions of
+// the same values in the same order); if rounding leaves none, the last j
+// with e_j > 0.
+// Outputs the rank, its score and its probability e_j / z.
+__device__ __forceinline__ void row_draw(const float* __restrict__ row, int K, float uu, float inv_tau,
+                                         int& arg, float& val, float& q) {
+    int pick = -1, last = 0;
+    float vp = 0.f, ep = 0.f, vl = 0.f, el = 0.f, z = 0.f;
+    if (K <= 16) {
+        float v[16], e[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = xload(row + min(u, K - 1));
+        float m = v[0];
+#pragma unroll
+        for (int u = 1; u < 16; ++u) m = (u < K) ? fmaxf(m, v[u]) : m;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            e[u] = (u < K) ? expf((v[u] - m) * inv_tau) : 0.f;
+            z += e[u];
+        }
+        const float target = uu * z;
+        float c = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            c += e[u];
+            if (e[u] > 0.f) {
+                last = u;
+                vl = v[u];
+                el = e[u];
+            }
+            if (pick < 0 && target < c) {
+                pick = u;
+                vp = v[u];
+                ep = e[u];
+            }
+        }
+    } else {
+        // three passes over the row, reloading 16 values at a time
+        float m = -INFINITY;
+        for (int c0 = 0; c0 < K; c0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = xload(row + min(c0 + u, K - 1));
+#pragma unroll
+            for (int u = 0; u < 16; ++u) m = (c0 + u < K) ? fmaxf(m, v[u]) : m;
+        }
+        for (int c0 = 0; c0 < K; c0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = xload(row + min(c0 + u, K - 1));
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (c0 + u < K) z += expf((v[u] - m) * inv_tau);
+        }
+        const float target = uu * z;
+        float c = 0.f;
+        for (int c0 = 0; c0 < K; c0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = xload(row + min(c0 + u, K - 1));
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (c0 + u < K) {
+                    const float e = expf((v[u] - m) * inv_tau);
+                    c += e;
+                    if (e > 0.f) {
+                        last = c0 + u;
+                        vl = v[u];
+                        el = e;
+                    }
+                    if (pick < 0 && target < c) {
+                        pick = c0 + u;
+                        vp = v[u];
+                        ep = e;
+                    }
+                }
+            }
+        }
+    }
+    if (pick < 0) {
+        pick = last;
+        vp = vl;
+        ep = el;
+    }
+    arg = pick;
+    val = vp;
+    q = ep / z;
+}
+
+// A chain walk of one sequence.  S: [P, K, K] scores (row 0 used at t = 0),
+// ids: [P, K] candidate ids, both read with xload; u: [P] uniforms (sampling
+// only; values outside [0, 1) are clamped into it, NaN to 0).  Writes
+// out_path[0 .. P), *out_score (the chosen scores summed in order of t, fp32)
+// and, when sampling, out_q[0 .. P) (each choice's probability).
+// Step 1, every thread: for each row (t, i) it owns, nx(t, i), its score and
+// (sampling) its probability go to LDS.  Step 2, wave 0: lane i holds them
+// for eight positions at a time and the chain runs through readlane.
+// Positions are taken in groups of kChainRows / K.  Every thread calls.
+template <int RULE>
+__device__ __forceinline__ void chain_seq(const float* __restrict__ S, const int32_t* __restrict__ ids,
+                                          const float* __restrict__ u, float inv_tau, int P, int K,
+                                          int32_t* __restrict__ out_path, float* __restrict__ out_q,
+                                          float* __restrict__ out_score, WalkLds& sm) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int PK = P * K;
     const bool ids_lds = PK <= kWalkIds;
     constexpr int QI = kWalkIds / kWG;
-    int32_t idv[QI];
+    float* val = sm.ST;
+    float* prob = sm.ST + kChainRows;
+    const int GT = kChainRows / K;      // K <= 64, so at least 32 positions a group
+    int j = 0;
+    float score = 0.f;
+    for (int t0 = 0; t0 < P; t0 += GT) {
+        const int t1 = min(P, t0 + GT);
+        const int n = (t1 - t0) * K;
+        const bool load_ids = t0 == 0 && ids_lds;
+        int32_t idv[QI];
 #pragma unroll
-    for (int q = 0; q < QI; ++q) idv[q] = ids_lds ? xload(ids + min(q * kWG + tid, PK - 1)) : 0;
-    for (int e = tid; e < PK; e += kWG) {
-        // row (t, i) = (e / K, e % K) starts at S + e * K
-        const float* row = S + (int64_t)e * K;
-        float best = -INFINITY;
-        int arg = 0;
-        for (int c = 0; c < K; c += 16) {
-            float v[16];
+        for (int q = 0; q < QI; ++q) idv[q] = load_ids ? xload(ids + min(q * kWG + tid, PK - 1)) : 0;
+        for (int e = tid; e < n; e += kWG) {
+            // row (t, i) = (t0 + e / K, e % K) starts at S + (t0 * K + e) * K
+            const float* row = S + ((int64_t)t0 * K + e) * K;
+            int arg;
+            float best;
+            if constexpr (RULE == kChainSample) {
+                float uu = u[t0 + e / K];
+                uu = (uu >= 0.f) ? fminf(uu, 0x1.fffffep-1f) : 0.f;
+                float q;
+                row_draw(row, K, uu, inv_tau, arg, best, q);
+                prob[e] = q;
+            } else {
+                row_best(row, K, arg, best);
+            }
+            sm.psi[e] = (uint8_t)arg;
+            val[e] = best;
+        }
+        if (load_ids) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = xload(row + min(c + u, K - 1));
+            for (int q = 0; q < QI; ++q)
+                if (q * kWG + tid < PK) sm.ids[q * kWG + tid] = idv[q];
+        }
+        __syncthreads();
+        if (w == 0) {
+            // eight positions at a time: their LDS reads go out together, then
+            // the chain runs through readlane (more at once costs registers)
+            constexpr int G = 8;
+            const int li = min(lane, K - 1);
+#pragma unroll 1
+            for (int ta = t0; ta < t1; ta += G) {
+                int nx[G];
+                float sv[G], qv[G];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                // strictly greater: the lower rank keeps a tie
-                if (c + u < K && (c + u == 0 || v[u] > best)) {
-                    best = v[u];
-                    arg = c + u;
+                for (int x = 0; x < G; ++x) {
+                    const int e = (min(ta + x, t1 - 1) - t0) * K + li;
+                    nx[x] = sm.psi[e];
+                    sv[x] = val[e];
+                    qv[x] = (RULE == kChainSample) ? prob[e] : 0.f;
+                }
+#pragma unroll
+                for (int x = 0; x < G; ++x) {
+                    if (ta + x < t1) {
+                        score += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv[x]), j));
+                        if constexpr (RULE == kChainSample) {
+                            const float qs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv[x]), j));
+                            if (lane == 0) sm.qpick[ta + x] = qs;
+                        }
+                        j = __builtin_amdgcn_readlane(nx[x], j);
+                        if (lane == 0) sm.rank[ta + x] = j;
+                    }
                 }
             }
         }
-        sm.psi[e] = (uint8_t)arg;
-        sm.ST[e] = best;
+        __syncthreads();
     }
-    if (ids_lds) {
-#pragma unroll
-        for (int q = 0; q < QI; ++q)
-            if (q * kWG + tid < PK) sm.ids[q * kWG + tid] = idv[q];
-    }
-    __syncthreads();
     if (w != 0) return;
-    // eight positions at a time: their LDS reads go out together, then the
-    // chain runs through readlane (more at once costs registers elsewhere)
-    constexpr int G = 8;
-    const int li = min(lane, K - 1);
-    int j = 0;
-    float score = 0.f;
-#pragma unroll 1
-    for (int t0 = 0; t0 < P; t0 += G) {
-        int nx[G];
-        float sv[G];
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            const int e = min(t0 + u, P - 1) * K + li;
-            nx[u] = sm.psi[e];
-            sv[u] = sm.ST[e];
-        }
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            if (t0 + u < P) {
-                score += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv[u]), j));
-                j = __builtin_amdgcn_readlane(nx[u], j);
-                if (lane == 0) sm.rank[t0 + u] = j;
-            }
-        }
-    }
     if (lane == 0) *out_score = score;
-    wave_sync();
     for (int t = lane; t < P; t += 64) {
         const int rk = sm.rank[t];
         out_path[t] = ids_lds ? sm.ids[t * K + rk] : xload(ids + (int64_t)t * K + rk);
+        if constexpr (RULE == kChainSample) out_q[t] = sm.qpick[t];
     }
 }
 

@@ -13,7 +13,8 @@
  * one walk over the precomputed scores, starting from the last verified
  * token.  This library reads H as a bias-free linear map d -> r,
  * H_t = W_H h_t, and the walk as a max-sum (Viterbi) pass with backtrack;
- * the section's literal greedy walk is available as a second walk mode.
+ * the section's literal greedy walk is available as a second walk mode, and
+ * its sampling walk through dflash2_select_sample / dflash2_sample_walk.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -123,6 +124,34 @@ df2_status dflash2_select_walk(const df2_dims* dims, const void* logits,
                                float* out_score, hipStream_t stream);
 
 /*
+ * dflash2_select with the sampling walk (same section: sampling draws from
+ * the same scores).  From the last verified token, position t draws its
+ * candidate from the softmax of the pair scores of the token chosen at
+ * t - 1 (row 0 at t = 0), at the given temperature:
+ *     q_t(j) = exp((S_t(i, j) - max_k S_t(i, k)) / temperature) / (sum over k)
+ *     j_t    = the first j whose running sum q_t(0) + ... + q_t(j) exceeds
+ *              u[b][t] (running sums in rank order; the last j with
+ *              q_t(j) > 0 if rounding leaves none).
+ *   temperature  > 0 and finite, 1 / temperature finite in fp32 (else DF2_EINVAL)
+ *   u         [B, P] float  caller's uniforms in [0, 1) (values outside are
+ *                           clamped into it, NaN to 0); the library draws
+ *                           no random numbers itself
+ *   out_path  [B, P] int32  drawn token at each position
+ *   out_q     [B, P] float  q_t(j_t): the draft probability of each drawn
+ *                           token, for rejection sampling against the target
+ *   out_score [B] float     sum_t S_t(j_{t-1}, j_t), added in order of t
+ * Other arguments as for dflash2_select; u and out_q 4-byte aligned.
+ * Arithmetic: fp32 (expf); scores must be finite.
+ */
+df2_status dflash2_select_sample(const df2_dims* dims, const void* logits,
+                                 const void* hidden, const void* A_tab,
+                                 const void* B_tab, const void* W_H,
+                                 const int32_t* prev_tok, int32_t K,
+                                 float temperature, const float* u,
+                                 int32_t* out_path, float* out_q,
+                                 float* out_score, hipStream_t stream);
+
+/*
  * Top-K of each row ("keep the top 16 candidates at each position").
  *   logits  [rows, V] (dtype)
  *   out_idx [rows, K] int32  candidate token ids, best first
@@ -179,6 +208,18 @@ df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B,
 df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B,
                         int32_t P, int32_t K, df2_walk walk, int32_t* out_path,
                         float* out_score, hipStream_t stream);
+
+/*
+ * The sampling walk alone (see dflash2_select_sample) over given scores.
+ *   S [B, P, K, K] float, cand_idx [B, P, K] int32, as for dflash2_walk;
+ *   u [B, P] float uniforms, temperature, out_path [B, P] int32,
+ *   out_q [B, P] float, out_score [B] float.
+ */
+df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx,
+                               const float* u, int32_t B, int32_t P, int32_t K,
+                               float temperature, int32_t* out_path,
+                               float* out_q, float* out_score,
+                               hipStream_t stream);
 
 /*
  * Waits for `stream`, then reports and clears the device-side flags of its

@@ -10,7 +10,13 @@ path must be within the tolerance of the best score.  For the greedy walk the
 rule applies per step: following the GPU's own choices, each step's choice
 must be the oracle's best successor of the same predecessor, or within the
 tolerance of it; the GPU score is checked against the oracle's score of the
-GPU path.
+GPU path.  For the sampling walk, following the GPU's choices, each step's
+uniform must fall in the oracle's CDF interval of the GPU's choice, widened
+by the slack that the score error allows: scores off by at most e move each
+probability by a factor within exp(+-2e / tau), so every cumulative sum by at
+most expm1(2e / tau); the GPU's probability of its choice gets the same bound.
+e = rel * (largest sigma of the row); rel = 1e-5 for fp32 inputs, 1e-4 for
+bf16 inputs (the pair scores' relative error is near 2^-16 of sigma there).
 """
 from __future__ import annotations
 
@@ -23,6 +29,7 @@ import oracle
 from draft_selection_topk16_amd import synth
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL_SAMPLE = {"f32": 1e-5, "bf16": 1e-4}
 
 
 def say(*a):
@@ -141,4 +148,45 @@ def check_greedy(path, score, o, tol, label=""):
             label, b, score[b], own, err)
     say("  %s: %d sequences, %d tolerated greedy path mismatches, worst score rel err %.3g"
         % (label, path.shape[0], mism, worst))
+    return mism
+
+
+def check_sample(path, q, score, o, rel, label=""):
+    """Acceptance rule for the sampling walk; returns the number of
+    sequences whose path differs from the oracle's draw."""
+    path = np.asarray(path)
+    q = np.asarray(q, dtype=np.float64)
+    score = np.asarray(score, dtype=np.float64)
+    S, sig, u, tau = o["S"], o["sigma"], o["u"], o["tau"]
+    mism = 0
+    worst_q = 0.0
+    worst_s = 0.0
+    for b in range(path.shape[0]):
+        ranks = path_ranks(o, b, path[b])
+        mism += 0 if np.array_equal(path[b], o["sample_path"][b]) else 1
+        i = 0
+        own = 0.0
+        own_sig = 0.0
+        for t, j in enumerate(ranks):
+            row, srow = S[b, t, i], sig[b, t, i]
+            e = np.exp((row - row.max()) / tau)
+            qr = e / e.sum()
+            cdf = np.cumsum(qr)
+            slack = np.expm1(2.0 * rel * srow.max() / tau) + 1e-6
+            lo = cdf[j - 1] if j > 0 else 0.0
+            assert lo - slack <= u[b, t] < cdf[j] + slack, (
+                "%s seq %d t=%d: u=%.9g drew rank %d, whose interval is [%.9g, %.9g)"
+                % (label, b, t, u[b, t], j, lo, cdf[j]))
+            dq = abs(q[b, t] - qr[j])
+            assert dq <= qr[j] * slack + 1e-7, (label, b, t, q[b, t], qr[j])
+            worst_q = max(worst_q, dq / max(qr[j], 1e-30))
+            own += row[j]
+            own_sig += srow[j]
+            i = j
+        err = abs(score[b] - own) / max(abs(own), own_sig)
+        worst_s = max(worst_s, err)
+        assert err <= rel * 10, "%s seq %d: score %.9g vs oracle %.9g (rel %.3g)" % (
+            label, b, score[b], own, err)
+    say("  %s: %d sequences, %d tolerated draw mismatches, worst q rel err %.3g, worst score rel err %.3g"
+        % (label, path.shape[0], mism, worst_q, worst_s))
     return mism

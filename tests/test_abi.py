@@ -128,6 +128,24 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     assert lib.dflash2_select_walk(ctypes.byref(dsel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2,
                                    FAKE, FAKE, None) == DF2_EINVAL
     assert b"walk" in lib.dflash2_last_error()
+    # sampling walk: temperature, uniforms and out_q are checked on the host
+    for tau in (0.0, -1.0, float("inf"), float("nan"), 1e-39):
+        assert lib.dflash2_sample_walk(FAKE, FAKE, FAKE, 2, 3, 4, tau, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+        assert b"temperature" in lib.dflash2_last_error()
+        assert lib.dflash2_select_sample(ctypes.byref(dsel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                         tau, FAKE, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_sample_walk(FAKE, FAKE, None, 2, 3, 4, 1.0, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_sample_walk(FAKE, FAKE, FAKE, 2, 3, 4, 1.0, FAKE, None, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_sample_walk(FAKE, FAKE, FAKE + 2, 2, 3, 4, 1.0, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_sample_walk(FAKE, FAKE, FAKE, 2, 0, 4, 1.0, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_sample_walk(FAKE, FAKE, FAKE, 2, 3, 65, 1.0, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_sample_walk(FAKE, FAKE, FAKE, 0, 3, 4, 1.0, FAKE, FAKE, FAKE, None) == DF2_OK
+    assert lib.dflash2_select_sample(ctypes.byref(dsel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 1.0,
+                                     None, FAKE, FAKE, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_select_sample(ctypes.byref(dsel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 1.0,
+                                     FAKE, FAKE, FAKE + 1, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_select_sample(ctypes.byref(dsel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1.0,
+                                     FAKE, FAKE, FAKE, FAKE, None) == DF2_EINVAL
     d = Dims(2, 3, 100, 32, 64, 1)
     assert lib.dflash2_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 4,
                                    FAKE, None) == DF2_EINVAL

@@ -12,8 +12,8 @@ import torch
 import oracle
 import draft_selection_topk16_amd as df2
 from draft_selection_topk16_amd import synth
-from gpu_util import (TOL, check_greedy, check_scores, check_select, dev_tensor, run_oracle, say,
-                      to_device)
+from gpu_util import (TOL, TOL_SAMPLE, check_greedy, check_sample, check_scores, check_select,
+                      dev_tensor, run_oracle, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -467,3 +467,144 @@ def test_greedy_stages_compose_to_select():
                         walk="greedy")
     assert torch.equal(p1, p2)
     assert torch.allclose(s1, s2, rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------- sampling walk
+def uniforms(B, P, seed):
+    return np.random.default_rng(seed).random((B, P))
+
+
+def f32_uniforms(u):
+    """The uniforms as the GPU sees them (fp32), widened back for the oracle."""
+    return u.astype(np.float32)
+
+
+@pytest.mark.parametrize("K,P,tau", [(16, 7, 1.0), (32, 15, 0.7), (5, 3, 2.0), (1, 4, 1.0), (64, 2, 1.0),
+                                     (16, 64, 1.0), (64, 64, 1.5), (3, 17, 0.3)])
+def test_sample_stage(K, P, tau):
+    say("sample walk K=%d P=%d tau=%g" % (K, P, tau))
+    rng = np.random.default_rng(K * 100 + P + 11)
+    B = 9
+    S = (rng.standard_normal((B, P, K, K)) * 2).astype(np.float32)
+    S[:, 0, 1:, :] = S[:, 0, :1, :]
+    cand = rng.integers(0, 1 << 20, size=(B, P, K)).astype(np.int32)
+    u = f32_uniforms(uniforms(B, P, K + P))
+    path, q, score = df2.sample_walk(torch.from_numpy(S).cuda(), torch.from_numpy(cand).cuda(),
+                                     torch.from_numpy(u).cuda(), tau)
+    Sd = S.astype(np.float64)
+    pr, pt, qr, sc = oracle.sample(Sd, cand, u.astype(np.float64), tau)
+    o = dict(cand=cand, S=Sd, sigma=np.abs(Sd), u=u.astype(np.float64), tau=tau, sample_path=pt)
+    mism = check_sample(path.cpu().numpy(), q.cpu().numpy(), score.cpu().numpy(), o, 1e-6, "stage")
+    assert mism <= 1
+
+
+def test_sample_stage_closed_forms():
+    """u = 0 draws rank 0 at every step; a huge temperature draws rank
+    floor(u K) with probability 1/K; K = 1 draws the only candidate with
+    probability 1."""
+    say("sample walk closed forms")
+    rng = np.random.default_rng(12)
+    B, P, K = 6, 9, 8
+    S = torch.from_numpy(rng.standard_normal((B, P, K, K)).astype(np.float32)).cuda()
+    cand = torch.from_numpy(np.tile(np.arange(K, dtype=np.int32), (B, P, 1)) + 100).cuda()
+    path, q, _ = df2.sample_walk(S, cand, torch.zeros((B, P), dtype=torch.float32, device="cuda"), 1.0)
+    assert torch.all(path == 100)
+    u = (rng.integers(0, K, size=(B, P)) + rng.uniform(0.05, 0.95, size=(B, P))) / K
+    path, q, _ = df2.sample_walk(S, cand, torch.from_numpy(u.astype(np.float32)).cuda(), 1e30)
+    assert np.array_equal(path.cpu().numpy() - 100, np.floor(u * K).astype(np.int32))
+    assert torch.allclose(q, torch.full_like(q, 1.0 / K), rtol=1e-6)
+    S1 = S[:, :, :1, :1].contiguous()
+    path, q, score = df2.sample_walk(S1, cand[:, :, :1].contiguous(),
+                                     torch.from_numpy(rng.random((B, P)).astype(np.float32)).cuda(), 1.0)
+    assert torch.all(path == 100) and torch.all(q == 1.0)
+
+
+def gpu_select_sample(x, u, tau):
+    t = to_device(x)
+    path, q, score = df2.select_sample(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"],
+                                       x.wl.K, torch.from_numpy(u).cuda(), tau)
+    torch.cuda.synchronize()
+    return path.cpu().numpy(), q.cpu().numpy(), score.cpu().numpy()
+
+
+def oracle_sample(x, u, tau, seqs=None):
+    f = x.f64()
+    return oracle.select(f["logits"], f["hidden"], f["A"], f["Bt"], f["W"], f["prev"], x.wl.K,
+                         seqs=seqs, u=u.astype(np.float64), tau=tau)
+
+
+@pytest.mark.parametrize("name,tau", [("tiny_f32", 1.0), ("qwen3_4b_b1", 1.0), ("t27b_b32", 1.0),
+                                      ("t27b_b32", 0.5), ("stress_b256", 1.0)])
+def test_select_sample_workloads(name, tau):
+    x = inputs(name)
+    say("select sample %s tau=%g B=%d P=%d V=%d K=%d" % (name, tau, x.wl.B, x.wl.P, x.wl.V, x.wl.K))
+    u = f32_uniforms(uniforms(x.wl.B, x.wl.P, 99))
+    path, q, score = gpu_select_sample(x, u, tau)
+    seqs = STRESS_SEQS if name == "stress_b256" else None
+    o = oracle_sample(x, u, tau, seqs)
+    if seqs is not None:
+        path, q, score = path[seqs], q[seqs], score[seqs]
+    check_sample(path, q, score, o, TOL_SAMPLE[x.wl.dtype], name)
+    assert flags_clear()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {"pair_scale": 8.0, "V": 4000}),
+    ("t27b_b8", {"pair_scale": 8.0, "V": 30000, "d": 512}),
+])
+def test_select_sample_pair_dominant(name, kw):
+    x = inputs(name, **kw)
+    say("select sample pair-dominant %s %s" % (name, kw))
+    u = f32_uniforms(uniforms(x.wl.B, x.wl.P, 7))
+    path, q, score = gpu_select_sample(x, u, 1.0)
+    check_sample(path, q, score, oracle_sample(x, u, 1.0), TOL_SAMPLE[x.wl.dtype], name)
+
+
+@pytest.mark.parametrize("B,P,V,K,d", [(1, 1, 5000, 16, 64), (3, 64, 3000, 16, 64),
+                                       (2, 5, 64, 64, 64), (2, 4, 300, 1, 64),
+                                       (4, 7, 9999, 3, 96), (33, 7, 2048, 16, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_sample_edge_shapes(B, P, V, K, d, dtype):
+    say("select sample edge %s B=%d P=%d V=%d K=%d d=%d" % (dtype, B, P, V, K, d))
+    wl = synth.Workload("edge", 1, B=B, P=P, V=V, d=d, K=K, r=64, dtype=dtype, pair_scale=4.0)
+    x = synth.make_inputs(wl, seed=B * 1000 + P * 10 + K + 9)
+    u = f32_uniforms(uniforms(B, P, B + P + K))
+    path, q, score = gpu_select_sample(x, u, 1.0)
+    check_sample(path, q, score, oracle_sample(x, u, 1.0), TOL_SAMPLE[dtype], "sample edge")
+
+
+def test_sample_stages_compose_to_select():
+    """topk -> project -> pair_scores -> sample_walk gives the fused draw bit for bit."""
+    x = inputs("qwen3_4b_b1")
+    say("sample stages compose")
+    t = to_device(x)
+    u = torch.from_numpy(f32_uniforms(uniforms(x.wl.B, x.wl.P, 5))).cuda()
+    idx, val = df2.topk(t["logits"], 16)
+    H = df2.project(t["hidden"], t["W"])
+    S = df2.pair_scores(idx, val, H, t["A"], t["Bt"], t["prev"])
+    p1, q1, s1 = df2.sample_walk(S, idx, u, 0.8)
+    p2, q2, s2 = df2.select_sample(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], 16,
+                                   u, 0.8)
+    assert torch.equal(p1, p2)
+    assert torch.allclose(q1, q2, rtol=1e-6, atol=0)
+    assert torch.allclose(s1, s2, rtol=1e-6, atol=1e-6)
+
+
+def test_sample_draw_frequencies_follow_q():
+    """Many draws over one score table (one uniform grid per step): the share
+    of draws of each candidate at t = 0 follows the oracle's q within 1/N."""
+    say("sample draw frequencies")
+    rng = np.random.default_rng(31)
+    N, P, K = 4096, 2, 16
+    S1 = (rng.standard_normal((1, P, K, K)) * 1.5).astype(np.float32)
+    S1[:, 0, 1:, :] = S1[:, 0, :1, :]
+    S = np.repeat(S1, N, axis=0)
+    cand = np.tile(np.arange(K, dtype=np.int32), (N, P, 1))
+    u = np.stack([(np.arange(N) + 0.5) / N, rng.random(N)], axis=1).astype(np.float32)
+    path, q, _ = df2.sample_walk(torch.from_numpy(S).cuda(), torch.from_numpy(cand).cuda(),
+                                 torch.from_numpy(u).cuda(), 1.0)
+    counts = np.bincount(path.cpu().numpy()[:, 0], minlength=K)
+    row = S1[0, 0, 0].astype(np.float64)
+    e = np.exp(row - row.max())
+    qr = e / e.sum()
+    assert np.all(np.abs(counts - N * qr) <= 2.0), (counts, N * qr)
