@@ -8,7 +8,9 @@ The steps follow "DFlash 2: Keep Drafting Parallel", section "A Lightweight
 Path Selector" (top-16 candidates, the pair-score equation, one walk from the
 last verified token); the walk is read as max-sum Viterbi with backtrack, the
 literal greedy walk and the sampling walk are further modes, and H(h_t) is
-read as a bias-free linear map d -> r (see the header of oracle.c).
+read as a bias-free linear map d -> r (see the header of oracle.c).  conv2 is
+the drafter's two-tap dynamic convolution ("A Lightweight Local
+Convolution").
 
 Every function here is pinned by CPU tests against something other than
 itself (brute-force enumeration, closed forms, exact integer cases, an
@@ -60,6 +62,8 @@ def _load():
         lib.orc_greedy.restype = None
         lib.orc_sample.argtypes = [P, P, P, I, I, I, ctypes.c_double, P, P, P, P]
         lib.orc_sample.restype = ctypes.c_int
+        lib.orc_conv2.argtypes = [P, P, P, P, I, I, I, P, P]
+        lib.orc_conv2.restype = None
         lib.orc_second_best.argtypes = [P, P, I, I, I, P]
         lib.orc_second_best.restype = ctypes.c_int
         _lib = lib
@@ -163,6 +167,22 @@ def sample(S, cand, u, tau: float):
                           _p(sc)) != 0:
         raise MemoryError("orc_sample")
     return pr, pt, q, sc
+
+
+def conv2(x, x_prev, base, Wc):
+    """Two-tap dynamic depthwise convolution (see orc_conv2):
+    x [B,P,d], x_prev [B,d], base [2,d], Wc [2,d/16,d] -> (y, sigma) [B,P,d]."""
+    x = _f64(x)
+    x_prev = _f64(x_prev)
+    base = _f64(base)
+    Wc = _f64(Wc)
+    Bn, P, d = x.shape
+    if d % 16 or x_prev.shape != (Bn, d) or base.shape != (2, d) or Wc.shape != (2, d // 16, d):
+        raise ValueError("conv2: inconsistent shapes")
+    y = np.empty_like(x)
+    sig = np.empty_like(x)
+    _load().orc_conv2(_p(x), _p(x_prev), _p(base), _p(Wc), Bn, P, d, _p(y), _p(sig))
+    return y, sig
 
 
 def path_sigma(sig, path_rank) -> np.ndarray:

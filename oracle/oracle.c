@@ -33,6 +33,9 @@
  *     to the smaller rank.
  *   - U_t(b) is the raw logit.
  *
+ * The drafter's two-tap convolution (orc_conv2, section "A Lightweight Local
+ * Convolution") is here too; its readings are stated beside it.
+ *
  * Parity pins (checked by the CPU test suite, not by this file): brute-force
  * enumeration of all K^P paths on tiny inputs, zeroed pair term reducing to
  * independent top-1 picks, K = 1 and P = 1 closed forms, exact integer
@@ -341,4 +344,52 @@ int orc_second_best(const double* S, const int32_t* path_rank, int64_t Bn,
     free(alpha);
     free(beta);
     return 0;
+}
+
+/*
+ * Two-tap dynamic depthwise convolution ("DFlash 2: Keep Drafting Parallel",
+ * section "A Lightweight Local Convolution", the equation for Conv_k):
+ *   y_t[c] = k_{t,0}[c] * x_t[c] + k_{t,1}[c] * x_{t-1}[c]
+ * with x_{-1} = x_prev (the last verified token's representation) and each
+ * coefficient a learned base plus a correction from the current hidden state
+ * shared by 16 consecutive channels.  Readings: the correction is a bias-free
+ * linear map of x_t,
+ *   corr_t[tap][g] = sum_m Wc[tap][g][m] * x_t[m],   g = 0 .. d/16 - 1,
+ *   k_{t,tap}[c]   = base[tap][c] + corr_t[tap][c / 16].
+ * x [Bn, P, d], x_prev [Bn, d], base [2, d], Wc [2, d/16, d], y [Bn, P, d];
+ * sigma [Bn, P, d] gets the magnitude
+ *   (|base0| + sum |Wc0 x|) |x_t| + (|base1| + sum |Wc1 x|) |x_{t-1}|
+ * that scales the rounding error of any evaluation order.
+ * d must be a multiple of 16.
+ */
+void orc_conv2(const double* x, const double* x_prev, const double* base, const double* Wc,
+               int64_t Bn, int64_t P, int64_t d, double* y, double* sigma) {
+    const int64_t G = d / 16;
+    for (int64_t b = 0; b < Bn; ++b)
+        for (int64_t t = 0; t < P; ++t) {
+            const double* xt = x + (b * P + t) * d;
+            const double* xp = (t == 0) ? x_prev + b * d : x + (b * P + t - 1) * d;
+            double* yt = y + (b * P + t) * d;
+            double* st = sigma + (b * P + t) * d;
+            for (int64_t g = 0; g < G; ++g) {
+                double corr[2], cmag[2];
+                for (int tap = 0; tap < 2; ++tap) {
+                    const double* w = Wc + ((int64_t)tap * G + g) * d;
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t m = 0; m < d; ++m) {
+                        acc += w[m] * xt[m];
+                        mag += fabs(w[m] * xt[m]);
+                    }
+                    corr[tap] = acc;
+                    cmag[tap] = mag;
+                }
+                for (int64_t c = 16 * g; c < 16 * g + 16; ++c) {
+                    const double k0 = base[c] + corr[0];
+                    const double k1 = base[d + c] + corr[1];
+                    yt[c] = k0 * xt[c] + k1 * xp[c];
+                    st[c] = (fabs(base[c]) + cmag[0]) * fabs(xt[c]) +
+                            (fabs(base[d + c]) + cmag[1]) * fabs(xp[c]);
+                }
+            }
+        }
 }
