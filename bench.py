@@ -21,6 +21,9 @@ Prints ONE JSON line:
               workload and on its pair-dominant variant);
   sample      the same workloads with the sampling walk (temperature 1,
               seeded uniforms resident on the device);
+  conv        the drafter's two-tap dynamic convolution (dflash2_conv2) at
+              the two drafter shapes: µs per call (HIP events) and % of HBM
+              peak for its algorithmic bytes, input copies rotated;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -163,6 +166,50 @@ def _time_calls(calls, nsets: int, steps: int, warmup: int, stream):
     return res
 
 
+def conv_bytes(B: int, P: int, d: int, esz: int) -> int:
+    """x, x_prev, base and W_c read once, y written once."""
+    return esz * (B * P * d + B * d + 2 * d + 2 * (d // 16) * d + B * P * d)
+
+
+def time_conv(name: str, steps: int, warmup: int, rotate_mb: float):
+    import torch
+    import numpy as np
+    import draft_selection_topk16_amd as df2
+    from draft_selection_topk16_amd import synth
+    shp = synth.CONV_WORKLOADS[name]
+    B, P, d = shp["B"], shp["P"], shp["d"]
+    c = synth.make_conv_inputs(B, P, d, "bf16")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    one = (dev(c.x), dev(c.x_prev), dev(c.base), dev(c.W_c))
+    per = sum(t.nbytes for t in one) + one[0].nbytes
+    nsets = max(1, int(math.ceil(rotate_mb * 1e6 / per)))
+    sets = [one] + [tuple(t.clone() for t in one) for _ in range(nsets - 1)]
+    outs = [torch.empty_like(s[0]) for s in sets]
+    for i in range(warmup):
+        k = i % nsets
+        df2.conv2(*sets[k], out=outs[k])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        k = (warmup + i) % nsets
+        ev[i][0].record(stream)
+        df2.conv2(*sets[k], out=outs[k])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = statistics.fmean(a.elapsed_time(b) for a, b in ev) * 1e3
+    ab = conv_bytes(B, P, d, 2)
+    del sets, outs
+    torch.cuda.empty_cache()
+    return {"workload": "%s: B=%d P=%d d=%d bf16" % (name, B, P, d), "us_per_call": us,
+            "algorithmic_bytes": ab, "hbm_frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "rotation_sets": nsets}
+
+
 def _differ(paths):
     """Sequences whose greedy path differs from the Viterbi path."""
     import numpy as np
@@ -217,6 +264,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b1", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
     args = ap.parse_args()
 
@@ -319,6 +367,11 @@ def main():
         _, _, pp = time_workload(wlp, 3, 1, 0.0, ("viterbi", "greedy"))
         out["greedy"]["pair_dominant"] = {"workload": "%s with A and B scaled by 8" % wl.name,
                                           "paths_differ_from_viterbi": _differ(pp)}
+    if not args.no_conv:
+        out["conv"] = {}
+        for name in synth.CONV_WORKLOADS:
+            log("timing %s" % name)
+            out["conv"][name] = time_conv(name, args.steps, args.warmup, args.rotate_mb)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle for %.0f s" % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -24,7 +24,8 @@ WALKS = {"viterbi": 0, "greedy": 1}
 EXPORTED = (
     "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_topk",
     "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
-    "dflash2_sample_walk", "dflash2_device_error", "dflash2_release", "dflash2_status_string",
+    "dflash2_sample_walk", "dflash2_conv2", "dflash2_device_error", "dflash2_release",
+    "dflash2_status_string",
     "dflash2_last_error", "dflash2_version",
 )
 
@@ -68,6 +69,7 @@ def load() -> ctypes.CDLL:
         "dflash2_viterbi": [vp, vp, i32, i32, i32, vp, vp, vp],
         "dflash2_walk": [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp],
         "dflash2_sample_walk": [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp],
+        "dflash2_conv2": [vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp],
         "dflash2_device_error": [vp, u32p],
         "dflash2_release": [],
     }
@@ -281,6 +283,25 @@ def sample_walk(S: torch.Tensor, cand: torch.Tensor, u: torch.Tensor,
                                    float(temperature), _dev(path, "path"), _dev(q, "q"),
                                    _dev(score, "score"), _stream(S.device)))
     return path, q, score
+
+
+def conv2(x: torch.Tensor, x_prev: torch.Tensor, base: torch.Tensor, W_c: torch.Tensor,
+          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Two-tap dynamic depthwise convolution: x [B, P, d], x_prev [B, d],
+    base [2, d], W_c [2, d/16, d] (one dtype) -> y [B, P, d] in that dtype."""
+    lib = load()
+    B, P, d = x.shape
+    dt = _dtype_code(x)
+    for name, t in (("x_prev", x_prev), ("base", base), ("W_c", W_c)):
+        if t.dtype != x.dtype:
+            raise TypeError("%s must have the dtype of x" % name)
+    if x_prev.shape != (B, d) or base.shape != (2, d) or W_c.shape != (2, d // 16, d):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.dflash2_conv2(_dev(x, "x"), _dev(x_prev, "x_prev"), _dev(base, "base"),
+                             _dev(W_c, "W_c"), B, P, d, dt, _dev(out, "out"), _stream(x.device)))
+    return out
 
 
 def device_error(device: Optional[torch.device] = None) -> int:

@@ -41,6 +41,7 @@
 
 #include "dflash2.h"
 #include "common.hpp"
+#include "conv.hpp"
 #include "gate.hpp"
 #include "pairs.hpp"
 #include "topk.hpp"
@@ -1014,6 +1015,55 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx, const fl
 df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,
                            int32_t K, int32_t* out_path, float* out_score, hipStream_t stream) {
     return dflash2_walk(S, cand_idx, B, P, K, DF2_WALK_VITERBI, out_path, out_score, stream);
+}
+
+df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base, const void* W_c,
+                         int32_t B, int32_t P, int32_t d, df2_dtype dtype, void* out,
+                         hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != DF2_F32 && dtype != DF2_BF16) return fail(DF2_EINVAL, "unknown dtype");
+    if (B < 0) return fail(DF2_EINVAL, "B < 0");
+    if (P < 1) return fail(DF2_EINVAL, "P < 1");
+    if (d < 512 || d % 512 != 0 || d > 8192)
+        return fail(DF2_EUNSUPPORTED, "d must be a multiple of 512 in [512, 8192]");
+    if (B == 0) return DF2_OK;
+    const int64_t M = (int64_t)B * P;
+    if (M > (1 << 24)) return fail(DF2_EUNSUPPORTED, "B * P too large");
+    if (!x || !x_prev || !base || !W_c || !out) return fail(DF2_EINVAL, "NULL pointer argument");
+    if (!aligned16(x) || !aligned16(x_prev) || !aligned16(base) || !aligned16(W_c) || !aligned16(out))
+        return fail(DF2_EINVAL, "x, x_prev, base, W_c and out must be 16-byte aligned");
+    // the corrections: [M, d/8] = x [M, d] times W_c^T, on the gate's slices
+    const int N = d / 8;
+    Plan pl;
+    std::memset(&pl.p, 0, sizeof(pl.p));
+    pl.bf16 = dtype == DF2_BF16;
+    plan_gate(pl, M, d, N);
+    Params& p = pl.p;
+    p.rows = M;
+    p.hidden = x;
+    p.W = W_c;
+    const size_t counter_bytes = 256;          // the error word; nothing else is counted
+    const size_t off_ppart = counter_bytes;
+    const size_t off_corr = align_up(off_ppart + (p.S > 1 ? (size_t)p.S * M * N * 4 : 0), 256);
+    const size_t total = align_up(off_corr + (size_t)M * N * 4, 256);
+    void* sbase = nullptr;
+    df2_status st;
+    if ((st = get_scratch(stream, total, counter_bytes, &sbase)) != DF2_OK) return st;
+    note_layout(stream, counter_bytes);
+    char* c = reinterpret_cast<char*>(sbase);
+    p.err = reinterpret_cast<uint32_t*>(c);
+    p.ppart = reinterpret_cast<float*>(c + off_ppart);
+    p.H = reinterpret_cast<float*>(c + off_corr);
+    const float* corr = p.H;
+    return launch_checked([&] {
+        launch_gate(pl, stream);
+        const int64_t nv = M * (d / 8);
+        dim3 grid((unsigned)((nv + kWG - 1) / kWG)), block(kWG);
+        if (pl.bf16)
+            hipLaunchKernelGGL((k_conv2<true>), grid, block, 0, stream, x, x_prev, base, corr, out, M, P, d);
+        else
+            hipLaunchKernelGGL((k_conv2<false>), grid, block, 0, stream, x, x_prev, base, corr, out, M, P, d);
+    }, "dflash2_conv2 launch");
 }
 
 df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {

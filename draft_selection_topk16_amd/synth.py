@@ -36,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "Inputs", "make_inputs", "f32_to_bf16_bits",
-    "bf16_bits_to_f64", "to_f64",
+    "bf16_bits_to_f64", "to_f64", "ConvInputs", "CONV_WORKLOADS", "make_conv_inputs",
 ]
 
 
@@ -178,3 +178,46 @@ def make_inputs(wl: Workload, seed: Optional[int] = None,
     dt = wl.dtype
     return Inputs(wl=wl, logits=_store(logits, dt), hidden=_store(hidden, dt),
                   A=_store(A, dt), Bt=_store(Bt, dt), W=_store(W, dt), prev=prev)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the drafter's two-tap convolution ("A Lightweight Local
+# Convolution").  The pages give no trained values; the recipe: sublayer
+# inputs x and x_prev ~ N(0, 1); base tap 0 ~ 1 + 0.1 N(0, 1) (close to the
+# identity), tap 1 ~ 0.1 N(0, 1); correction map W_c ~ 0.1 N(0, 1) / sqrt(d)
+# (a small content-dependent correction, as the pages describe it).
+# Shapes follow the selector workloads: d = 2560 (Qwen3-4B drafter) and
+# d = 5120 (27B-target drafter), P = 7 draft positions.
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class ConvInputs:
+    B: int
+    P: int
+    d: int
+    dtype: str
+    x: np.ndarray        # [B, P, d]
+    x_prev: np.ndarray   # [B, d]
+    base: np.ndarray     # [2, d]
+    W_c: np.ndarray      # [2, d/16, d]
+
+    def f64(self):
+        dt = self.dtype
+        return dict(x=to_f64(self.x, dt), x_prev=to_f64(self.x_prev, dt),
+                    base=to_f64(self.base, dt), W_c=to_f64(self.W_c, dt))
+
+
+CONV_WORKLOADS = {
+    "conv_qwen3_4b_b1": dict(B=1, P=7, d=2560),
+    "conv_t27b_b32": dict(B=32, P=7, d=5120),
+}
+
+
+def make_conv_inputs(B: int, P: int, d: int, dtype: str = "bf16", seed: int = 0xC0) -> ConvInputs:
+    g = np.random.Generator(np.random.PCG64(0xDF2C00 + int(seed)))
+    x = g.standard_normal((B, P, d), dtype=np.float32)
+    x_prev = g.standard_normal((B, d), dtype=np.float32)
+    base = np.stack([1.0 + 0.1 * g.standard_normal(d, dtype=np.float32),
+                     0.1 * g.standard_normal(d, dtype=np.float32)]).astype(np.float32)
+    W_c = (0.1 / math.sqrt(d)) * g.standard_normal((2, d // 16, d), dtype=np.float32)
+    return ConvInputs(B, P, d, dtype, _store(x, dtype), _store(x_prev, dtype), _store(base, dtype),
+                      _store(W_c.astype(np.float32), dtype))

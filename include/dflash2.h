@@ -222,6 +222,30 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx,
                                hipStream_t stream);
 
 /*
+ * Two-tap dynamic depthwise convolution of the block drafter ("DFlash 2:
+ * Keep Drafting Parallel", section "A Lightweight Local Convolution"),
+ * applied around each attention and feed-forward sublayer:
+ *     y_t[c] = k_{t,0}[c] x_t[c] + k_{t,1}[c] x_{t-1}[c],   x_{-1} = x_prev,
+ *     k_{t,tap}[c] = base[tap][c] + corr_t[tap][c / 16],
+ *     corr_t[tap][g] = sum_m W_c[tap][g][m] x_t[m].
+ * The pages give a learned base plus a correction from the current hidden
+ * state shared by 16 channels; the correction's form is this library's
+ * reading (a bias-free linear map of x_t).
+ *   x      [B, P, d]     (dtype) sublayer input at the draft positions
+ *   x_prev [B, d]        (dtype) the same for the last verified token
+ *   base   [2, d]        (dtype) base kernel, tap 0 (current) then tap 1 (previous)
+ *   W_c    [2, d/16, d]  (dtype) correction map
+ *   out    [B, P, d]     (dtype) y; fp32 arithmetic, bf16 output rounded to
+ *                        nearest even; must not overlap x or x_prev
+ * B >= 0 (B == 0 enqueues nothing), P >= 1, d a multiple of 512 in
+ * [512, 8192]; every pointer 16-byte aligned.  The corrections go through
+ * the library's scratch (as dflash2_project's partials do).
+ */
+df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base,
+                         const void* W_c, int32_t B, int32_t P, int32_t d,
+                         df2_dtype dtype, void* out, hipStream_t stream);
+
+/*
  * Waits for `stream`, then reports and clears the device-side flags of its
  * scratch buffer: *flags receives a bit mask (bit 0: a prev_tok outside
  * [0, V) was replaced by 0; bit 1: a cand_idx entry outside [0, V) was

@@ -152,6 +152,15 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     assert lib.dflash2_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 101,
                                    FAKE, None) == DF2_EINVAL
     assert lib.dflash2_device_error(None, None) == DF2_EINVAL
+    # two-tap convolution
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE, 0, 7, 512, 1, FAKE, None) == DF2_OK
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE, 2, 7, 500, 1, FAKE, None) == DF2_EUNSUPPORTED
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE, 2, 7, 8704, 1, FAKE, None) == DF2_EUNSUPPORTED
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE, 2, 0, 512, 1, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE, -1, 7, 512, 1, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE, 2, 7, 512, 3, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_conv2(FAKE, None, FAKE, FAKE, 2, 7, 512, 1, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE + 8, 2, 7, 512, 1, FAKE, None) == DF2_EINVAL
 
 
 def test_binding_rejects_unknown_walk_name():
