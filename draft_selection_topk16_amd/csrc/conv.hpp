@@ -9,15 +9,20 @@
 // formula is not printed; this library reads it as a bias-free linear map
 //     corr_t[tap][g] = sum_m W_c[tap][g][m] x_t[m],  k_{t,tap}[c] = base[tap][c] + corr_t[tap][c / 16].
 //
-// The corrections are a small GEMM ([B*P, d] x [d, d/8]) done by the gate
-// projection's matrix-core slices; this file holds the combine: one thread
-// per 8 channels of one position (16-byte loads of x_t, x_{t-1} and both
-// base rows, two correction values), fp32 arithmetic, output in the input
-// type (bf16 rounded to nearest even).  HBM-bound: every byte is read once
-// apart from x, which the GEMM also reads.
+// One launch.  The corrections are a small GEMM ([B*P, d] x [d, d/8]) on
+// the gate projection's matrix-core slices, with the output columns ordered
+// (group, tap) so that a tile of 16*NB columns holds both taps of 8*NB
+// channel groups.  Every slice stores its partial tile and arrives on the
+// tile's counter; the last to arrive sums the S partials in slice order and
+// applies the combine to its rows and 128*NB channels: one thread per 8
+// channels of one position (16-byte loads of x_t, x_{t-1} and both base
+// rows), fp32 arithmetic, output in the input type (bf16 rounded to nearest
+// even).  HBM-bound: W_c, x_prev, base and y move once, x twice (GEMM and
+// combine, the second mostly from L2).
 #pragma once
 
 #include "common.hpp"
+#include "gate.hpp"
 
 namespace df2 {
 
@@ -59,32 +64,90 @@ __device__ __forceinline__ void store8(void* __restrict__ p, int64_t off, const 
     }
 }
 
-// x [M = B*P, d], x_prev [B, d], base [2, d], corr [M, d/8] (tap 0 groups,
-// then tap 1 groups), out [M, d].  One thread per 8 channels.
-template <bool BF16>
-__global__ __launch_bounds__(kWG) void k_conv2(const void* __restrict__ x, const void* __restrict__ x_prev,
-                                               const void* __restrict__ base,
-                                               const float* __restrict__ corr, void* __restrict__ out,
-                                               int64_t M, int P, int d) {
-    const int64_t i = (int64_t)blockIdx.x * kWG + threadIdx.x;
-    const int dv = d / 8, N = d / 8, G = d / 16;
-    if (i >= M * dv) return;
-    const int64_t m = i / dv;
-    const int c0 = (int)(i % dv) * 8;
-    const int t = (int)(m % P);
-    const float k0c = corr[m * N + (c0 >> 4)];
-    const float k1c = corr[m * N + G + (c0 >> 4)];
-    float xt[8], xp[8], b0[8], b1[8], y[8];
-    load8<BF16>(x, m * d + c0, xt);
-    if (t == 0)
-        load8<BF16>(x_prev, (m / P) * d + c0, xp);
-    else
-        load8<BF16>(x, (m - 1) * d + c0, xp);
-    load8<BF16>(base, c0, b0);
-    load8<BF16>(base, (int64_t)d + c0, b1);
+struct ConvArgs {
+    const void* x;         // [M, d]
+    const void* x_prev;    // [B, d]
+    const void* base;      // [2, d]
+    const void* Wc;        // [2, d/16, d]
+    void* out;             // [M, d]
+    float* ppart;          // [S, M, d/8] partial corrections, columns (group, tap)
+    uint32_t* tile_cnt;    // [mtiles * ntiles] slices done, reset by the last
+    int64_t M;
+    int P, d, S, ntiles;
+};
+
+struct ConvLds {
+    union {
+        GateLds g;
+        float corr[64 * 64];       // the tile's summed corrections [row][column]
+    };
+    uint32_t flag;
+};
+
+template <bool BF16, int MB>
+__global__ __launch_bounds__(kWG) void k_conv2(ConvArgs a) {
+    constexpr int NB = MB == 1 ? 4 : 2;
+    constexpr int TR = 16 * MB, TC = 16 * NB;      // tile rows, tile columns
+    __shared__ ConvLds sm;
+    const int tid = threadIdx.x;
+    const int N = a.d / 8, G = a.d / 16;
+    const int s = (int)(blockIdx.x % a.S), tile = (int)(blockIdx.x / a.S);
+    const int mt = tile / a.ntiles, nt = tile % a.ntiles;
+    gate_slice<BF16, MB, NB>(a.x, a.Wc, (int)a.M, a.d, N, mt, nt, s, a.S, a.ppart, sm.g, G);
+    if (!block_arrive_last(&a.tile_cnt[tile], (uint32_t)a.S, &sm.flag)) return;
+    if (tid == 0) reset_counter(&a.tile_cnt[tile]);
+    // sum the S partials of the tile in slice order; a thread's loads all
+    // go out before the first add
+    const int64_t m0 = (int64_t)mt * TR;
+    constexpr int PER = TR * TC / kWG;              // entries per thread (4 or 8)
+    const int64_t plane = a.M * N;
+    float acc[PER];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (b0[e] + k0c) * xt[e] + (b1[e] + k1c) * xp[e];
-    store8<BF16>(out, m * d + c0, y);
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    for (int q0 = 0; q0 < a.S; q0 += 4) {
+        float v[4][PER];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int x = e * kWG + tid, row = x / TC, col = x % TC;
+                const int64_t mm = min(m0 + row, a.M - 1);
+                const int q = min(q0 + qq, a.S - 1);
+                v[qq][e] = xload(a.ppart + q * plane + mm * N + nt * TC + col);
+            }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                if (q0 + qq < a.S) acc[e] = (q0 + qq == 0) ? v[qq][e] : acc[e] + v[qq][e];
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) sm.corr[e * kWG + tid] = acc[e];
+    __syncthreads();
+    // combine: rows m0 .., channels of groups g0 .. g0 + TC / 2
+    const int g0 = nt * (TC / 2);
+    constexpr int VPR = TC / 2 * 2;                 // 8-channel vectors per row (2 per group)
+    for (int v = tid; v < TR * VPR; v += kWG) {
+        const int row = v / VPR, vc = v % VPR;
+        const int64_t m = m0 + row;
+        if (m >= a.M) continue;
+        const int gl = vc >> 1;                     // group within the tile
+        const int c0 = (g0 + gl) * 16 + (vc & 1) * 8;
+        const float k0c = sm.corr[row * TC + 2 * gl];
+        const float k1c = sm.corr[row * TC + 2 * gl + 1];
+        const int t = (int)(m % a.P);
+        float xt[8], xp[8], b0[8], b1[8], y[8];
+        load8<BF16>(a.x, m * a.d + c0, xt);
+        if (t == 0)
+            load8<BF16>(a.x_prev, (m / a.P) * a.d + c0, xp);
+        else
+            load8<BF16>(a.x, (m - 1) * a.d + c0, xp);
+        load8<BF16>(a.base, c0, b0);
+        load8<BF16>(a.base, (int64_t)a.d + c0, b1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (b0[e] + k0c) * xt[e] + (b1[e] + k1c) * xp[e];
+        store8<BF16>(a.out, m * a.d + c0, y);
+    }
 }
 
 }  // namespace df2

@@ -1032,37 +1032,51 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base, co
     if (!x || !x_prev || !base || !W_c || !out) return fail(DF2_EINVAL, "NULL pointer argument");
     if (!aligned16(x) || !aligned16(x_prev) || !aligned16(base) || !aligned16(W_c) || !aligned16(out))
         return fail(DF2_EINVAL, "x, x_prev, base, W_c and out must be 16-byte aligned");
-    // the corrections: [M, d/8] = x [M, d] times W_c^T, on the gate's slices
+    // the corrections [M, d/8] = x [M, d] times W_c^T on the gate's slices,
+    // then the combine by the last slice of each tile, in one launch
     const int N = d / 8;
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = dtype == DF2_BF16;
     plan_gate(pl, M, d, N);
-    Params& p = pl.p;
-    p.rows = M;
-    p.hidden = x;
-    p.W = W_c;
-    const size_t counter_bytes = 256;          // the error word; nothing else is counted
+    {
+        // fewer, longer slices than the selector's: the last slice of a tile
+        // sums them all
+        const int KS = d / 32;
+        int S = std::max(1, std::min(env_int("DF2_CONV_S", 4), KS / (kWaves * gate_kb(pl.bf16))));
+        pl.p.S = S;
+    }
+    const int ntiles_total = pl.p.mtiles * pl.p.ntiles;
+    const size_t counter_bytes = align_up(4 * (1 + (size_t)ntiles_total), 256);
     const size_t off_ppart = counter_bytes;
-    const size_t off_corr = align_up(off_ppart + (p.S > 1 ? (size_t)p.S * M * N * 4 : 0), 256);
-    const size_t total = align_up(off_corr + (size_t)M * N * 4, 256);
+    const size_t total = align_up(off_ppart + (size_t)pl.p.S * M * N * 4, 256);
     void* sbase = nullptr;
     df2_status st;
     if ((st = get_scratch(stream, total, counter_bytes, &sbase)) != DF2_OK) return st;
     note_layout(stream, counter_bytes);
     char* c = reinterpret_cast<char*>(sbase);
-    p.err = reinterpret_cast<uint32_t*>(c);
-    p.ppart = reinterpret_cast<float*>(c + off_ppart);
-    p.H = reinterpret_cast<float*>(c + off_corr);
-    const float* corr = p.H;
+    ConvArgs a;
+    a.x = x;
+    a.x_prev = x_prev;
+    a.base = base;
+    a.Wc = W_c;
+    a.out = out;
+    a.ppart = reinterpret_cast<float*>(c + off_ppart);
+    a.tile_cnt = reinterpret_cast<uint32_t*>(c) + 1;    // word 0 is the error flag
+    a.M = M;
+    a.P = P;
+    a.d = d;
+    a.S = pl.p.S;
+    a.ntiles = pl.p.ntiles;
+    dim3 grid((unsigned)(ntiles_total * pl.p.S)), block(kWG);
     return launch_checked([&] {
-        launch_gate(pl, stream);
-        const int64_t nv = M * (d / 8);
-        dim3 grid((unsigned)((nv + kWG - 1) / kWG)), block(kWG);
-        if (pl.bf16)
-            hipLaunchKernelGGL((k_conv2<true>), grid, block, 0, stream, x, x_prev, base, corr, out, M, P, d);
-        else
-            hipLaunchKernelGGL((k_conv2<false>), grid, block, 0, stream, x, x_prev, base, corr, out, M, P, d);
+        if (pl.bf16) {
+            if (pl.mb == 1) hipLaunchKernelGGL((k_conv2<true, 1>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((k_conv2<true, 4>), grid, block, 0, stream, a);
+        } else {
+            if (pl.mb == 1) hipLaunchKernelGGL((k_conv2<false, 1>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((k_conv2<false, 4>), grid, block, 0, stream, a);
+        }
     }, "dflash2_conv2 launch");
 }
 

@@ -34,11 +34,13 @@ struct GateLds {
 
 // Slice s (of S) of tile (mt, nt); tile rows mt*16*MB.., columns nt*16*NB..
 // dst: [S, M, r] partials (slice s at dst + s*M*r); with S == 1 this is H.
-// Rows m >= M load row M - 1 and are not written.  Every thread calls.
+// Rows m >= M load row M - 1 and are not written.  With pair_half > 0,
+// output column q takes row (q % 2) * pair_half + q / 2 of W (two
+// half-matrices interleaved column by column).  Every thread calls.
 template <bool BF16, int MB, int NB>
 __device__ void gate_slice(const void* __restrict__ hidden, const void* __restrict__ W, int M,
                            int d, int r, int mt, int nt, int s, int S, float* __restrict__ dst,
-                           GateLds& sm) {
+                           GateLds& sm, int pair_half = 0) {
     static_assert((MB * NB) % 4 == 0, "blocks are summed four at a time");
     constexpr int KB = gate_kb(BF16);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -60,7 +62,10 @@ __device__ void gate_slice(const void* __restrict__ hidden, const void* __restri
     for (int i = 0; i < MB; ++i)
         arow[i] = (int64_t)min(mt * 16 * MB + 16 * i + row, M - 1) * d;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) brow[j] = (int64_t)(nt * 16 * NB + 16 * j + row) * d;
+    for (int j = 0; j < NB; ++j) {
+        const int q = nt * 16 * NB + 16 * j + row;
+        brow[j] = (int64_t)(pair_half > 0 ? (q & 1) * pair_half + (q >> 1) : q) * d;
+    }
 
     // wave w takes steps kb .. kb + KB - 1, kb = ks0 + KB * (w + 4 i)
     for (int kb = ks0 + KB * w; kb < ks1; kb += kWaves * KB) {
