@@ -83,6 +83,7 @@ struct Params {
     int C;                // chunks per row
     int nseg;             // segments per row
     int aligned;          // logits rows are 16-byte aligned and V % per-vector == 0
+    int split;            // vectors per lane the chunks were counted with
     int gm_rows;          // rows per gate tile
     int mtiles, ntiles, S, n_gate;
     int64_t n_chunk;      // segment workgroups (rows * nseg)
@@ -131,7 +132,7 @@ template <bool BF16, int NV>
 __device__ void segment_of(const Params& p, int64_t row, int seg, ChunkLds& sm) {
     const size_t esz = BF16 ? 2 : 4;
     const char* rowp = reinterpret_cast<const char*>(p.logits) + (size_t)row * p.V * esz;
-    segment_topk<BF16, NV>(rowp, p.V, p.C, seg, p.nseg, p.K, p.aligned != 0,
+    segment_topk<BF16, NV>(rowp, p.V, p.C, seg, p.nseg, p.K, p.split,
                            p.part + ((size_t)row * p.nseg + seg) * kWaves * p.K, sm);
 }
 
@@ -546,6 +547,7 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     const int forced = env_int("DF2_NV", 0);
     if (forced == 1 || forced == 2 || forced == 4) nv = forced;
     pl.nv = nv;
+    p.split = nv;
     p.C = chunks(nv);
     target = std::max<int64_t>(1, env_int("DF2_WGS", (int)std::min<int64_t>(target, 1 << 30)));
     // at most kMergeMax words per row merge; fewer lists also make the merge
@@ -556,7 +558,9 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     p.rows = rows;
     p.V = V;
     p.K = K;
-    p.aligned = (aligned16(logits) && (V % pv) == 0) ? 1 : 0;
+    // the aligned path reads a row through a buffer resource: under 2^31 bytes
+    p.aligned = (aligned16(logits) && (V % pv) == 0 && (int64_t)V * (bf16 ? 2 : 4) < (1LL << 31))
+                    ? 1 : 0;
     pl.n_chunk_blocks = rows * p.nseg;
     p.n_chunk = pl.n_chunk_blocks;
 }
@@ -673,7 +677,8 @@ void launch_select(const Plan& pl, hipStream_t stream) {
         else DF2_SEL_W(BF, NV_, MB_, false);                      \
     } while (0)
 #define DF2_SEL_NV(BF, MB_)                  \
-    switch (pl.nv) {                         \
+    switch (pl.p.aligned ? pl.nv : 0) {      \
+        case 0: DF2_SEL(BF, 0, MB_); break;  \
         case 1: DF2_SEL(BF, 1, MB_); break;  \
         case 2: DF2_SEL(BF, 2, MB_); break;  \
         default: DF2_SEL(BF, 4, MB_); break; \
@@ -691,7 +696,8 @@ void launch_select(const Plan& pl, hipStream_t stream) {
 void launch_topk(const Plan& pl, hipStream_t stream) {
     dim3 grid((unsigned)pl.n_chunk_blocks), block(kWG);
 #define DF2_TOPK(BF)                                                                          \
-    switch (pl.nv) {                                                                          \
+    switch (pl.p.aligned ? pl.nv : 0) {                                                       \
+        case 0: hipLaunchKernelGGL((k_topk<BF, 0>), grid, block, 0, stream, pl.p); break;   \
         case 1: hipLaunchKernelGGL((k_topk<BF, 1>), grid, block, 0, stream, pl.p); break;   \
         case 2: hipLaunchKernelGGL((k_topk<BF, 2>), grid, block, 0, stream, pl.p); break;   \
         default: hipLaunchKernelGGL((k_topk<BF, 4>), grid, block, 0, stream, pl.p); break;  \

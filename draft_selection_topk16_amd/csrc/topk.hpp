@@ -131,6 +131,24 @@ __device__ __forceinline__ u32x4_t load_vec(const void* __restrict__ row, int V,
     }
 }
 
+// Aligned rows are read through a raw buffer resource that spans exactly the
+// row (num_records = its bytes).  A load whose offset lies past the end
+// returns zeros without touching memory, so prefetches beyond the segment
+// (and the vector slots beyond the row in its last chunk) cost no traffic.
+// Loads carry the non-temporal hint: the logits are read once.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, (int)bytes,
+                                             0x00020000);
+}
+constexpr uint32_t kOutOfRow = 0x80000000u;     // beyond any row (rows are < 2^31 bytes)
+template <bool BF16>
+__device__ __forceinline__ u32x4_t load_vec_rs(__amdgpu_buffer_rsrc_t rs, int V, int64_t e0,
+                                               bool live) {
+    constexpr int ESZ = BF16 ? 2 : 4;
+    const uint32_t off = (live && e0 < V) ? (uint32_t)(e0 * ESZ) : kOutOfRow;
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+}
+
 // At consumption: an aligned vector that lies beyond the row becomes the
 // sentinel (its load read an in-bounds stand-in).
 template <bool ALIGNED>
@@ -376,18 +394,29 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
         }
     };
     // Two register buffers, used in turn without copies: while one chunk is
-    // processed the next one's loads are in flight.  Past the segment end a
-    // prefetch re-reads the last chunk (in bounds, never consumed).
+    // processed the next one's loads are in flight.  Aligned rows load
+    // through the row's buffer resource, and a prefetch past the segment end
+    // reads nothing; otherwise it re-reads the last chunk (in bounds, never
+    // consumed).
     u32x4_t b0[NV], b1[NV];
     const int clast = nc - 1;
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, (uint32_t)V * (BF16 ? 2u : 4u));
+    auto fetch = [&](u32x4_t (&b)[NV], int c) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if constexpr (ALIGNED)
+                b[j] = load_vec_rs<BF16>(rs, V, eb_of(min(c, clast)) + (int64_t)(j * 64 + lane) * PV,
+                                         c <= clast);
+            else
+                b[j] = load_vec<BF16, false>(row, V, eb_of(min(c, clast)) + (int64_t)(j * 64 + lane) * PV);
+        }
+    };
     // The shared bounds start at zero (one barrier, before any load is in
     // flight).
     if (tid == 0) sm.bound = 0;
     if (tid < kWaves) sm.qkey[tid] = 0;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(0) + (int64_t)(j * 64 + lane) * PV);
+    fetch(b0, 0);
     {
         // Initial bound, per wave: the K-th largest of its 64 lane maxima
         // over its first chunk (K lane maxima reach it); published with an
@@ -407,20 +436,14 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
             __hip_atomic_fetch_max(&sm.bound, T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     for (int c = 0; c < nc; c += 2) {
-        const int cn = min(c + 1, clast);
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            b1[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(cn) + (int64_t)(j * 64 + lane) * PV);
+        fetch(b1, c + 1);
         tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c), K, b0, tk, wg_bound(), npend, sm.wv[w]);
         settle(false);
         // Keep the next half's uses of its loads below this point: hoisting
         // one would wait on every load in flight, prefetch included.
         __builtin_amdgcn_sched_barrier(0);
         if (c + 1 >= nc) break;
-        const int cnn = min(c + 2, clast);
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            b0[j] = load_vec<BF16, ALIGNED>(row, V, eb_of(cnn) + (int64_t)(j * 64 + lane) * PV);
+        fetch(b0, c + 2);
         tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c + 1), K, b1, tk, wg_bound(), npend, sm.wv[w]);
         settle(false);
         __builtin_amdgcn_sched_barrier(0);
@@ -432,17 +455,23 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
 }
 
 // Segment seg of nseg of a row of C chunks (chunks seg, seg + nseg, ...).
+//   NV >= 1: rows are 16-byte aligned and V is a multiple of kPerVec; chunks
+//   of NV vectors per lane.
+//   NV == 0: rows that are not aligned load element by element; the C chunks
+//   were counted with `split` vectors per lane, and each is taken as `split`
+//   one-vector chunks so that this rare path stays small in registers.  It
+//   is a kernel instantiation of its own: kept beside the aligned path, the
+//   compiler emits it as a called function, and the call stack then gives
+//   every workgroup of the launch a private segment.
 template <bool BF16, int NV>
-__device__ void segment_topk(const void* __restrict__ row, int V, int C, int seg, int nseg, int K,
-                             bool aligned, uint64_t* __restrict__ out, ChunkLds& sm) {
+__device__ __forceinline__ void segment_topk(const void* __restrict__ row, int V, int C, int seg,
+                                             int nseg, int K, int split,
+                                             uint64_t* __restrict__ out, ChunkLds& sm) {
     const int nc = (C - seg + nseg - 1) / nseg;
-    // Rows that are not 16-byte aligned load element by element; they use
-    // one-vector chunks (each chunk split in NV) so that this rare path stays
-    // small in registers.
-    if (aligned)
-        segment_topk_impl<BF16, NV, true>(row, V, seg, nseg, nc, 1, K, out, sm);
+    if constexpr (NV == 0)
+        segment_topk_impl<BF16, 1, false>(row, V, seg, nseg, nc * split, split, K, out, sm);
     else
-        segment_topk_impl<BF16, 1, false>(row, V, seg, nseg, nc * NV, NV, K, out, sm);
+        segment_topk_impl<BF16, NV, true>(row, V, seg, nseg, nc, 1, K, out, sm);
 }
 
 // Stage 2: top K of one row from its nl sorted segment lists (K words each,
