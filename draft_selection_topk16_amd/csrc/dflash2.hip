@@ -446,6 +446,7 @@ struct Scratch {
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 std::map<int, int> g_capacity;         // device -> resident select workgroups
+std::map<int, int> g_cus;              // device -> compute units
 
 // Scratch of at least `bytes`, whose first `counter_bytes` are zero when the
 // stream reaches the next launch.
@@ -519,6 +520,22 @@ int select_capacity() {
     return cap;
 }
 
+// Compute units of the current device.
+int cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_cus.find(dev);
+        if (it != g_cus.end()) return it->second;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_cus[dev] = cus;
+    return cus;
+}
+
 struct Plan {
     Params p;
     int nv = 1;
@@ -530,10 +547,11 @@ struct Plan {
 };
 
 // Chunk size (16-byte vectors per thread) and segmentation of the rows.
-// Chunks of 256 x 4 vectors keep two register buffers per thread cheap;
-// smaller chunks are used when there are too few rows to give every CU a
-// workgroup.  Rows are then cut into segments so that about `target`
-// workgroups stream in total; a row's segment lists must fit one merge.
+// Chunks of 256 x 4 vectors (16 KB of bf16) whenever a row holds at least
+// eight of them; for shorter rows, smaller chunks when there are too few
+// rows to give every CU a workgroup.  Rows are then cut into segments so
+// that about `target` workgroups stream in total; a row's segment lists
+// must fit one merge.
 void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits,
                int64_t target) {
     Params& p = pl.p;
@@ -541,8 +559,12 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     const int pv = bf16 ? 8 : 4;
     auto chunks = [&](int nv) { return (int)((V + (int64_t)kWG * pv * nv - 1) / ((int64_t)kWG * pv * nv)); };
     int nv = 1;
-    for (int cand : {4, 2, 1}) {
-        if (rows * chunks(cand) >= 256) { nv = cand; break; }
+    if (chunks(4) >= 8) {
+        nv = 4;
+    } else {
+        for (int cand : {4, 2, 1}) {
+            if (rows * chunks(cand) >= 256) { nv = cand; break; }
+        }
     }
     const int forced = env_int("DF2_NV", 0);
     if (forced == 1 || forced == 2 || forced == 4) nv = forced;
@@ -772,9 +794,14 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = bf16;
     plan_gate(pl, rows, dims->d, dims->r);
-    // segments fill what the gate leaves of one resident wave of workgroups
+    // About two and a half segment workgroups per CU, within what the gate
+    // leaves of one resident wave of workgroups.  Measured at V = 151936,
+    // d = 5120 (bf16): 2 segments per row at batch 32 (448 workgroups) beat 3
+    // by 1.5 us and 1 by 1.4 us; 11 to 14 per row at batch 8 beat 16 by
+    // 4 us.
     const int64_t cap = select_capacity();
-    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, cap - pl.p.n_gate));
+    const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, (5 * (int64_t)cu_count()) / 2);
+    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target));
     if (pl.p.n_gate + pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "problem too large");
     plan_layout(pl, rows, rows, dims->B, true);
     Params& p = pl.p;
