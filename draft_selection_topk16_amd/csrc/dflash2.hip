@@ -590,8 +590,10 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
 // Gate tiles and slices of d.  Tiles are 16 x 64 for a single tile row of
 // at most 16 rows, else 64 x 32.  A slice is at least one round of loads
 // (4 waves x gate_kb k steps); S is the largest count of such slices that
-// stays within kMaxFusedSlices (the pair scores sum the partials): many
-// short slices finish early, beside the streaming segments.  The standalone
+// stays within kMaxFusedSlices (the pair scores sum the partials) and gives
+// about one gate workgroup per CU at most: many short slices finish early,
+// beside the streaming segments, but past one per CU the gate's workgroups
+// take slots and issue cycles from the streaming.  The standalone
 // projection uses the same slices, so both paths round alike.
 void plan_gate(Plan& pl, int64_t M, int d, int r) {
     Params& p = pl.p;
@@ -603,6 +605,10 @@ void plan_gate(Plan& pl, int64_t M, int d, int r) {
     const int KS = d / 32;
     const int per_round = kWaves * gate_kb(pl.bf16);
     int S = std::max(1, std::min(kMaxFusedSlices, (KS + per_round - 1) / per_round));
+    // at least four slices; measured at d = 5120: batch 32 runs 37.5 us per
+    // cycle with 8 slices against 41.0 with 16, batch 8 keeps 16 (its rows
+    // are ready sooner, so its gate must end sooner)
+    S = std::min(S, std::max(4, cu_count() / (p.mtiles * p.ntiles)));
     const int forced = env_int("DF2_S", 0);
     if (forced >= 1 && forced <= std::min(KS, kMaxFusedSlices)) S = forced;
     p.S = S;
