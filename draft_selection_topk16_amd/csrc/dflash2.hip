@@ -1080,9 +1080,11 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base, co
     plan_gate(pl, M, d, N);
     {
         // fewer, longer slices than the selector's: the last slice of a tile
-        // sums them all
+        // sums them all (measured best: 4 with 64-row tiles, B = 32,
+        // d = 5120; 8 with one 16-row tile, B = 1, d = 2560)
         const int KS = d / 32;
-        int S = std::max(1, std::min(env_int("DF2_CONV_S", 4), KS / (kWaves * gate_kb(pl.bf16))));
+        const int s_def = pl.mb == 1 ? 8 : 4;
+        int S = std::max(1, std::min(env_int("DF2_CONV_S", s_def), KS / (kWaves * gate_kb(pl.bf16))));
         pl.p.S = S;
     }
     const int ntiles_total = pl.p.mtiles * pl.p.ntiles;

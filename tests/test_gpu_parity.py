@@ -332,6 +332,30 @@ def test_select_empty_batch():
     assert path.shape == (0, 7) and score.shape == (0,)
 
 
+@pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1"])
+def test_select_same_result_under_any_segment_plan(name, monkeypatch):
+    """The segment plan (segments per row, chunk width) changes neither the
+    gate sums nor any comparison: candidate words are exact and the merge is
+    independent of how a row was cut, so path and score are bit-identical
+    across plans."""
+    say("select under segment plans %s" % name)
+    x = inputs(name)
+    t = to_device(x)
+    args = (t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K)
+    ref = [a.clone() for a in df2.select(*args)]
+    torch.cuda.synchronize()
+    for env in ({"DF2_WGS": "64"}, {"DF2_WGS": "700"}, {"DF2_NV": "1"}, {"DF2_NV": "2", "DF2_WGS": "300"}):
+        for k in ("DF2_WGS", "DF2_NV"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        p, s = df2.select(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(p, ref[0]) and torch.equal(s, ref[1]), env
+    for k in ("DF2_WGS", "DF2_NV"):
+        monkeypatch.delenv(k, raising=False)
+
+
 def test_select_deterministic_and_scratch_reuse():
     say("select determinism and scratch reuse")
     big = inputs("t27b_b32")
