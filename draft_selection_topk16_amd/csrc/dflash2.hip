@@ -1081,9 +1081,10 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base, co
     {
         // fewer, longer slices than the selector's: the last slice of a tile
         // sums them all (measured best: 4 with 64-row tiles, B = 32,
-        // d = 5120; 8 with one 16-row tile, B = 1, d = 2560)
+        // d = 5120; with one 16-row tile as many as one round of loads per
+        // slice allows, 10 at B = 1, d = 2560: 11.0 us against 13.0 with 4)
         const int KS = d / 32;
-        const int s_def = pl.mb == 1 ? 8 : 4;
+        const int s_def = pl.mb == 1 ? 16 : 4;
         int S = std::max(1, std::min(env_int("DF2_CONV_S", s_def), KS / (kWaves * gate_kb(pl.bf16))));
         pl.p.S = S;
     }
