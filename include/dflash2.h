@@ -39,6 +39,18 @@
  *  - Top-K order: value descending; equal values (IEEE, -0 == +0) go to the
  *    lower vocabulary index.  Walk ties go to the smaller predecessor rank,
  *    the final pick to the smaller rank.
+ *  - The launch plan is chosen from the shapes and the device; environment
+ *    variables, read at every call, override it for measurement:
+ *      DF2_WGS     target count of top-K segment workgroups
+ *      DF2_NV      16-byte vectors per lane per chunk (1, 2 or 4)
+ *      DF2_MWORDS  most candidate words one row merge takes (<= 1024)
+ *      DF2_S       gate slices of d (1..16)
+ *      DF2_GSEP    1: the gate runs as a launch of its own first
+ *      DF2_CONV_S  k slices of the convolution's correction GEMM
+ *    The top-K plan (DF2_WGS, DF2_NV, DF2_MWORDS) never changes a result.
+ *    DF2_S and DF2_CONV_S change the fp32 summation order of the gate and
+ *    of the corrections (results stay within the documented tolerances,
+ *    and dflash2_project keeps matching dflash2_select bit for bit).
  */
 #ifndef DFLASH2_H
 #define DFLASH2_H
