@@ -124,29 +124,47 @@ __global__ __launch_bounds__(kWG) void k_conv2(ConvArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) sm.corr[e * kWG + tid] = acc[e];
     __syncthreads();
-    // combine: rows m0 .., channels of groups g0 .. g0 + TC / 2
+    // combine: rows m0 .., channels of groups g0 .. g0 + TC / 2.  Vector v
+    // (8 channels of one row) goes to thread v % kWG; since kWG is a
+    // multiple of the vectors per row, all of a thread's vectors cover the
+    // same 8 channels, so the two base rows are loaded once, and the x loads
+    // of a batch of vectors all go out before the first is used.
     const int g0 = nt * (TC / 2);
     constexpr int VPR = TC / 2 * 2;                 // 8-channel vectors per row (2 per group)
-    for (int v = tid; v < TR * VPR; v += kWG) {
-        const int row = v / VPR, vc = v % VPR;
-        const int64_t m = m0 + row;
-        if (m >= a.M) continue;
-        const int gl = vc >> 1;                     // group within the tile
-        const int c0 = (g0 + gl) * 16 + (vc & 1) * 8;
-        const float k0c = sm.corr[row * TC + 2 * gl];
-        const float k1c = sm.corr[row * TC + 2 * gl + 1];
-        const int t = (int)(m % a.P);
-        float xt[8], xp[8], b0[8], b1[8], y[8];
-        load8<BF16>(a.x, m * a.d + c0, xt);
-        if (t == 0)
-            load8<BF16>(a.x_prev, (m / a.P) * a.d + c0, xp);
-        else
-            load8<BF16>(a.x, (m - 1) * a.d + c0, xp);
-        load8<BF16>(a.base, c0, b0);
-        load8<BF16>(a.base, (int64_t)a.d + c0, b1);
+    static_assert(kWG % VPR == 0, "a thread's vectors share their channels");
+    constexpr int NVEC = TR * VPR / kWG;            // vectors per thread
+    constexpr int BATCH = BF16 ? NVEC : (NVEC > 2 ? NVEC / 2 : NVEC);
+    const int vc = tid % VPR, gl = vc >> 1;
+    const int c0 = (g0 + gl) * 16 + (vc & 1) * 8;
+    float b0[8], b1[8];
+    load8<BF16>(a.base, c0, b0);
+    load8<BF16>(a.base, (int64_t)a.d + c0, b1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (b0[e] + k0c) * xt[e] + (b1[e] + k1c) * xp[e];
-        store8<BF16>(a.out, m * a.d + c0, y);
+    for (int k0 = 0; k0 < NVEC; k0 += BATCH) {
+        float xt[BATCH][8], xp[BATCH][8];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int row = (tid + (k0 + u) * kWG) / VPR;
+            const int64_t m = min(m0 + row, a.M - 1);   // rows past M load row M - 1, unused
+            const int t = (int)(m % a.P);
+            load8<BF16>(a.x, m * a.d + c0, xt[u]);
+            if (t == 0)
+                load8<BF16>(a.x_prev, (m / a.P) * a.d + c0, xp[u]);
+            else
+                load8<BF16>(a.x, (m - 1) * a.d + c0, xp[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int row = (tid + (k0 + u) * kWG) / VPR;
+            const int64_t m = m0 + row;
+            if (m >= a.M) continue;
+            const float k0c = sm.corr[row * TC + 2 * gl];
+            const float k1c = sm.corr[row * TC + 2 * gl + 1];
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (b0[e] + k0c) * xt[u][e] + (b1[e] + k1c) * xp[u][e];
+            store8<BF16>(a.out, m * a.d + c0, y);
+        }
     }
 }
 
