@@ -98,37 +98,27 @@ __device__ __forceinline__ uint32_t elem_bits(const u32x4_t& v, int p) {
     }
 }
 
-// Loads of the 16-byte vector holding elements [e0, e0 + kPerVec) of a row.
-//   ALIGNED: the row start is 16-byte aligned and V is a multiple of
-//   kPerVec, so a vector is all in or all out.  The load is then issued
-//   unconditionally from a clamped (in-bounds) address and nothing is done
-//   with the value until it is consumed (mask_vec), so consecutive loads stay
-//   in flight together.
-//   Otherwise elements are loaded one by one; out-of-row ones read as the
-//   all-ones sentinel.
-template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ u32x4_t load_vec(const void* __restrict__ row, int V, int64_t e0) {
+// Element-wise load of the 16-byte vector holding elements [e0, e0 + kPerVec)
+// of a row that is not 16-byte aligned (or whose length is not a multiple of
+// kPerVec); out-of-row elements read as the all-ones sentinel.
+template <bool BF16>
+__device__ __forceinline__ u32x4_t load_vec_elems(const void* __restrict__ row, int V, int64_t e0) {
     constexpr int PV = Elem<BF16>::kPerVec;
-    if constexpr (ALIGNED) {
-        const int64_t vi = (e0 < V) ? e0 / PV : 0;
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row) + vi);
-    } else {
-        uint32_t wv[4] = {~0u, ~0u, ~0u, ~0u};
+    uint32_t wv[4] = {~0u, ~0u, ~0u, ~0u};
 #pragma unroll
-        for (int p = 0; p < PV; ++p) {
-            const int64_t e = e0 + p;
-            if (e < V) {
-                if constexpr (BF16) {
-                    const uint32_t bits = reinterpret_cast<const uint16_t*>(row)[e];
-                    const uint32_t sh = (p & 1) * 16;
-                    wv[p >> 1] = (wv[p >> 1] & ~(0xFFFFu << sh)) | (bits << sh);
-                } else {
-                    wv[p] = reinterpret_cast<const uint32_t*>(row)[e];
-                }
+    for (int p = 0; p < PV; ++p) {
+        const int64_t e = e0 + p;
+        if (e < V) {
+            if constexpr (BF16) {
+                const uint32_t bits = reinterpret_cast<const uint16_t*>(row)[e];
+                const uint32_t sh = (p & 1) * 16;
+                wv[p >> 1] = (wv[p >> 1] & ~(0xFFFFu << sh)) | (bits << sh);
+            } else {
+                wv[p] = reinterpret_cast<const uint32_t*>(row)[e];
             }
         }
-        return u32x4_t{wv[0], wv[1], wv[2], wv[3]};
     }
+    return u32x4_t{wv[0], wv[1], wv[2], wv[3]};
 }
 
 // Aligned rows are read through a raw buffer resource that spans exactly the
@@ -150,7 +140,7 @@ __device__ __forceinline__ u32x4_t load_vec_rs(__amdgpu_buffer_rsrc_t rs, int V,
 }
 
 // At consumption: an aligned vector that lies beyond the row becomes the
-// sentinel (its load read an in-bounds stand-in).
+// sentinel (its buffer load returned zeros).
 template <bool ALIGNED>
 __device__ __forceinline__ u32x4_t mask_vec(u32x4_t x, int64_t e0, int V) {
     if constexpr (ALIGNED) {
@@ -408,7 +398,7 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
                 b[j] = load_vec_rs<BF16>(rs, V, eb_of(min(c, clast)) + (int64_t)(j * 64 + lane) * PV,
                                          c <= clast);
             else
-                b[j] = load_vec<BF16, false>(row, V, eb_of(min(c, clast)) + (int64_t)(j * 64 + lane) * PV);
+                b[j] = load_vec_elems<BF16>(row, V, eb_of(min(c, clast)) + (int64_t)(j * 64 + lane) * PV);
         }
     };
     // The shared bounds start at zero (one barrier, before any load is in
