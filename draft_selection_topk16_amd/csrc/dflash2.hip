@@ -128,11 +128,11 @@ __device__ void gate_role(const Params& p, int gb, GateLds& sm) {
     if (threadIdx.x == 0) arrive(&p.gate_cnt[mt]);
 }
 
-template <bool BF16, int NV>
+template <bool BF16, int NV, bool LDSR = false>
 __device__ void segment_of(const Params& p, int64_t row, int seg, ChunkLds& sm) {
     const size_t esz = BF16 ? 2 : 4;
     const char* rowp = reinterpret_cast<const char*>(p.logits) + (size_t)row * p.V * esz;
-    segment_topk<BF16, NV>(rowp, p.V, p.C, seg, p.nseg, p.K, p.split,
+    segment_topk<BF16, NV, LDSR>(rowp, p.V, p.C, seg, p.nseg, p.K, p.split,
                            p.part + ((size_t)row * p.nseg + seg) * kWaves * p.K, sm);
 }
 
@@ -192,26 +192,14 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
     pair_tiles<BF16>(p.A, p.Bt, K, r, e0, ne, p.Sb + (rb + e0) * K * K, sm, [] {});
 }
 
-// The whole selector in one launch.
-template <bool BF16, int NV, int MB, bool SAMPLE>
-__global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
-    __shared__ SharedAll sm;
-    __shared__ uint32_t flag;
+// Everything after a row's segments: the row merge (with the gate row H_t),
+// the pair scores of the transitions the row completes, and the walk of the
+// sequence whose last transition it scores.  Every thread of the workgroup
+// calls.
+template <bool BF16, int MB, bool SAMPLE>
+__device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll& sm,
+                                         uint32_t& flag) {
     const int tid = threadIdx.x;
-    const int64_t g = blockIdx.x + p.base;
-    if (g < p.n_gate) {
-        // the gate and everything after a segment are on the critical path;
-        // the streaming waves that share the SIMDs mostly wait on memory
-        __builtin_amdgcn_s_setprio(3);
-        gate_role<BF16, MB>(p, (int)g, sm.g);
-        return;
-    }
-    const int64_t sb = g - p.n_gate;
-    const int64_t row = sb / p.nseg;
-    segment_of<BF16, NV>(p, row, (int)(sb % p.nseg), sm.c);
-    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
-    __builtin_amdgcn_s_setprio(3);
-    if (tid == 0) reset_counter(&p.row_cnt[row]);
     const int K = p.K, P = p.P, r = p.r;
     // The row's gate H_t: once the gate tile row is complete (its workgroups
     // were dispatched first and never wait; this is almost always so by
@@ -316,6 +304,51 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
         chain_seq<kChainGreedy>(Sq, ids, nullptr, 0.f, P, K, p.out_path + rb, nullptr, p.out_score + b, sm.wk);
     else
         walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+}
+
+// The whole selector in one launch.
+template <bool BF16, int NV, int MB, bool SAMPLE>
+__global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    const int64_t g = blockIdx.x + p.base;
+    if (g < p.n_gate) {
+        // the gate and everything after a segment are on the critical path;
+        // the streaming waves that share the SIMDs mostly wait on memory
+        __builtin_amdgcn_s_setprio(3);
+        gate_role<BF16, MB>(p, (int)g, sm.g);
+        return;
+    }
+    const int64_t sb = g - p.n_gate;
+    const int64_t row = sb / p.nseg;
+    segment_of<BF16, NV>(p, row, (int)(sb % p.nseg), sm.c);
+    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
+    __builtin_amdgcn_s_setprio(3);
+    if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
+    row_tail<BF16, MB, SAMPLE>(p, row, sm, flag);
+}
+
+// The selector in two launches: k_scan runs the gate slices and the segments
+// (each stores its lists and ends), then k_tail runs row_tail for every row,
+// one workgroup per row.  Each launch is compiled under its own register
+// budget, the scan's without the tail's code.
+template <bool BF16, int NV, int MB>
+__global__ __launch_bounds__(kWG, 5) void k_scan(Params p) {
+    __shared__ SharedAll sm;
+    const int64_t g = blockIdx.x;
+    if (g < p.n_gate) {
+        gate_role<BF16, MB>(p, (int)g, sm.g);
+        return;
+    }
+    const int64_t sb = g - p.n_gate;
+    segment_of<BF16, NV, true>(p, sb / p.nseg, (int)(sb % p.nseg), sm.c);
+}
+
+template <bool BF16, int MB, bool SAMPLE>
+__global__ __launch_bounds__(kWG, 5) void k_tail(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    row_tail<BF16, MB, SAMPLE>(p, (int64_t)blockIdx.x, sm, flag);
 }
 
 // Top-K alone: segments, then the row merge on last arrival.
@@ -538,6 +571,7 @@ int cu_count() {
 
 struct Plan {
     Params p;
+    bool two = false;           // scan and tail as two launches
     int nv = 1;
     int mb = 4;                 // gate tile: 16*mb rows x 16*(mb == 1 ? 4 : 2) columns
     bool bf16 = true;
@@ -693,6 +727,14 @@ void launch_select(const Plan& pl, hipStream_t stream) {
     dim3 block(kWG);
 #define DF2_SEL_W(BF, NV_, MB_, SM)                                                            \
     do {                                                                                       \
+        if (pl.two) {                                                                          \
+            hipLaunchKernelGGL((k_scan<BF, NV_, MB_>),                                         \
+                               dim3((unsigned)(pl.p.n_gate + pl.n_chunk_blocks)), block, 0,    \
+                               stream, pl.p);                                                  \
+            hipLaunchKernelGGL((k_tail<BF, MB_, SM>), dim3((unsigned)pl.p.rows), block, 0,     \
+                               stream, pl.p);                                                  \
+            break;                                                                             \
+        }                                                                                      \
         if (split)                                                                             \
             hipLaunchKernelGGL((k_select<BF, NV_, MB_, SM>), dim3((unsigned)pl.p.n_gate), block, \
                                0, stream, p1);                                                 \
@@ -800,13 +842,18 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = bf16;
     plan_gate(pl, rows, dims->d, dims->r);
-    // About two and a half segment workgroups per CU, within what the gate
+    // Two launches (k_scan, then k_tail) unless DF2_SPLIT=0 asks for the
+    // single fused launch.  Segment workgroups: about three per CU for the
+    // scan launch, two and a half for the fused one, within what the gate
     // leaves of one resident wave of workgroups.  Measured at V = 151936,
-    // d = 5120 (bf16): 2 segments per row at batch 32 (448 workgroups) beat 3
-    // by 1.5 us and 1 by 1.4 us; 11 to 14 per row at batch 8 beat 16 by
-    // 4 us.
+    // d = 5120 (bf16): two launches at batch 32 ran 35.2 us per cycle with 3
+    // segments per row against 36.3 with 2; the fused launch ran 2 per row
+    // 1.5 us faster than 3 (and 11 to 14 per row at batch 8 4 us faster than
+    // 16).
+    pl.two = env_int("DF2_SPLIT", 1) != 0;
     const int64_t cap = select_capacity();
-    const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, (5 * (int64_t)cu_count()) / 2);
+    const int64_t cus = cu_count();
+    const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, pl.two ? 3 * cus : (5 * cus) / 2);
     plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target));
     if (pl.p.n_gate + pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "problem too large");
     plan_layout(pl, rows, rows, dims->B, true);

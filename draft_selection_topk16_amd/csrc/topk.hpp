@@ -206,9 +206,41 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
 // a time, one per lane; every rank is counted from registers (readlane over
 // the candidates and over the list), then the words whose rank is below K
 // are scattered through LDS.
+// LDSR: ranks are counted from broadcast LDS reads of the other words
+// (independent of each other) instead of readlanes (a dependent chain); it
+// needs more registers and is used where the kernel has them to spare.
+template <bool LDSR>
 __device__ __forceinline__ uint64_t list_merge(uint64_t tk, const uint64_t* c, int m, int K,
                                                WaveLds& sm) {
     const int lane = lane_id();
+    if constexpr (LDSR) {
+        sm.L2[lane] = (lane < K) ? tk : 0ull;
+        wave_sync();
+        for (int base = 0; base < m; base += 64) {
+            const int mg = min(64, m - base);
+            const uint64_t ci = (lane < mg) ? c[base + lane] : 0ull;
+            int rc = 0;         // candidates above ci
+            int rl = lane;      // new rank of the list word tk
+#pragma unroll 8
+            for (int i = 0; i < mg; ++i) {
+                const uint64_t x = c[base + i];
+                rc += (x > ci) ? 1 : 0;
+                rl += (x > tk) ? 1 : 0;
+            }
+            int rk = 0;         // list words above ci
+#pragma unroll 8
+            for (int k = 0; k < K; ++k) rk += (sm.L2[k] > ci) ? 1 : 0;
+            wave_sync();
+            sm.L2[lane] = 0ull;
+            wave_sync();
+            if (lane < K && tk != 0 && rl < K) sm.L2[rl] = tk;
+            if (lane < mg && rc + rk < K) sm.L2[rc + rk] = ci;
+            wave_sync();
+            tk = (lane < K) ? sm.L2[lane] : 0ull;
+        }
+        wave_sync();
+        return tk;
+    }
     wave_sync();
     for (int base = 0; base < m; base += 64) {
         const int mg = min(64, m - base);
@@ -235,7 +267,7 @@ __device__ __forceinline__ uint64_t list_merge(uint64_t tk, const uint64_t* c, i
 
 // Keys the wave's pending vectors and merges every word that beats the K-th
 // kept word (and reaches Tm) into the sorted list tk.
-template <bool BF16>
+template <bool BF16, bool LDSR = false>
 __device__ uint64_t flush_pending(int V, int K, uint32_t Tm, uint64_t tk, int np, WaveLds& sm) {
     using E = Elem<BF16>;
     constexpr int PV = E::kPerVec;
@@ -263,13 +295,13 @@ __device__ uint64_t flush_pending(int V, int K, uint32_t Tm, uint64_t tk, int np
         if (pred) sm.cand[n + __popcll(b2 & ((1ull << lane) - 1ull))] = word;
         n += __popcll(b2);
         if (n > kWCand - 64) {
-            tk = list_merge(tk, sm.cand, n, K, sm);
+            tk = list_merge<LDSR>(tk, sm.cand, n, K, sm);
             n = 0;
             kth = readlane_u64(tk, K - 1);
             Tm = max(Tm, (uint32_t)(kth >> 32));
         }
     }
-    if (n > 0) tk = list_merge(tk, sm.cand, n, K, sm);
+    if (n > 0) tk = list_merge<LDSR>(tk, sm.cand, n, K, sm);
     wave_sync();            // the pending slots are rewritten next
     return tk;
 }
@@ -280,7 +312,7 @@ __device__ uint64_t flush_pending(int V, int K, uint32_t Tm, uint64_t tk, int np
 //   hold element eb + (j * 64 + l) * kPerVec + p.
 //   trow: a key that at least K values of the row are known to reach (the
 //   best K-th kept key among the workgroup's waves; 0 if none known).
-template <bool BF16, int NV, bool ALIGNED>
+template <bool BF16, int NV, bool ALIGNED, bool LDSR = false>
 __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV], uint64_t tk,
                                uint32_t trow, int& np, WaveLds& sm) {
     using E = Elem<BF16>;
@@ -318,7 +350,7 @@ __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV
         const uint64_t bal = __ballot(vin);
         if (bal == 0) continue;
         if (np + __popcll(bal) > kWPend) {
-            tk = flush_pending<BF16>(V, K, Tm, tk, np, sm);
+            tk = flush_pending<BF16, LDSR>(V, K, Tm, tk, np, sm);
             np = 0;
         }
         if (vin) {
@@ -339,7 +371,7 @@ __device__ uint64_t wave_chunk(int V, int64_t eb, int K, const u32x4_t (&raw)[NV
 //   row: first element of the row; V: row length; K <= 64.
 //   ALIGNED: the row start is 16-byte aligned and V is a multiple of kPerVec.
 //   out: 4 x K hand-off words, one sorted list per wave (0 for empty slots).
-template <bool BF16, int NV, bool ALIGNED>
+template <bool BF16, int NV, bool ALIGNED, bool LDSR = false>
 __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, int cs, int nc,
                                   int split, int K, uint64_t* __restrict__ out, ChunkLds& sm) {
     static_assert(NV >= 1 && NV <= kMaxNV, "chunk vectors per lane");
@@ -378,7 +410,7 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     auto settle = [&](bool last) {
         if (npend >= kWPend / 2 || (last && npend > 0)) {
             const uint32_t Tb = max(wg_bound(), 1u);
-            tk = flush_pending<BF16>(V, K, Tb, tk, npend, sm.wv[w]);
+            tk = flush_pending<BF16, LDSR>(V, K, Tb, tk, npend, sm.wv[w]);
             npend = 0;
             if (!last) publish();
         }
@@ -427,14 +459,14 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
     }
     for (int c = 0; c < nc; c += 2) {
         fetch(b1, c + 1);
-        tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c), K, b0, tk, wg_bound(), npend, sm.wv[w]);
+        tk = wave_chunk<BF16, NV, ALIGNED, LDSR>(V, eb_of(c), K, b0, tk, wg_bound(), npend, sm.wv[w]);
         settle(false);
         // Keep the next half's uses of its loads below this point: hoisting
         // one would wait on every load in flight, prefetch included.
         __builtin_amdgcn_sched_barrier(0);
         if (c + 1 >= nc) break;
         fetch(b0, c + 2);
-        tk = wave_chunk<BF16, NV, ALIGNED>(V, eb_of(c + 1), K, b1, tk, wg_bound(), npend, sm.wv[w]);
+        tk = wave_chunk<BF16, NV, ALIGNED, LDSR>(V, eb_of(c + 1), K, b1, tk, wg_bound(), npend, sm.wv[w]);
         settle(false);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -453,15 +485,15 @@ __device__ void segment_topk_impl(const void* __restrict__ row, int V, int c0, i
 //   is a kernel instantiation of its own: kept beside the aligned path, the
 //   compiler emits it as a called function, and the call stack then gives
 //   every workgroup of the launch a private segment.
-template <bool BF16, int NV>
+template <bool BF16, int NV, bool LDSR = false>
 __device__ __forceinline__ void segment_topk(const void* __restrict__ row, int V, int C, int seg,
                                              int nseg, int K, int split,
                                              uint64_t* __restrict__ out, ChunkLds& sm) {
     const int nc = (C - seg + nseg - 1) / nseg;
     if constexpr (NV == 0)
-        segment_topk_impl<BF16, 1, false>(row, V, seg, nseg, nc * split, split, K, out, sm);
+        segment_topk_impl<BF16, 1, false, LDSR>(row, V, seg, nseg, nc * split, split, K, out, sm);
     else
-        segment_topk_impl<BF16, NV, true>(row, V, seg, nseg, nc, 1, K, out, sm);
+        segment_topk_impl<BF16, NV, true, LDSR>(row, V, seg, nseg, nc, 1, K, out, sm);
 }
 
 // Stage 2: top K of one row from its nl sorted segment lists (K words each,
