@@ -191,7 +191,7 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torc
            out_path: Optional[torch.Tensor] = None,
            out_score: Optional[torch.Tensor] = None,
            walk: str = "viterbi") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Selected path [B, P] int32 and its score [B] float32 (one launch);
+    """Selected path [B, P] int32 and its score [B] float32 (one select call);
     walk: "viterbi" (max-sum with backtrack) or "greedy"."""
     return PreparedSelect(logits, hidden, A, Bt, W, prev, K, out_path, out_score, walk)()
 
@@ -199,7 +199,7 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torc
 def select_sample(logits: torch.Tensor, hidden: torch.Tensor, A: torch.Tensor, Bt: torch.Tensor,
                   W: torch.Tensor, prev: torch.Tensor, K: int, u: torch.Tensor,
                   temperature: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Sampling walk in one launch: (path [B, P] int32, q [B, P] float32 =
+    """Sampling walk in one select call: (path [B, P] int32, q [B, P] float32 =
     each drawn token's probability, score [B] float32); u [B, P] float32
     uniforms in [0, 1)."""
     call = PreparedSelect(logits, hidden, A, Bt, W, prev, K, walk="sample", u=u,

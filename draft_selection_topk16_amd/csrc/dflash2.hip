@@ -6,15 +6,18 @@
 // adjacent pair with S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, and walks
 // the scores once from the last verified token.
 //
-// dflash2_select runs everything in ONE launch.  Workgroups are dealt out in
-// index order, and each one's job follows from its index:
+// dflash2_select runs in two launches by default (k_scan, then k_tail), or
+// in one (k_select, with DF2_SPLIT=0).  Workgroups are dealt out in index
+// order, and each one's job follows from its index:
 //   * the first n_gate compute one slice of one gate tile (a partial of H)
 //     and count it on the tile row's counter;
 //   * every other one streams one contiguous vocabulary segment of one
-//     logits row, leaving a sorted list of K candidates, and arrives on the
-//     row's counter.
-// The work after that is handed on by "last arrival": nobody waits for a
-// producer except for the gate, below.
+//     logits row, leaving a sorted list of K candidates; in the single
+//     launch it then arrives on the row's counter, and the last to arrive
+//     goes on with the row (row_tail); in two launches k_scan ends here and
+//     k_tail runs row_tail for every row, one workgroup per row.
+// The work after the segments is handed on by "last arrival": nobody waits
+// for a producer except for the gate, below.
 //   row:      the last segment of a row merges the row's lists into its
 //             top-K (ids and logits) and arrives on the counters of the two
 //             transitions the row takes part in (t - 1 -> t and t -> t + 1);
@@ -306,7 +309,7 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
         walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
-// The whole selector in one launch.
+// The whole selector in one launch (DF2_SPLIT=0).
 template <bool BF16, int NV, int MB, bool SAMPLE>
 __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     __shared__ SharedAll sm;

@@ -334,25 +334,26 @@ def test_select_empty_batch():
 
 @pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1"])
 def test_select_same_result_under_any_segment_plan(name, monkeypatch):
-    """The segment plan (segments per row, chunk width) changes neither the
-    gate sums nor any comparison: candidate words are exact and the merge is
-    independent of how a row was cut, so path and score are bit-identical
-    across plans."""
+    """The segment plan (segments per row, chunk width) and the choice of one
+    fused launch or two (scan, then tail) change neither the gate sums nor
+    any comparison: candidate words are exact and the merge is independent of
+    how a row was cut, so path and score are bit-identical across plans."""
     say("select under segment plans %s" % name)
     x = inputs(name)
     t = to_device(x)
     args = (t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K)
     ref = [a.clone() for a in df2.select(*args)]
     torch.cuda.synchronize()
-    for env in ({"DF2_WGS": "64"}, {"DF2_WGS": "700"}, {"DF2_NV": "1"}, {"DF2_NV": "2", "DF2_WGS": "300"}):
-        for k in ("DF2_WGS", "DF2_NV"):
+    for env in ({"DF2_WGS": "64"}, {"DF2_WGS": "700"}, {"DF2_NV": "1"}, {"DF2_NV": "2", "DF2_WGS": "300"},
+                {"DF2_SPLIT": "0"}, {"DF2_SPLIT": "0", "DF2_WGS": "300"}):
+        for k in ("DF2_WGS", "DF2_NV", "DF2_SPLIT"):
             monkeypatch.delenv(k, raising=False)
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         p, s = df2.select(*args)
         torch.cuda.synchronize()
         assert torch.equal(p, ref[0]) and torch.equal(s, ref[1]), env
-    for k in ("DF2_WGS", "DF2_NV"):
+    for k in ("DF2_WGS", "DF2_NV", "DF2_SPLIT"):
         monkeypatch.delenv(k, raising=False)
 
 
