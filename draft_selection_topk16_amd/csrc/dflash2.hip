@@ -845,16 +845,20 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = bf16;
     plan_gate(pl, rows, dims->d, dims->r);
-    // Two launches (k_scan, then k_tail) unless DF2_SPLIT=0 asks for the
-    // single fused launch.  Segment workgroups: about three per CU for the
-    // scan launch, two and a half for the fused one, within what the gate
-    // leaves of one resident wave of workgroups.  Measured at V = 151936,
-    // d = 5120 (bf16): two launches at batch 32 ran 35.2 us per cycle with 3
-    // segments per row against 36.3 with 2; the fused launch ran 2 per row
-    // 1.5 us faster than 3 (and 11 to 14 per row at batch 8 4 us faster than
-    // 16).
-    pl.two = env_int("DF2_SPLIT", 1) != 0;
+    // Two launches (k_scan, then k_tail) when the gate and one segment per
+    // row fit one resident wave of workgroups; otherwise the single fused
+    // launch, whose row tails overlap the streaming of later waves (B = 256,
+    // P = 15, V = 262144: 490 us fused against 523 us in two launches; at
+    // batch 32, 35.2 us in two launches against 37.8 fused).  DF2_SPLIT=0 or
+    // 1 forces either.  Segment workgroups: about three per CU for the scan
+    // launch, two and a half for the fused one, within what the gate leaves
+    // of one resident wave.  Measured at V = 151936, d = 5120 (bf16): two
+    // launches at batch 32 ran 35.2 us per cycle with 3 segments per row
+    // against 36.3 with 2; the fused launch ran 2 per row 1.5 us faster than
+    // 3 (and 11 to 14 per row at batch 8 4 us faster than 16).
     const int64_t cap = select_capacity();
+    const int split_env = env_int("DF2_SPLIT", -1);
+    pl.two = split_env >= 0 ? split_env != 0 : pl.p.n_gate + rows <= cap;
     const int64_t cus = cu_count();
     const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, pl.two ? 3 * cus : (5 * cus) / 2);
     plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target));

@@ -47,8 +47,10 @@
  *      DF2_S       gate slices of d (1..16)
  *      DF2_GSEP    1: the gate runs as a launch of its own first
  *      DF2_CONV_S  k slices of the convolution's correction GEMM
- *      DF2_SPLIT   0: dflash2_select as a single fused launch (default 1:
- *                  a scan launch, then a tail launch)
+ *      DF2_SPLIT   1: dflash2_select as a scan launch, then a tail launch;
+ *                  0: one fused launch (default: two launches when the gate
+ *                  and one segment per row fit one resident wave of
+ *                  workgroups)
  *    The top-K plan (DF2_WGS, DF2_NV, DF2_MWORDS) never changes a result.
  *    DF2_S and DF2_CONV_S change the fp32 summation order of the gate and
  *    of the corrections (results stay within the documented tolerances,
@@ -106,8 +108,9 @@ typedef struct df2_dims {
 /*
  * The whole selector ("A Lightweight Path Selector": top-K, pair scores, one
  * walk from the last verified token), enqueued as two kernel launches (the
- * vocabulary scan with the gate, then the merges, pair scores and walks), or
- * as one with DF2_SPLIT=0; the results are the same bits either way.
+ * vocabulary scan with the gate, then the merges, pair scores and walks) or,
+ * for batches too large for one resident wave of workgroups, as one fused
+ * launch; the results are the same bits either way.
  *   logits   [B, P, V]   drafter logits U_t
  *   hidden   [B, P, d]   drafter hidden states h_t
  *   A_tab    [V, r]      predecessor embeddings A(.)
