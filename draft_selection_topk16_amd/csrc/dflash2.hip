@@ -155,42 +155,48 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
                             const float (&hown)[2], PairLds& sm) {
     const int tid = threadIdx.x, K = p.K, r = p.r;
     const int64_t rb = (int64_t)b * p.P;
+    // Every load of a thread is issued before any of them is checked, so the
+    // ids, the candidate values and the gate rows cost one round trip
+    // (atomic loads are not hoisted past the id check's branch).  Addresses
+    // are clamped into their buffers and unused values dropped afterwards.
+    const bool prev_row = tid < K;
+    const bool cur_row = tid >= 64 && tid < 64 + ne * K;
+    const int x = cur_row ? tid - 64 : 0, q = x / K, k = x % K;
+    float hv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        const int64_t grow = min(rb + e0 + qq, (int64_t)p.rows - 1);
+        hv[qq][0] = xload(p.Hb + grow * r + min(tid, r - 1));
+        if (r > kWG) hv[qq][1] = xload(p.Hb + grow * r + min(tid + kWG, r - 1));
+    }
+    const int64_t crow = prev_row ? rb + max(e0 - 1, 0) : rb + e0 + q;
+    const int ck = prev_row ? tid : k;
+    int32_t id = xload(p.cand + crow * K + ck);
+    const float uval = xload(p.cval + crow * K + ck);
+    const int32_t pid = xload(p.prev + b);
     // Candidate ids come from the row merges and are always in [0, V); they
     // are still checked, so that no gather can leave the tables.
-    if (tid < K) {
-        int32_t id;
+    if (prev_row) {
         if (e0 > 0) {
-            id = checked_id(xload(p.cand + (rb + e0 - 1) * K + tid), p.V, p.err, 2u);
+            id = checked_id(id, p.V, p.err, 2u);
         } else {
-            id = p.prev[b];
+            id = pid;
             if ((unsigned)id >= (unsigned)p.V) {
                 if (tid == 0) atomicOr(p.err, 1u);
                 id = 0;
             }
         }
         sm.ids[0][tid] = id;
-    } else if (tid >= 64 && tid < 64 + ne * K) {
-        const int x = tid - 64, q = x / K, k = x % K;
-        sm.ids[1 + q][k] = checked_id(xload(p.cand + (rb + e0 + q) * K + k), p.V, p.err, 2u);
-        sm.u[q][k] = xload(p.cval + (rb + e0 + q) * K + k);
-    }
-    // gate rows of the positions, in the same round of loads
-    float hv[2][2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int64_t grow = rb + e0 + q;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int k = tid + u * kWG;
-            hv[q][u] = (grow == own) ? hown[u]
-                                     : ((q < ne && k < r) ? xload(p.Hb + grow * r + k) : 0.f);
-        }
+    } else if (cur_row) {
+        sm.ids[1 + q][k] = checked_id(id, p.V, p.err, 2u);
+        sm.u[q][k] = uval;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            if (q < ne && tid + u * kWG < r) sm.H[q][tid + u * kWG] = hv[q][u];
+            if (qq < ne && tid + u * kWG < r)
+                sm.H[qq][tid + u * kWG] = (rb + e0 + qq == own) ? hown[u] : hv[qq][u];
     __syncthreads();
     pair_tiles<BF16>(p.A, p.Bt, K, r, e0, ne, p.Sb + (rb + e0) * K * K, sm, [] {});
 }

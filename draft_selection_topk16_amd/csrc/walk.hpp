@@ -126,15 +126,9 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
             for (int x = tid; x < (t1 - t0) * KP2; x += kWG) sm.ST[x] = 0.f;
             __syncthreads();
         }
-        // candidate ids (first group) and the group's scores, all loads of a
-        // thread issued before any is stored
+        // the group's scores, all loads of a thread issued before any is
+        // stored
         const int nt = t1 - t0;
-        const bool load_ids = t0 == 0 && ids_lds;
-        constexpr int QI = kWalkIds / kWG;
-        int32_t idv[QI];
-#pragma unroll
-        for (int q = 0; q < QI; ++q)
-            idv[q] = load_ids ? xload(ids + min(q * kWG + tid, P * K - 1)) : 0;
         for (int e = tid; e < KK; e += kWG) {
             const int i = e / K, j = e % K;
             const float* src = S + (int64_t)t0 * KK + e;
@@ -148,16 +142,23 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
                     if (tb + u < nt) dst[(tb + u) * KP2] = v[u];
             }
         }
-        if (load_ids) {
-#pragma unroll
-            for (int q = 0; q < QI; ++q)
-                if (q * kWG + tid < P * K) sm.ids[q * kWG + tid] = idv[q];
-        }
         __syncthreads();
         if (w == 0) {
             if (KP == 16) delta = walk_steps<16>(t0, t1, K, delta, sm);
             else if (KP == 32) delta = walk_steps<32>(t0, t1, K, delta, sm);
             else delta = walk_steps<64>(t0, t1, K, delta, sm);
+        } else if (t0 == 0 && ids_lds) {
+            // the other waves bring the candidate ids into LDS meanwhile, so
+            // their round trip is off the walk's path
+            constexpr int NW = kWG - 64;
+            constexpr int QI = (kWalkIds + NW - 1) / NW;
+            int32_t idv[QI];
+#pragma unroll
+            for (int q = 0; q < QI; ++q)
+                idv[q] = q * NW + tid - 64 < P * K ? xload(ids + q * NW + tid - 64) : 0;
+#pragma unroll
+            for (int q = 0; q < QI; ++q)
+                if (q * NW + tid - 64 < P * K) sm.ids[q * NW + tid - 64] = idv[q];
         }
         __syncthreads();
     }
