@@ -320,6 +320,22 @@ def test_select_edge_shapes(B, P, V, K, d, dtype):
     check_select(path, score, run_oracle(x), TOL[dtype], "edge")
 
 
+@pytest.mark.parametrize("r", [320, 512])
+@pytest.mark.parametrize("split", ["0", "1"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_select_wide_gate(r, split, dtype, monkeypatch):
+    """Gate ranks above one value per thread (r > 256, up to the 512 the
+    library accepts): the row merge sums a second gate value per thread, the
+    pair job loads a second one per position and takes 16 k steps, in the
+    fused launch and in the two-launch path."""
+    say("select wide gate %s r=%d split=%s" % (dtype, r, split))
+    monkeypatch.setenv("DF2_SPLIT", split)
+    wl = synth.Workload("wide", 1, B=3, P=5, V=3000, d=128, K=16, r=r, dtype=dtype, pair_scale=4.0)
+    x = synth.make_inputs(wl, seed=r + 7)
+    path, score = gpu_select(x)
+    check_select(path, score, run_oracle(x), TOL[dtype], "wide gate")
+
+
 def test_select_empty_batch():
     say("select empty batch")
     dev = "cuda"
