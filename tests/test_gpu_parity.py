@@ -135,7 +135,8 @@ def test_project_workloads(name):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,d,r", [(1, 32, 64), (17, 96, 128), (64, 64, 64), (300, 512, 256), (3840, 256, 256)])
+@pytest.mark.parametrize("M,d,r", [(1, 32, 64), (17, 96, 128), (64, 64, 64), (300, 512, 256), (3840, 256, 256),
+                                   (17, 96, 320), (40, 256, 512)])
 def test_project_shapes(dtype, M, d, r):
     say("project shape %s M=%d d=%d r=%d" % (dtype, M, d, r))
     rng = np.random.default_rng(M + d + r)
@@ -152,7 +153,9 @@ def test_project_shapes(dtype, M, d, r):
 # ------------------------------------------------------------- pair scores
 @pytest.mark.parametrize("name,kw", [("tiny_f32", {}), ("qwen3_4b_b1", {}),
                                      ("t27b_b8", {"pair_scale": 8.0}),
-                                     ("stress_b256", {"B": 3, "V": 20000, "d": 256})])
+                                     ("stress_b256", {"B": 3, "V": 20000, "d": 256}),
+                                     ("tiny_f32", {"r": 320, "V": 4000}),
+                                     ("qwen3_4b_b1", {"r": 512, "V": 20000})])
 def test_pair_scores_stage(name, kw):
     x = inputs(name, **kw)
     say("pair_scores %s %s" % (name, kw))
