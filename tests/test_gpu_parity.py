@@ -351,12 +351,14 @@ def test_select_empty_batch():
     assert path.shape == (0, 7) and score.shape == (0,)
 
 
-@pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1"])
+@pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1", "stress_b256"])
 def test_select_same_result_under_any_segment_plan(name, monkeypatch):
     """The segment plan (segments per row, chunk width) and the choice of one
     fused launch or two (scan, then tail) change neither the gate sums nor
     any comparison: candidate words are exact and the merge is independent of
-    how a row was cut, so path and score are bit-identical across plans."""
+    how a row was cut, so path and score are bit-identical across plans.  The
+    stress workload defaults to the fused launch; forcing two launches there
+    gives a tail grid of 3840 rows, more than one resident wave."""
     say("select under segment plans %s" % name)
     x = inputs(name)
     t = to_device(x)
@@ -364,7 +366,8 @@ def test_select_same_result_under_any_segment_plan(name, monkeypatch):
     ref = [a.clone() for a in df2.select(*args)]
     torch.cuda.synchronize()
     for env in ({"DF2_WGS": "64"}, {"DF2_WGS": "700"}, {"DF2_NV": "1"}, {"DF2_NV": "2", "DF2_WGS": "300"},
-                {"DF2_SPLIT": "0"}, {"DF2_SPLIT": "0", "DF2_WGS": "300"}):
+                {"DF2_SPLIT": "0"}, {"DF2_SPLIT": "0", "DF2_WGS": "300"},
+                {"DF2_SPLIT": "1"}, {"DF2_SPLIT": "1", "DF2_WGS": "300"}):
         for k in ("DF2_WGS", "DF2_NV", "DF2_SPLIT"):
             monkeypatch.delenv(k, raising=False)
         for k, v in env.items():
