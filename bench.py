@@ -256,8 +256,8 @@ def copy_calibration(mb: float, reps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="t27b_b32")
     ap.add_argument("--b1-workload", default="qwen3_4b_b1")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
