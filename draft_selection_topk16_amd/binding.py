@@ -21,10 +21,15 @@ DF2_BF16 = 1
 # df2_walk
 WALKS = {"viterbi": 0, "greedy": 1}
 
+# df2_plan_knob
+PLAN_KNOBS = {"segment_wgs": 0, "chunk_vectors": 1, "merge_words": 2, "gate_slices": 3,
+              "conv_slices": 4, "launches": 5}
+
 EXPORTED = (
     "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_topk",
     "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
-    "dflash2_sample_walk", "dflash2_conv2", "dflash2_device_error", "dflash2_release",
+    "dflash2_sample_walk", "dflash2_conv2", "dflash2_device_error", "dflash2_plan_override",
+    "dflash2_release",
     "dflash2_status_string",
     "dflash2_last_error", "dflash2_version",
 )
@@ -71,6 +76,7 @@ def load() -> ctypes.CDLL:
         "dflash2_sample_walk": [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp],
         "dflash2_conv2": [vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp],
         "dflash2_device_error": [vp, u32p],
+        "dflash2_plan_override": [ctypes.c_int, i32],
         "dflash2_release": [],
     }
     for name, args in sig.items():
@@ -311,6 +317,31 @@ def device_error(device: Optional[torch.device] = None) -> int:
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     _check(lib.dflash2_device_error(_stream(dev), ctypes.byref(flags)))
     return int(flags.value)
+
+
+def plan_override(knob: str, value: int) -> None:
+    """Pins one launch-plan knob for later calls (0 = automatic); for
+    measurement and plan-invariance tests."""
+    if knob not in PLAN_KNOBS:
+        raise ValueError("knob must be one of %s" % sorted(PLAN_KNOBS))
+    _check(load().dflash2_plan_override(PLAN_KNOBS[knob], int(value)))
+
+
+class plan:
+    """Context manager: plan knobs pinned inside, automatic again after."""
+
+    def __init__(self, **knobs):
+        self.knobs = knobs
+
+    def __enter__(self):
+        for k, v in self.knobs.items():
+            plan_override(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k in self.knobs:
+            plan_override(k, 0)
+        return False
 
 
 def release() -> None:

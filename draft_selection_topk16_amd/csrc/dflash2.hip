@@ -7,7 +7,7 @@
 // the scores once from the last verified token.
 //
 // dflash2_select runs in two launches by default (k_scan, then k_tail), or
-// in one (k_select, with DF2_SPLIT=0).  Workgroups are dealt out in index
+// in one (k_select), as the plan decides.  Workgroups are dealt out in index
 // order, and each one's job follows from its index:
 //   * the first n_gate compute one slice of one gate tile (a partial of H)
 //     and count it on the tile row's counter;
@@ -90,7 +90,6 @@ struct Params {
     int gm_rows;          // rows per gate tile
     int mtiles, ntiles, S, n_gate;
     int64_t n_chunk;      // segment workgroups (rows * nseg)
-    int64_t base;         // index of the launch's first workgroup
     int walk;             // kWalkViterbi, kWalkGreedy or kWalkSample
     const float* u;       // [B, P] uniforms of the sampling walk
     float* out_q;         // [B, P] probabilities of the sampled choices
@@ -315,12 +314,12 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
         walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
-// The whole selector in one launch (DF2_SPLIT=0).
+// The whole selector in one launch.
 template <bool BF16, int NV, int MB, bool SAMPLE>
 __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
-    const int64_t g = blockIdx.x + p.base;
+    const int64_t g = blockIdx.x;
     if (g < p.n_gate) {
         // the gate and everything after a segment are on the critical path;
         // the streaming waves that share the SIMDs mostly wait on memory
@@ -536,9 +535,21 @@ void note_layout(hipStream_t stream, size_t counter_bytes) {
     if (it != g_scratch.end()) it->second.zeroed_counter_bytes = counter_bytes;
 }
 
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
+// Plan overrides for measurement (dflash2_plan_override); 0 = automatic.
+// Set only through the C ABI: the library never reads the environment.
+struct Overrides {
+    int wgs = 0;          // target count of top-K segment workgroups
+    int nv = 0;           // 16-byte vectors per lane per chunk (1, 2 or 4)
+    int mwords = 0;       // most candidate words one row merge takes (<= 1024)
+    int gate_s = 0;       // gate slices of d (1..16)
+    int conv_s = 0;       // k slices of the convolution's correction GEMM
+    int launches = 0;     // dflash2_select: 1 = one fused launch, 2 = scan then tail
+};
+Overrides g_over;
+
+Overrides overrides() {
+    std::lock_guard<std::mutex> lock(g_mu);
+    return g_over;
 }
 
 // Workgroups of the select kernel that are resident at once on the current
@@ -596,7 +607,7 @@ struct Plan {
 // that about `target` workgroups stream in total; a row's segment lists
 // must fit one merge.
 void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits,
-               int64_t target) {
+               int64_t target, const Overrides& ov) {
     Params& p = pl.p;
     pl.bf16 = bf16;
     const int pv = bf16 ? 8 : 4;
@@ -609,15 +620,16 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
             if (rows * chunks(cand) >= 256) { nv = cand; break; }
         }
     }
-    const int forced = env_int("DF2_NV", 0);
-    if (forced == 1 || forced == 2 || forced == 4) nv = forced;
+    if (ov.nv == 1 || ov.nv == 2 || ov.nv == 4) nv = ov.nv;
     pl.nv = nv;
     p.split = nv;
     p.C = chunks(nv);
-    target = std::max<int64_t>(1, env_int("DF2_WGS", (int)std::min<int64_t>(target, 1 << 30)));
+    if (ov.wgs > 0) target = ov.wgs;
+    target = std::max<int64_t>(1, std::min<int64_t>(target, 1 << 30));
     // at most kMergeMax words per row merge; fewer lists also make the merge
     // bound sharper
-    const int max_segs = std::max(1, std::min(kMergeMax, env_int("DF2_MWORDS", 1024)) / (kWaves * K));
+    const int mwords = ov.mwords > 0 ? std::min(kMergeMax, ov.mwords) : kMergeMax;
+    const int max_segs = std::max(1, mwords / (kWaves * K));
     int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, target / rows));
     p.nseg = std::min(nseg, max_segs);
     p.rows = rows;
@@ -638,7 +650,7 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
 // beside the streaming segments, but past one per CU the gate's workgroups
 // take slots and issue cycles from the streaming.  The standalone
 // projection uses the same slices, so both paths round alike.
-void plan_gate(Plan& pl, int64_t M, int d, int r) {
+void plan_gate(Plan& pl, int64_t M, int d, int r, const Overrides& ov) {
     Params& p = pl.p;
     pl.mb = (M <= 16) ? 1 : 4;
     const int nb = (pl.mb == 1) ? 4 : 2;
@@ -652,8 +664,7 @@ void plan_gate(Plan& pl, int64_t M, int d, int r) {
     // cycle with 8 slices against 41.0 with 16, batch 8 keeps 16 (its rows
     // are ready sooner, so its gate must end sooner)
     S = std::min(S, std::max(4, cu_count() / (p.mtiles * p.ntiles)));
-    const int forced = env_int("DF2_S", 0);
-    if (forced >= 1 && forced <= std::min(KS, kMaxFusedSlices)) S = forced;
+    if (ov.gate_s >= 1 && ov.gate_s <= std::min(KS, kMaxFusedSlices)) S = ov.gate_s;
     p.S = S;
     p.n_gate = p.mtiles * p.ntiles * S;
     p.d = d;
@@ -726,13 +737,9 @@ df2_status launch_checked(F&& f, const char* what) {
     return DF2_OK;
 }
 
-// The gate can run as a launch of its own, before the segments (every pair
-// job then finds H complete), or inside the same launch.
+// One fused launch (k_select), or the scan launch and then the tail launch.
 void launch_select(const Plan& pl, hipStream_t stream) {
-    const bool split = env_int("DF2_GSEP", 0) != 0;
-    Params p1 = pl.p, p2 = pl.p;
-    p2.base = split ? pl.p.n_gate : 0;
-    const int64_t n2 = split ? pl.n_chunk_blocks : pl.p.n_gate + pl.n_chunk_blocks;
+    const int64_t n2 = pl.p.n_gate + pl.n_chunk_blocks;
     dim3 block(kWG);
 #define DF2_SEL_W(BF, NV_, MB_, SM)                                                            \
     do {                                                                                       \
@@ -744,11 +751,8 @@ void launch_select(const Plan& pl, hipStream_t stream) {
                                stream, pl.p);                                                  \
             break;                                                                             \
         }                                                                                      \
-        if (split)                                                                             \
-            hipLaunchKernelGGL((k_select<BF, NV_, MB_, SM>), dim3((unsigned)pl.p.n_gate), block, \
-                               0, stream, p1);                                                 \
         hipLaunchKernelGGL((k_select<BF, NV_, MB_, SM>), dim3((unsigned)n2), block, 0, stream,  \
-                           p2);                                                                \
+                           pl.p);                                                              \
     } while (0)
 #define DF2_SEL(BF, NV_, MB_)                                     \
     do {                                                          \
@@ -847,27 +851,27 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     if (!bf16 && ((uintptr_t)logits & 3u)) return fail(DF2_EINVAL, "fp32 logits must be 4-byte aligned");
     if (bf16 && ((uintptr_t)logits & 1u)) return fail(DF2_EINVAL, "bf16 logits must be 2-byte aligned");
     const int64_t rows = (int64_t)dims->B * dims->P;
+    const Overrides ov = overrides();
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = bf16;
-    plan_gate(pl, rows, dims->d, dims->r);
+    plan_gate(pl, rows, dims->d, dims->r, ov);
     // Two launches (k_scan, then k_tail) when the gate and one segment per
     // row fit one resident wave of workgroups; otherwise the single fused
     // launch, whose row tails overlap the streaming of later waves (B = 256,
     // P = 15, V = 262144: 490 us fused against 523 us in two launches; at
-    // batch 32, 35.2 us in two launches against 37.8 fused).  DF2_SPLIT=0 or
-    // 1 forces either.  Segment workgroups: about three per CU for the scan
+    // batch 32, 35.2 us in two launches against 37.8 fused).  The launches
+    // plan knob forces either.  Segment workgroups: about three per CU for the scan
     // launch, two and a half for the fused one, within what the gate leaves
     // of one resident wave.  Measured at V = 151936, d = 5120 (bf16): two
     // launches at batch 32 ran 35.2 us per cycle with 3 segments per row
     // against 36.3 with 2; the fused launch ran 2 per row 1.5 us faster than
     // 3 (and 11 to 14 per row at batch 8 4 us faster than 16).
     const int64_t cap = select_capacity();
-    const int split_env = env_int("DF2_SPLIT", -1);
-    pl.two = split_env >= 0 ? split_env != 0 : pl.p.n_gate + rows <= cap;
+    pl.two = ov.launches ? ov.launches == 2 : pl.p.n_gate + rows <= cap;
     const int64_t cus = cu_count();
     const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, pl.two ? 3 * cus : (5 * cus) / 2);
-    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target));
+    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target), ov);
     if (pl.p.n_gate + pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "problem too large");
     plan_layout(pl, rows, rows, dims->B, true);
     Params& p = pl.p;
@@ -961,7 +965,7 @@ df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V, df2_dtype d
         return fail(DF2_EINVAL, "logits misaligned for its dtype");
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
-    plan_topk(pl, rows, V, K, bf16, logits, select_capacity());
+    plan_topk(pl, rows, V, K, bf16, logits, select_capacity(), overrides());
     if (pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "too many rows");
     pl.p.S = 1;
     plan_layout(pl, rows, 0, 0, false);
@@ -994,7 +998,7 @@ df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M, int32
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = dtype == DF2_BF16;
-    plan_gate(pl, M, d, r);
+    plan_gate(pl, M, d, r, overrides());
     pl.p.C = 0;
     pl.p.K = 0;
     plan_layout(pl, 0, M, 0, false);
@@ -1137,7 +1141,8 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base, co
     Plan pl;
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = dtype == DF2_BF16;
-    plan_gate(pl, M, d, N);
+    const Overrides ov = overrides();
+    plan_gate(pl, M, d, N, ov);
     {
         // fewer, longer slices than the selector's: the last slice of a tile
         // sums them all (measured best: 4 with 64-row tiles, B = 32,
@@ -1145,7 +1150,7 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base, co
         // slice allows, 10 at B = 1, d = 2560: 11.0 us against 13.0 with 4)
         const int KS = d / 32;
         const int s_def = pl.mb == 1 ? 16 : 4;
-        int S = std::max(1, std::min(env_int("DF2_CONV_S", s_def), KS / (kWaves * gate_kb(pl.bf16))));
+        int S = std::max(1, std::min(ov.conv_s > 0 ? ov.conv_s : s_def, KS / (kWaves * gate_kb(pl.bf16))));
         pl.p.S = S;
     }
     const int ntiles_total = pl.p.mtiles * pl.p.ntiles;
@@ -1203,8 +1208,37 @@ df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {
         const uint32_t zero = 0;
         if ((e = hipMemcpy(ptr, &zero, 4, hipMemcpyHostToDevice)) != hipSuccess)
             return hip_fail(e, "hipMemcpy flags");
+        // A raised flag may come from a launch that left arrival counters
+        // behind (a gate wait that gave up): the next call on this stream
+        // clears its whole counter prefix before it launches.
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_scratch.find(std::make_pair(dev, stream));
+        if (it != g_scratch.end()) it->second.zeroed_counter_bytes = 0;
     }
     *flags = v;
+    return DF2_OK;
+}
+
+df2_status dflash2_plan_override(df2_plan_knob knob, int32_t value) {
+    g_last_error.clear();
+    if (value < 0) return fail(DF2_EINVAL, "override values are >= 0 (0 restores the automatic plan)");
+    std::lock_guard<std::mutex> lock(g_mu);
+    switch (knob) {
+        case DF2_PLAN_SEGMENT_WGS: g_over.wgs = value; break;
+        case DF2_PLAN_CHUNK_VECTORS:
+            if (value != 0 && value != 1 && value != 2 && value != 4)
+                return fail(DF2_EINVAL, "chunk vectors must be 0, 1, 2 or 4");
+            g_over.nv = value;
+            break;
+        case DF2_PLAN_MERGE_WORDS: g_over.mwords = value; break;
+        case DF2_PLAN_GATE_SLICES: g_over.gate_s = value; break;
+        case DF2_PLAN_CONV_SLICES: g_over.conv_s = value; break;
+        case DF2_PLAN_LAUNCHES:
+            if (value > 2) return fail(DF2_EINVAL, "launches must be 0, 1 or 2");
+            g_over.launches = value;
+            break;
+        default: return fail(DF2_EINVAL, "unknown plan knob");
+    }
     return DF2_OK;
 }
 

@@ -39,22 +39,12 @@
  *  - Top-K order: value descending; equal values (IEEE, -0 == +0) go to the
  *    lower vocabulary index.  Walk ties go to the smaller predecessor rank,
  *    the final pick to the smaller rank.
- *  - The launch plan is chosen from the shapes and the device; environment
- *    variables, read at every call, override it for measurement:
- *      DF2_WGS     target count of top-K segment workgroups
- *      DF2_NV      16-byte vectors per lane per chunk (1, 2 or 4)
- *      DF2_MWORDS  most candidate words one row merge takes (<= 1024)
- *      DF2_S       gate slices of d (1..16)
- *      DF2_GSEP    1: the gate runs as a launch of its own first
- *      DF2_CONV_S  k slices of the convolution's correction GEMM
- *      DF2_SPLIT   1: dflash2_select as a scan launch, then a tail launch;
- *                  0: one fused launch (default: two launches when the gate
- *                  and one segment per row fit one resident wave of
- *                  workgroups)
- *    The top-K plan (DF2_WGS, DF2_NV, DF2_MWORDS) never changes a result.
- *    DF2_S and DF2_CONV_S change the fp32 summation order of the gate and
- *    of the corrections (results stay within the documented tolerances,
- *    and dflash2_project keeps matching dflash2_select bit for bit).
+ *  - The launch plan is chosen from the shapes and the device.  It can be
+ *    overridden for measurement only through dflash2_plan_override(); the
+ *    library never reads the environment.  The top-K plan never changes a
+ *    result; the gate and convolution slice counts change the fp32 summation
+ *    order of H and of the corrections (within the documented tolerances;
+ *    dflash2_project keeps matching dflash2_select bit for bit).
  */
 #ifndef DFLASH2_H
 #define DFLASH2_H
@@ -82,6 +72,16 @@ typedef enum { DF2_F32 = 0, DF2_BF16 = 1 } df2_dtype;
  *                     S_t, added in order of t.
  */
 typedef enum { DF2_WALK_VITERBI = 0, DF2_WALK_GREEDY = 1 } df2_walk;
+
+/* Plan knobs that dflash2_plan_override() can pin (0 = automatic). */
+typedef enum {
+    DF2_PLAN_SEGMENT_WGS = 0,   /* target count of top-K segment workgroups */
+    DF2_PLAN_CHUNK_VECTORS = 1, /* 16-byte vectors per lane per chunk: 1, 2 or 4 */
+    DF2_PLAN_MERGE_WORDS = 2,   /* most candidate words one row merge takes (<= 1024) */
+    DF2_PLAN_GATE_SLICES = 3,   /* slices of d of the gate projection (<= 16) */
+    DF2_PLAN_CONV_SLICES = 4,   /* k slices of the convolution's correction GEMM */
+    DF2_PLAN_LAUNCHES = 5       /* dflash2_select: 1 = one fused launch, 2 = scan then tail */
+} df2_plan_knob;
 
 typedef enum {
     DF2_OK = 0,
@@ -273,6 +273,15 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base,
  * are then unreliable).  Returns DF2_OK, or DF2_EHIP.
  */
 df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags);
+
+/*
+ * Pins one plan knob for every later call of this process (value 0 restores
+ * the automatic choice), for measurement and plan-invariance tests.  Values
+ * out of a knob's range are clamped to what the shapes allow.  Returns
+ * DF2_EINVAL for an unknown knob or a negative value.  Not for use while
+ * another thread is enqueueing selector work.
+ */
+df2_status dflash2_plan_override(df2_plan_knob knob, int32_t value);
 
 /* Frees every scratch buffer the library holds (call with no work in flight). */
 df2_status dflash2_release(void);

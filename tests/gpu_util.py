@@ -1,9 +1,16 @@
 """Helpers for the GPU parity tests: device copies of seeded inputs and the
 acceptance rule against the oracle.
 
-Tolerances (relative, against the scale sigma = |U| + sum_q |A H B| of each
-score, summed along the path for path scores): 1e-5 for fp32 inputs, 2e-2 for
-bf16 inputs.  Top-K indices and values must match exactly.  A selected path
+Tolerances are relative, against the scale sigma = |U| + sum_q |A H B| of
+each score (summed along the path for path scores).  The acceptance bound
+of the task is 1e-5 for fp32 inputs and 2e-2 for bf16 inputs (TOL_ACCEPT).
+The tests apply the tighter bound the arithmetic allows (TOL): 1e-5 for fp32
+and 1e-4 for bf16.  With bf16 tables G = A (.) H enters the matrix cores as a
+bf16 high plus a bf16 low part, a relative error near 2^-16 per product,
+and H and S are fp32 sums, a few 1e-6 of sigma; 1e-4 keeps a factor of
+about three over that sum and stays inside the acceptance bound, so a
+walk that returned a near-best path on a sequence with a clear margin
+fails.  Top-K indices and values must match exactly.  A selected path
 may differ from the oracle's only where the oracle's best-versus-second
 margin is within the tolerance, and then the oracle's own score of the GPU
 path must be within the tolerance of the best score.  For the greedy walk the
@@ -28,8 +35,10 @@ import torch
 import oracle
 from draft_selection_topk16_amd import synth
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
-TOL_SAMPLE = {"f32": 1e-5, "bf16": 1e-4}
+TOL_ACCEPT = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 1e-4}
+TOL_SAMPLE = TOL
+assert all(TOL[k] <= TOL_ACCEPT[k] for k in TOL)
 
 
 def say(*a):
@@ -52,10 +61,31 @@ def to_device(x: synth.Inputs, device="cuda"):
                 prev=torch.from_numpy(np.ascontiguousarray(x.prev)).to(device))
 
 
-def run_oracle(x: synth.Inputs, seqs=None):
-    f = x.f64()
-    return oracle.select(f["logits"], f["hidden"], f["A"], f["Bt"], f["W"], f["prev"],
-                         x.wl.K, seqs=seqs)
+def run_oracle(x: synth.Inputs, seqs=None, u=None, tau: float = 1.0, threads: int = 1):
+    """oracle.select on the workload (or the sequences `seqs`).  With
+    threads > 1 the sequences are split over a host thread pool (the oracle's
+    C calls release the GIL), each thread widening only its own logits, and
+    the per-sequence results are concatenated in sequence order."""
+    dt = x.wl.dtype
+    seqs = np.arange(x.wl.B) if seqs is None else np.asarray(seqs)
+    shared = dict(hidden=synth.to_f64(x.hidden, dt), A=synth.to_f64(x.A, dt), Bt=synth.to_f64(x.Bt, dt),
+                  W=synth.to_f64(x.W, dt))
+    uu = None if u is None else np.asarray(u)
+
+    def work(q):
+        return oracle.select(synth.to_f64(x.logits[q], dt), shared["hidden"][q], shared["A"], shared["Bt"],
+                             shared["W"], x.prev[q], x.wl.K, u=None if uu is None else uu[q], tau=tau)
+
+    if threads <= 1 or len(seqs) < 2:
+        return work(seqs)
+    from concurrent.futures import ThreadPoolExecutor
+    parts = np.array_split(seqs, min(threads, len(seqs)))
+    with ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        outs = list(ex.map(work, parts))
+    res = {}
+    for k, v in outs[0].items():
+        res[k] = np.concatenate([o[k] for o in outs], axis=0) if isinstance(v, np.ndarray) and v.ndim else v
+    return res
 
 
 def path_score_under_oracle(o, b, path):
@@ -73,25 +103,32 @@ def path_score_under_oracle(o, b, path):
 
 
 def check_select(path, score, o, tol, label=""):
-    """Apply the acceptance rule; returns the number of tolerated mismatches."""
+    """Apply the acceptance rule; returns the number of tolerated mismatches
+    (only sequences whose best-versus-second margin is within tol * sigma
+    may differ; how many that allows is in every message)."""
     path = np.asarray(path)
     score = np.asarray(score, dtype=np.float64)
     mism = 0
     worst = 0.0
-    for b in range(path.shape[0]):
+    n = path.shape[0]
+    close = int(np.sum(o["margin"] <= tol * o["sigma_path"]))
+    for b in range(n):
         sp = o["sigma_path"][b]
         if not np.array_equal(path[b], o["path"][b]):
             mism += 1
             assert o["margin"][b] <= tol * sp, (
-                "%s seq %d: path differs but margin %.3g > tol*sigma %.3g" % (label, b, o["margin"][b], tol * sp))
+                "%s seq %d: path differs but margin %.3g > tol*sigma %.3g (paths equal so far %d of %d; "
+                "%d sequences have a margin within tol)" % (label, b, o["margin"][b], tol * sp, b - mism + 1, b + 1,
+                                                           close))
             s = path_score_under_oracle(o, b, path[b])
             assert s >= o["score"][b] - tol * sp, (label, b, s, o["score"][b])
         err = abs(score[b] - o["score"][b]) / max(abs(o["score"][b]), sp)
         worst = max(worst, err)
         assert err <= tol, "%s seq %d: score %.9g vs oracle %.9g (rel %.3g)" % (
             label, b, score[b], o["score"][b], err)
-    say("  %s: %d sequences, %d tolerated path mismatches, worst score rel err %.3g"
-        % (label, path.shape[0], mism, worst))
+    say("  %s: paths equal to oracle %d/%d (%d tolerated: margins within tol on %d), worst score rel err %.3g"
+        % (label, n - mism, n, mism, close, worst))
+    assert mism <= close
     return mism
 
 
