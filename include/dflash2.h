@@ -120,8 +120,11 @@ typedef struct df2_dims {
  *   K        candidates per position, 1 <= K <= min(V, 64) (the pages use 16)
  *   out_path  [B, P] int32   selected token at each draft position
  *   out_score [B] float      score of the selected path, sum_t S_t (fp32)
- * Arithmetic: gate and pair scores accumulate in fp32 (bf16 inputs are
- * widened exactly).
+ * Arithmetic: inputs are read exactly; H and S accumulate in fp32.  With
+ * bf16 tables the products G = A(a) (.) H_t enter the matrix cores as a bf16
+ * high part plus a bf16 low part (about 16 significant bits, a relative
+ * error near 2^-16 per product); B(b) is exact.  fp32 tables use the fp32
+ * matrix instruction throughout.
  */
 df2_status dflash2_select(const df2_dims* dims, const void* logits,
                           const void* hidden, const void* A_tab,
@@ -183,7 +186,10 @@ df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V,
                         float* out_val, hipStream_t stream);
 
 /*
- * Gate projection H = W_H h for M rows (the reading of H(h_t)).
+ * Gate projection H = W_H h for M rows ("DFlash 2: Keep Drafting Parallel",
+ * section "A Lightweight Path Selector": the context gate H(h_t) of the
+ * drafter state, whose formula the page cuts off; read as a bias-free
+ * linear map d -> r).
  *   hidden [M, d] (dtype), W_H [r, d] (dtype), out_H [M, r] float
  * d multiple of 32, r multiple of 64 and <= 1024; hidden, W_H and out_H
  * 16-byte aligned.  H is rounded exactly as inside dflash2_select (the same
@@ -194,7 +200,9 @@ df2_status dflash2_project(const void* hidden, const void* W_H, int64_t M,
                            hipStream_t stream);
 
 /*
- * Pair scores of the selector equation for every adjacent candidate pair.
+ * Pair scores of the selector equation for every adjacent candidate pair
+ * (same section: S_t(a, b) = U_t(b) + < A(a) (.) H(h_t), B(b) >, every
+ * adjacent pair scored at once).
  *   cand_idx [B, P, K] int32, cand_val [B, P, K] float (from dflash2_topk)
  *   H        [B, P, r] float (from dflash2_project)
  *   A_tab, B_tab [V, r] (dims->dtype), prev_tok [B] int32
@@ -210,7 +218,9 @@ df2_status dflash2_pair_scores(const df2_dims* dims, const int32_t* cand_idx,
                                float* out_S, hipStream_t stream);
 
 /*
- * The walk alone: max-sum pass over S plus backtrack.
+ * The walk alone (same section: the one sequential step is a walk over the
+ * precomputed scores from the last verified token), read as a max-sum pass
+ * over S plus backtrack.
  *   S        [B, P, K, K] float (row 0 of t == 0 is used)
  *   cand_idx [B, P, K] int32
  *   out_path [B, P] int32, out_score [B] float
@@ -220,7 +230,8 @@ df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B,
                            float* out_score, hipStream_t stream);
 
 /*
- * The walk alone, either mode (see df2_walk).  Arguments as for
+ * The walk alone, either mode (see df2_walk; same section: the walk over
+ * the precomputed scores, max-sum or greedy).  Arguments as for
  * dflash2_viterbi, which is this call with DF2_WALK_VITERBI; 1 <= P <= 64,
  * 1 <= K <= 64; S, cand_idx, out_path and out_score 4-byte aligned.
  */
@@ -229,7 +240,8 @@ df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B,
                         float* out_score, hipStream_t stream);
 
 /*
- * The sampling walk alone (see dflash2_select_sample) over given scores.
+ * The sampling walk alone (see dflash2_select_sample; same section:
+ * sampling draws from the same scores) over given scores.
  *   S [B, P, K, K] float, cand_idx [B, P, K] int32, as for dflash2_walk;
  *   u [B, P] float uniforms, temperature, out_path [B, P] int32,
  *   out_q [B, P] float, out_score [B] float.
