@@ -26,7 +26,8 @@ PLAN_KNOBS = {"segment_wgs": 0, "chunk_vectors": 1, "merge_words": 2, "gate_slic
               "conv_slices": 4, "launches": 5}
 
 EXPORTED = (
-    "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_topk",
+    "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_select_noalloc",
+    "dflash2_topk",
     "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
     "dflash2_sample_walk", "dflash2_conv2", "dflash2_device_error", "dflash2_plan_override",
     "dflash2_release",
@@ -66,6 +67,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "dflash2_select": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
         "dflash2_select_walk": [dp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp, vp],
+        "dflash2_select_noalloc": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp],
         "dflash2_select_sample": [dp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp,
                                   vp],
         "dflash2_topk": [vp, i64, i32, ctypes.c_int, i32, vp, vp, vp],

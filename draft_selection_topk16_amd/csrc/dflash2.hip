@@ -460,6 +460,20 @@ __global__ __launch_bounds__(kWG) void k_walk(WalkArgs a) {
         walk_seq(S, ids, a.P, a.K, a.out_path + rb, a.out_score + b, sm);
 }
 
+// Zeroes n words; clears the arrival counters of the no-allocation entry
+// point (a kernel, not a memset, so that callers may capture it in a graph).
+__global__ __launch_bounds__(kWG) void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kWG + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Scratch of dflash2_select_noalloc: one copy per device, zero when the
+// module loads, kept until the process ends.  Host code uses only the
+// address hipGetSymbolAddress returns for the current device, never the
+// name.
+constexpr size_t kStaticScratchBytes = (size_t)48 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 // ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
@@ -486,6 +500,7 @@ struct Scratch {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::map<int, void*> g_static_scratch;   // device -> address of `scratch` on it
 std::map<int, int> g_capacity;         // device -> resident select workgroups
 std::map<int, int> g_cus;              // device -> compute units
 
@@ -522,6 +537,24 @@ df2_status get_scratch(hipStream_t stream, size_t bytes, size_t counter_bytes, v
         s.zeroed_counter_bytes = counter_bytes;
     }
     *out = s.ptr;
+    return DF2_OK;
+}
+
+// The address of the static scratch on the current device (looked up once per
+// device).
+df2_status static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_static_scratch.find(dev);
+    if (it == g_static_scratch.end()) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (no-allocation scratch)");
+        it = g_static_scratch.emplace(dev, ptr).first;
+    }
+    *out = it->second;
     return DF2_OK;
 }
 
@@ -836,7 +869,8 @@ namespace {
 df2_status select_common(const df2_dims* dims, const void* logits, const void* hidden,
                          const void* A_tab, const void* B_tab, const void* W_H,
                          const int32_t* prev_tok, int32_t K, int walk, const float* u, float inv_tau,
-                         int32_t* out_path, float* out_q, float* out_score, hipStream_t stream) {
+                         int32_t* out_path, float* out_q, float* out_score, hipStream_t stream,
+                         bool noalloc = false) {
     df2_status st = check_dims(dims, true);
     if (st != DF2_OK) return st;
     if ((st = check_k(K, dims->V)) != DF2_OK) return st;
@@ -890,10 +924,27 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     p.out_q = out_q;
     p.inv_tau = inv_tau;
     void* base = nullptr;
-    if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
-    note_layout(stream, pl.counter_bytes);
+    if (noalloc) {
+        if (pl.total_bytes > kStaticScratchBytes)
+            return fail(DF2_EUNSUPPORTED, "problem needs " + std::to_string(pl.total_bytes) +
+                                              " bytes of scratch; the no-allocation entry point holds " +
+                                              std::to_string(kStaticScratchBytes));
+        if ((st = static_scratch(&base)) != DF2_OK) return st;
+    } else {
+        if ((st = get_scratch(stream, pl.total_bytes, pl.counter_bytes, &base)) != DF2_OK) return st;
+        note_layout(stream, pl.counter_bytes);
+    }
     bind_scratch(pl, base, rows, dims->B);
-    return launch_checked([&] { launch_select(pl, stream); }, "dflash2_select launch");
+    return launch_checked([&] {
+        if (noalloc) {
+            // the counters (all words after the device flag word) start at
+            // zero; the previous call may have left data there
+            const int64_t n = (int64_t)(pl.counter_bytes / 4) - 1;
+            hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + kWG - 1) / kWG)), dim3(kWG), 0, stream,
+                               pl.p.err + 1, n);
+        }
+        launch_select(pl, stream);
+    }, "dflash2_select launch");
 }
 
 // 1 / tau for the sampling walk, or an error for a temperature that is not
@@ -946,6 +997,15 @@ df2_status dflash2_select(const df2_dims* dims, const void* logits, const void* 
                           float* out_score, hipStream_t stream) {
     return dflash2_select_walk(dims, logits, hidden, A_tab, B_tab, W_H, prev_tok, K,
                                DF2_WALK_VITERBI, out_path, out_score, stream);
+}
+
+df2_status dflash2_select_noalloc(const df2_dims* dims, const void* logits, const void* hidden,
+                                  const void* A_tab, const void* B_tab, const void* W_H,
+                                  const int32_t* prev_tok, int32_t K, int32_t* out_path,
+                                  float* out_score, hipStream_t stream) {
+    g_last_error.clear();
+    return select_common(dims, logits, hidden, A_tab, B_tab, W_H, prev_tok, K, kWalkViterbi, nullptr, 0.f,
+                         out_path, nullptr, out_score, stream, true);
 }
 
 df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V, df2_dtype dtype, int32_t K,
@@ -1196,11 +1256,28 @@ df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {
     int dev = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
     void* ptr = nullptr;
+    void* sptr = nullptr;
     {
         std::lock_guard<std::mutex> lock(g_mu);
+        auto is = g_static_scratch.find(dev);
+        if (is != g_static_scratch.end()) sptr = is->second;
         auto it = g_scratch.find(std::make_pair(dev, stream));
-        if (it == g_scratch.end()) return DF2_OK;
-        ptr = it->second.ptr;
+        if (it != g_scratch.end()) ptr = it->second.ptr;
+    }
+    uint32_t sv = 0;
+    if (sptr) {
+        // flags of no-allocation calls on this device
+        if ((e = hipMemcpy(&sv, sptr, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+            return hip_fail(e, "hipMemcpy flags");
+        if (sv) {
+            const uint32_t zero = 0;
+            if ((e = hipMemcpy(sptr, &zero, 4, hipMemcpyHostToDevice)) != hipSuccess)
+                return hip_fail(e, "hipMemcpy flags");
+        }
+    }
+    if (!ptr) {
+        *flags = sv;
+        return DF2_OK;
     }
     uint32_t v = 0;
     if ((e = hipMemcpy(&v, ptr, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy flags");
@@ -1215,7 +1292,7 @@ df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags) {
         auto it = g_scratch.find(std::make_pair(dev, stream));
         if (it != g_scratch.end()) it->second.zeroed_counter_bytes = 0;
     }
-    *flags = v;
+    *flags = v | sv;
     return DF2_OK;
 }
 

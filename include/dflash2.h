@@ -174,6 +174,28 @@ df2_status dflash2_select_sample(const df2_dims* dims, const void* logits,
                                  float* out_score, hipStream_t stream);
 
 /*
+ * dflash2_select that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid it).  Same arguments, arithmetic and results as
+ * dflash2_select (the same kernels), but its scratch is a static device
+ * array of 48 MiB (50331648 bytes) that each GPU holds from module load
+ * until the process ends; the first call on a device looks up its address.
+ * Every call on one GPU shares that array: calls that overlap in time on a
+ * GPU (different streams, or threads) race and must be serialised by the
+ * caller.  Each call clears the array's arrival counters with a small
+ * kernel before its own launches (no memset, no allocation).  A problem
+ * whose scratch exceeds 48 MiB returns DF2_EUNSUPPORTED before anything is
+ * enqueued (the stress shape B = 256, P = 15, V = 262144, K = 32 needs about
+ * 40 MB).  Its device flags are reported by dflash2_device_error().
+ */
+df2_status dflash2_select_noalloc(const df2_dims* dims, const void* logits,
+                                  const void* hidden, const void* A_tab,
+                                  const void* B_tab, const void* W_H,
+                                  const int32_t* prev_tok, int32_t K,
+                                  int32_t* out_path, float* out_score,
+                                  hipStream_t stream);
+
+/*
  * Top-K of each row ("keep the top 16 candidates at each position").
  *   logits  [rows, V] (dtype)
  *   out_idx [rows, K] int32  candidate token ids, best first
@@ -278,7 +300,8 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base,
 
 /*
  * Waits for `stream`, then reports and clears the device-side flags of its
- * scratch buffer: *flags receives a bit mask (bit 0: a prev_tok outside
+ * scratch buffer and of the current device's no-allocation scratch: *flags
+ * receives a bit mask (bit 0: a prev_tok outside
  * [0, V) was replaced by 0; bit 1: a cand_idx entry outside [0, V) was
  * replaced by 0; bit 2: a pair-score job of dflash2_select gave up waiting
  * for its gate rows, which only a fault elsewhere can cause, and its scores

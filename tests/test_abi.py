@@ -176,3 +176,22 @@ def test_binding_raises_without_gpu_tensors():
     x = torch.zeros(2, 3, 100, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         df2.topk(x, 4)
+
+
+def test_select_noalloc_rejects_beyond_its_scratch(lib):
+    """A problem whose scratch exceeds the no-allocation entry point's static
+    array (48 MiB) is refused on the host, before any device call."""
+    dims = Dims(256, 64, 262144, 5120, 512, 1)
+    st = lib.dflash2_select_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64,
+                                    FAKE, FAKE, None)
+    assert st == DF2_EUNSUPPORTED
+    msg = lib.dflash2_last_error().decode()
+    assert "no-allocation" in msg and "50331648" in msg
+
+
+def test_select_noalloc_checks_arguments_like_select(lib):
+    assert lib.dflash2_select_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                      None) == DF2_EINVAL
+    dims = Dims(0, 7, 32000, 1024, 256, 1)
+    assert lib.dflash2_select_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                      FAKE, FAKE, None) == DF2_OK
