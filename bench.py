@@ -25,7 +25,16 @@ Prints ONE JSON line:
   conv        the drafter's two-tap dynamic convolution (dflash2_conv2) at
               the two drafter shapes: µs per call (HIP events) and % of HBM
               peak for its algorithmic bytes, input copies rotated;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+  c2, stress  the batch-8 workload (B=8, P=7, V=151936, d=5120) and the
+              stress workload (B=256, P=15, V=262144, d=5120, K=32): µs per
+              call and % of HBM peak;
+  b1.graph    the batch-1 select over every rotated input set captured in one
+              HIP graph and replayed (µs per call), replays checked against
+              the eager outputs;
+  project     the gate projection alone at the timed workload's shape: µs per
+              call and TFLOP/s against the bf16 matrix-core peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload, one
+              thread per usable host core (at most 16), and single-threaded.
 """
 from __future__ import annotations
 
@@ -43,6 +52,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "path-select µs/cycle at B=1, drafted positions/s at B=32; % HBM peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("common.hpp", "topk.hpp", "gate.hpp", "pairs.hpp", "walk.hpp", "dflash2.hip")
 
@@ -87,9 +97,13 @@ def traffic_for(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi",)):
+def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi",), graph=False):
     """Times dflash2_select_walk on `wl` for each walk in `walks` (same inputs);
-    returns (inputs, {walk: timings}, {walk: path of the first input set})."""
+    returns (inputs, {walk: timings}, {walk: path of the first input set}).
+    With graph=True the Viterbi select over every rotated input set is also
+    captured once into a HIP graph (on a stream warmed first, so that no
+    allocation or memset is captured) and replayed; each replay's outputs are
+    checked against the eager results."""
     import torch
     import draft_selection_topk16_amd as df2
     from draft_selection_topk16_amd import synth
@@ -126,9 +140,47 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi
         torch.cuda.synchronize()
         paths[walk] = calls[0].out_path.cpu().numpy().copy()
         del calls
+    if graph:
+        results["graph"] = _time_graph(sets, A, Bt, W, prev, wl, steps)
     del sets
     torch.cuda.empty_cache()
     return x, results, paths
+
+
+def _time_graph(sets, A, Bt, W, prev, wl, steps: int):
+    """One HIP graph holding a select call per rotated input set, replayed;
+    per-call time = replay wall time / calls.  Every replay is checked
+    against the eager outputs of the same calls."""
+    import torch
+    import draft_selection_topk16_amd as df2
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K) for (l, h) in sets]
+        for c in calls:
+            c()
+    gs.synchronize()
+    eager = [(c.out_path.clone(), c.out_score.clone()) for c in calls]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for c in calls:
+            c()
+    reps = max(2, steps // len(calls))
+    ok = True
+    for _ in range(2):
+        for c in calls:
+            c.out_path.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ok &= all(torch.equal(c.out_path, e[0]) and torch.equal(c.out_score, e[1]) for c, e in zip(calls, eager))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ok &= all(torch.equal(c.out_path, e[0]) and torch.equal(c.out_score, e[1]) for c, e in zip(calls, eager))
+    del g, calls
+    return {"us_per_cycle": wall * 1e6 / (reps * len(sets)), "calls_per_graph": len(sets), "replays": reps,
+            "replays_equal_eager": bool(ok)}
 
 
 def _time_calls(calls, nsets: int, steps: int, warmup: int, stream):
@@ -221,24 +273,96 @@ def _differ(paths):
             "of_positions": int(g.size)}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, seconds: float):
-    """The oracle, as it stands, on whole sequences of the workload, one at a
-    time, until `seconds` of CPU work; single-threaded C."""
+    """The oracle, as it stands, on whole sequences of the workload until
+    `seconds` of wall time: first one thread, then one thread per usable host
+    core (at most 16), each taking whole sequences (the oracle's C calls
+    release the GIL).  `value` is the all-cores rate."""
+    import threading
     import oracle
     f = x.f64()
     B, P = x.wl.B, x.wl.P
     oracle.select(f["logits"][:1], f["hidden"][:1], f["A"], f["Bt"], f["W"], f["prev"][:1], x.wl.K)
-    n = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        b = n % B
-        oracle.select(f["logits"], f["hidden"], f["A"], f["Bt"], f["W"], f["prev"], x.wl.K,
-                      seqs=[b])
-        n += 1
-    el = time.perf_counter() - t0
-    return {"value": n * P / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": "%d whole sequences (P=%d, V=%d) of the same workload, one at a time, "
-                      "%.1f s" % (n, P, x.wl.V, el)}
+
+    def run(nthreads, budget):
+        counts = [0] * nthreads
+        t0 = time.perf_counter()
+
+        def work(i):
+            b = i
+            while time.perf_counter() - t0 < budget:
+                oracle.select(f["logits"], f["hidden"], f["A"], f["Bt"], f["W"], f["prev"], x.wl.K,
+                              seqs=[b % B])
+                counts[i] += 1
+                b += nthreads
+        ts = [threading.Thread(target=work, args=(i,)) for i in range(nthreads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        el = time.perf_counter() - t0
+        return sum(counts), el
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    n1, e1 = run(1, seconds / 3)
+    nt, et = run(threads, 2 * seconds / 3)
+    return {"value": nt * P / et, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "usable_cores": len(os.sched_getaffinity(0)),
+            "single_thread": {"value": n1 * P / e1, "unit": "positions/s", "cores": 1,
+                              "sample": "%d whole sequences, %.1f s" % (n1, e1)},
+            "sample": "%d whole sequences (P=%d, V=%d) of the same workload on %d threads, %.1f s"
+                      % (nt, P, x.wl.V, threads, et)}
+
+
+def time_project(wl, steps: int, warmup: int, rotate_mb: float):
+    """dflash2_project (the gate projection H = W_H h) alone at the workload's
+    shape, input copies rotated beyond the Infinity Cache; HIP events per
+    call.  Reports TFLOP/s against the bf16 matrix-core peak."""
+    import torch
+    import numpy as np
+    import draft_selection_topk16_amd as df2
+    from draft_selection_topk16_amd import synth
+    x = synth.make_inputs(wl)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    one = (dev(x.hidden), dev(x.W))
+    per = sum(t.nbytes for t in one)
+    nsets = max(1, int(math.ceil(rotate_mb * 1e6 / per)))
+    sets = [one] + [tuple(t.clone() for t in one) for _ in range(nsets - 1)]
+    for i in range(warmup):
+        df2.project(*sets[i % nsets])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        df2.project(*sets[(warmup + i) % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = statistics.fmean(a.elapsed_time(b) for a, b in ev) * 1e3
+    M = wl.B * wl.P
+    flops = 2.0 * M * wl.d * wl.r
+    ab = 2 * (M * wl.d + wl.r * wl.d) + 4 * M * wl.r
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": "%s gate projection: M=%d d=%d r=%d bf16, fp32 accumulation" % (wl.name, M, wl.d, wl.r),
+            "us_per_call": us, "flops": flops, "tflops": flops / (us * 1e-6) / 1e12,
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "algorithmic_bytes": ab, "hbm_frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
 def copy_calibration(mb: float, reps: int):
@@ -266,6 +390,10 @@ def main():
     ap.add_argument("--no-b1", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the batch-8 and stress lines")
+    ap.add_argument("--no-project", action="store_true")
+    ap.add_argument("--only", choices=["project"], default=None,
+                    help="time one stage alone (for counter runs) and print its JSON object")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
     args = ap.parse_args()
 
@@ -289,6 +417,9 @@ def main():
     df2.load()
 
     wl = synth.WORKLOADS[args.workload]
+    if args.only == "project":
+        print(json.dumps(time_project(wl, args.steps, args.warmup, args.rotate_mb)), flush=True)
+        return
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
     walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy", "sample")
     x, allres, paths = time_workload(wl, args.steps, args.warmup, args.rotate_mb, walks)
@@ -344,7 +475,7 @@ def main():
     if not args.no_b1:
         wl1 = synth.WORKLOADS[args.b1_workload]
         log("timing %s" % wl1.name)
-        _, allr1, _ = time_workload(wl1, args.steps, args.warmup, args.rotate_mb, walks)
+        _, allr1, _ = time_workload(wl1, args.steps, args.warmup, args.rotate_mb, walks, graph=True)
         r1 = allr1["viterbi"]
         ab1 = algorithmic_bytes(wl1)
         out["b1"] = {"workload": "%s: B=%d P=%d V=%d d=%d K=%d" % (wl1.name, wl1.B, wl1.P, wl1.V, wl1.d, wl1.K),
@@ -352,7 +483,8 @@ def main():
                      "kernel_us_avg": r1["kernel_ms_avg"] * 1e3,
                      "positions_per_s": wl1.B * wl1.P / (r1["ms_per_step"] * 1e-3),
                      "hbm_frac": ab1 / (r1["kernel_ms_avg"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "timing": r1}
+                     "timing": r1,
+                     "graph": allr1["graph"]}
         if not args.no_greedy:
             g1 = allr1["greedy"]
             out["greedy"]["b1"] = {"workload": wl1.name,
@@ -368,6 +500,23 @@ def main():
         _, _, pp = time_workload(wlp, 3, 1, 0.0, ("viterbi", "greedy"))
         out["greedy"]["pair_dominant"] = {"workload": "%s with A and B scaled by 8" % wl.name,
                                           "paths_differ_from_viterbi": _differ(pp)}
+    if not args.no_extra:
+        for key, name, steps in (("c2", "t27b_b8", args.steps), ("stress", "stress_b256", max(20, args.steps // 10))):
+            wlx = synth.WORKLOADS[name]
+            log("timing %s" % name)
+            _, rx, _ = time_workload(wlx, steps, max(5, args.warmup // 10), args.rotate_mb, ("viterbi",))
+            r = rx["viterbi"]
+            abx = algorithmic_bytes(wlx)
+            out[key] = {"workload": "%s: B=%d P=%d V=%d d=%d K=%d r=%d %s" % (
+                            name, wlx.B, wlx.P, wlx.V, wlx.d, wlx.K, wlx.r, wlx.dtype),
+                        "us_per_cycle": r["ms_per_step"] * 1e3, "kernel_us_avg": r["kernel_ms_avg"] * 1e3,
+                        "positions_per_s": wlx.B * wlx.P / (r["ms_per_step"] * 1e-3),
+                        "algorithmic_bytes": abx,
+                        "hbm_frac": abx / (r["kernel_ms_avg"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "timing": r}
+    if not args.no_project:
+        log("timing the gate projection alone at %s" % wl.name)
+        out["project"] = time_project(wl, args.steps, args.warmup, args.rotate_mb)
     if not args.no_conv:
         out["conv"] = {}
         for name in synth.CONV_WORKLOADS:

@@ -718,3 +718,32 @@ def test_sample_draw_frequencies_follow_q():
     e = np.exp(row - row.max())
     qr = e / e.sum()
     assert np.all(np.abs(counts - N * qr) <= 2.0), (counts, N * qr)
+
+
+def test_select_graph_replay():
+    """A select call captured in a HIP graph (its stream warmed first, so the
+    capture holds no allocation and no memset) gives the eager result on
+    every replay, with eager work on another stream between replays."""
+    say("select graph replay")
+    x = inputs("qwen3_4b_b1")
+    t = to_device(x)
+    other = to_device(synth.make_inputs(synth.WORKLOADS["tiny_f32"].with_(V=5000)))
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        call = df2.PreparedSelect(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K)
+        for _ in range(3):
+            call()
+    gs.synchronize()
+    ref = (call.out_path.clone(), call.out_score.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        call()
+    for i in range(5):
+        call.out_path.zero_()
+        call.out_score.zero_()
+        df2.select(other["logits"], other["hidden"], other["A"], other["Bt"], other["W"], other["prev"], 16)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out_path, ref[0]) and torch.equal(call.out_score, ref[1]), i
+    assert flags_clear()
