@@ -37,6 +37,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "Inputs", "make_inputs", "f32_to_bf16_bits",
     "bf16_bits_to_f64", "to_f64", "ConvInputs", "CONV_WORKLOADS", "make_conv_inputs",
+    "LmHeadInputs", "make_lmhead_inputs", "bf16_bits_to_f32",
 ]
 
 
@@ -221,3 +222,80 @@ def make_conv_inputs(B: int, P: int, d: int, dtype: str = "bf16", seed: int = 0x
     W_c = (0.1 / math.sqrt(d)) * g.standard_normal((2, d // 16, d), dtype=np.float32)
     return ConvInputs(B, P, d, dtype, _store(x, dtype), _store(x_prev, dtype), _store(base, dtype),
                       _store(W_c.astype(np.float32), dtype))
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the drafter's LM head (the logits the selector starts from).  The
+# pages give no trained weights; the recipe reproduces the logit mix of the
+# workloads above from a hidden state and a weight matrix:
+#   * W_lm [V, d] ~ N(0, 1/d) (std 1/sqrt(d)), so a hidden state z ~ N(0, 1)^d
+#     gives logits ~ N(0, 1);
+#   * each position's hidden state is s * z with s = 2 for peaked rows and
+#     s = 1 for flat rows (the N(0, 2) and N(0, 1) logits of the selector
+#     workloads), plus, for a peaked row, delta_k * w / |w|^2 for each of its
+#     m ~ U{1,2,3} peak tokens (w = that token's bf16 weight row,
+#     delta_k = 4 + 6/k), which lifts that token's logit by delta_k;
+#   * flat rows, their fraction and the stress workload's reuse of the
+#     previous position's top peak follow the selector workloads.
+# Everything is bf16 (the drafter's precision); sequence b draws from
+# sub-seed seed * 1000 + b, the weights from the base seed in row blocks.
+# ---------------------------------------------------------------------------
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(b).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class LmHeadInputs:
+    wl: Workload
+    X: np.ndarray        # [B*P, d] bf16 bits, final hidden state per draft position
+    W_lm: np.ndarray     # [V, d] bf16 bits, one weight row per token
+    peaks: np.ndarray    # [B*P, 3] int32 planted peak tokens, -1 where none
+    flat: np.ndarray     # [B*P] bool
+
+    def f32(self):
+        """(X, W_lm) widened exactly to float32."""
+        return bf16_bits_to_f32(self.X), bf16_bits_to_f32(self.W_lm)
+
+
+def make_lmhead_inputs(wl: Workload, seed: Optional[int] = None,
+                       row_block: int = 8192) -> LmHeadInputs:
+    base = (0xDF2100 + wl.wid) if seed is None else int(seed)
+    g = np.random.Generator(np.random.PCG64(base))
+    B, P, V, d = wl.B, wl.P, wl.V, wl.d
+    M = B * P
+    W = np.empty((V, d), dtype=np.uint16)
+    scale = np.float32(1.0 / math.sqrt(d))
+    for r0 in range(0, V, row_block):
+        r1 = min(V, r0 + row_block)
+        W[r0:r1] = f32_to_bf16_bits(g.standard_normal((r1 - r0, d), dtype=np.float32) * scale)
+
+    flat = np.zeros(M, dtype=bool)
+    if wl.flat_frac > 0 and wl.flat_mode == "exact":
+        flat[g.permutation(M)[:int(round(wl.flat_frac * M))]] = True
+    elif wl.flat_frac > 0:
+        flat = g.random(M) < wl.flat_frac
+
+    X = np.empty((M, d), dtype=np.uint16)
+    peaks = np.full((M, 3), -1, dtype=np.int32)
+    for b in range(B):
+        gb = np.random.Generator(np.random.PCG64(base * 1000 + b))
+        last_top = -1
+        for t in range(P):
+            row = b * P + t
+            if flat[row]:
+                X[row] = f32_to_bf16_bits(gb.standard_normal(d, dtype=np.float32))
+                last_top = -1
+                continue
+            x = 2.0 * gb.standard_normal(d, dtype=np.float32).astype(np.float64)
+            m = int(gb.integers(1, 4))
+            toks = gb.integers(0, V, size=m)
+            if wl.dup_prob > 0 and last_top >= 0 and gb.random() < wl.dup_prob:
+                toks[0] = last_top
+            for k in range(m):
+                w = bf16_bits_to_f64(W[toks[k]])
+                x += (4.0 + 6.0 / (k + 1)) * w / np.dot(w, w)
+            peaks[row, :m] = toks
+            last_top = int(toks[0])
+            X[row] = f32_to_bf16_bits(x.astype(np.float32))
+    return LmHeadInputs(wl=wl, X=X, W_lm=W, peaks=peaks, flat=flat)

@@ -10,7 +10,8 @@ last verified token); the walk is read as max-sum Viterbi with backtrack, the
 literal greedy walk and the sampling walk are further modes, and H(h_t) is
 read as a bias-free linear map d -> r (see the header of oracle.c).  conv2 is
 the drafter's two-tap dynamic convolution ("A Lightweight Local
-Convolution").
+Convolution"); lmhead_topk is the drafter's LM head followed by top-K, the
+logits the selector starts from.
 
 Every function here is pinned by CPU tests against something other than
 itself (brute-force enumeration, closed forms, exact integer cases, an
@@ -66,6 +67,10 @@ def _load():
         lib.orc_conv2.restype = None
         lib.orc_second_best.argtypes = [P, P, I, I, I, P]
         lib.orc_second_best.restype = ctypes.c_int
+        lib.orc_lmhead_topk.argtypes = [P, P, I, I, I, ctypes.c_int32, P, P, P]
+        lib.orc_lmhead_topk.restype = ctypes.c_int
+        lib.orc_lmhead_dot.argtypes = [P, P, I, P, P, I, P, P]
+        lib.orc_lmhead_dot.restype = None
         _lib = lib
     return _lib
 
@@ -103,6 +108,49 @@ def project(h: np.ndarray, W: np.ndarray) -> np.ndarray:
     H = np.empty(h.shape[:-1] + (r,), dtype=np.float64)
     _load().orc_project(_p(h), _p(W), M, d, r, _p(H))
     return H
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def lmhead_topk(X, W, K: int, rows=None):
+    """LM head then top-K (see orc_lmhead_topk): X [M, d] hidden states,
+    W [V, d] LM-head weight, both holding exact fp32 or bf16 values.
+    Returns (idx int32 [M', K], val float64 [M', K], sigma float64 [M', K])
+    for the rows listed in `rows` (all rows when None), in that order."""
+    X = _f32(X)
+    W = _f32(W)
+    if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[1]:
+        raise ValueError("lmhead_topk: X must be [M, d] and W [V, d]")
+    if rows is not None:
+        X = _f32(X[np.asarray(rows, dtype=np.int64)])
+    M, d = X.shape
+    V = W.shape[0]
+    idx = np.empty((M, K), dtype=np.int32)
+    val = np.empty((M, K), dtype=np.float64)
+    sig = np.empty((M, K), dtype=np.float64)
+    if M and _load().orc_lmhead_topk(_p(X), _p(W), M, d, V, K, _p(idx), _p(val), _p(sig)) != 0:
+        raise ValueError("orc_lmhead_topk: bad K/V/d or out of memory")
+    return idx, val, sig
+
+
+def lmhead_dot(X, W, m, v):
+    """Logits W[v_i] . X[m_i] and their scales sum |W[v_i] * X[m_i]| (float64)."""
+    X = _f32(X)
+    W = _f32(W)
+    m = np.ascontiguousarray(m, dtype=np.int64).ravel()
+    v = np.ascontiguousarray(v, dtype=np.int64).ravel()
+    if m.shape != v.shape:
+        raise ValueError("lmhead_dot: m and v differ in length")
+    if m.size and (m.min() < 0 or m.max() >= X.shape[0] or v.min() < 0 or v.max() >= W.shape[0]):
+        raise ValueError("lmhead_dot: index out of range")
+    dot = np.empty(m.size, dtype=np.float64)
+    absdot = np.empty(m.size, dtype=np.float64)
+    if m.size:
+        _load().orc_lmhead_dot(_p(X), _p(W), X.shape[1], _p(m), _p(v), m.size, _p(dot),
+                               _p(absdot))
+    return dot, absdot
 
 
 def pair_scores(cand, U, H, A, Bt, prev):

@@ -34,7 +34,9 @@
  *   - U_t(b) is the raw logit.
  *
  * The drafter's two-tap convolution (orc_conv2, section "A Lightweight Local
- * Convolution") is here too; its readings are stated beside it.
+ * Convolution") and its LM head followed by top-K (orc_lmhead_topk, the
+ * logits the selector starts from) are here too; their readings are stated
+ * beside them.
  *
  * Parity pins (checked by the CPU test suite, not by this file): brute-force
  * enumeration of all K^P paths on tiny inputs, zeroed pair term reducing to
@@ -104,6 +106,77 @@ void orc_project(const double* h, const double* W, int64_t M, int64_t d,
             for (int64_t k = 0; k < d; ++k) acc += W[q * d + k] * h[m * d + k];
             H[m * r + q] = acc;
         }
+    }
+}
+
+/*
+ * The drafter's LM head followed by top-K, the upstream step the selector
+ * consumes ("DFlash 2: Keep Drafting Parallel", section "A Lightweight Path
+ * Selector": the selector works on the drafter's own logits and needs no
+ * extra LM-head pass).  Read as a bias-free linear map of the drafter's
+ * final hidden state onto the vocabulary:
+ *     U_t(v) = sum_k W_lm[v][k] * h_t[k]
+ * and then the same top-K order as orc_topk (value descending, equal values
+ * to the lower index).
+ *   X      [M][d]  hidden states (float storage of exact bf16/fp32 values)
+ *   W      [V][d]  LM-head weight, one row per token
+ *   idx    [M][K]  token id of the k-th best logit
+ *   val    [M][K]  that logit, every product and sum in float64
+ *   sigma  [M][K]  sum_k |W[v][k] h[k]| of that logit (scale for tolerances)
+ * Returns 0, or -1 on bad sizes or allocation failure.
+ */
+int orc_lmhead_topk(const float* X, const float* W, int64_t M, int64_t d,
+                    int64_t V, int32_t K, int32_t* idx, double* val,
+                    double* sigma) {
+    if (K < 1 || K > V || d < 1) return -1;
+    double* logit = (double*)malloc(sizeof(double) * (size_t)V);
+    double* row_val = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!logit || !row_val) {
+        free(logit);
+        free(row_val);
+        return -1;
+    }
+    int rc = 0;
+    for (int64_t m = 0; m < M && rc == 0; ++m) {
+        const float* x = X + m * d;
+        for (int64_t v = 0; v < V; ++v) {
+            const float* w = W + v * d;
+            double acc = 0.0;
+            for (int64_t k = 0; k < d; ++k) acc += (double)w[k] * (double)x[k];
+            logit[v] = acc;
+        }
+        rc = orc_topk(logit, 1, V, K, idx + m * K, row_val);
+        for (int32_t j = 0; j < K && rc == 0; ++j) {
+            const float* w = W + (int64_t)idx[m * K + j] * d;
+            double s = 0.0;
+            for (int64_t k = 0; k < d; ++k) s += fabs((double)w[k] * (double)x[k]);
+            val[m * K + j] = row_val[j];
+            sigma[m * K + j] = s;
+        }
+    }
+    free(logit);
+    free(row_val);
+    return rc;
+}
+
+/*
+ * Single LM-head logits for n given (row, token) pairs, with their scale:
+ *   dot[i]   = sum_k W[v_i][k] * X[m_i][k]      (float64)
+ *   absdot[i] = sum_k |W[v_i][k] * X[m_i][k]|
+ */
+void orc_lmhead_dot(const float* X, const float* W, int64_t d, const int64_t* m,
+                    const int64_t* v, int64_t n, double* dot, double* absdot) {
+    for (int64_t i = 0; i < n; ++i) {
+        const float* x = X + m[i] * d;
+        const float* w = W + v[i] * d;
+        double acc = 0.0, s = 0.0;
+        for (int64_t k = 0; k < d; ++k) {
+            const double p = (double)w[k] * (double)x[k];
+            acc += p;
+            s += fabs(p);
+        }
+        dot[i] = acc;
+        absdot[i] = s;
     }
 }
 

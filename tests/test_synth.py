@@ -41,3 +41,23 @@ def test_saturation_workload_flat_rows():
     # exactly round(0.2 * 224) = 45 flat rows: N(0,1) maxima stay below 5.5,
     # while N(0,2) rows (with or without their peaks) exceed it
     assert int((~peaked).sum()) == 45
+
+
+def test_lmhead_inputs_deterministic_and_peaked():
+    wl = synth.WORKLOADS["t27b_b32"].with_(B=2, V=4000, d=256)
+    a = synth.make_lmhead_inputs(wl)
+    b = synth.make_lmhead_inputs(wl)
+    assert a.X.shape == (14, 256) and a.W_lm.shape == (4000, 256) and a.X.dtype == np.uint16
+    assert np.array_equal(a.X, b.X) and np.array_equal(a.W_lm, b.W_lm)
+    assert np.array_equal(a.peaks, b.peaks)
+    X, W = a.f32()
+    assert np.array_equal(X.astype(np.float64), synth.bf16_bits_to_f64(a.X))
+    # W rows have norm close to 1; flat rows carry no planted token
+    assert abs(np.linalg.norm(W.astype(np.float64), axis=1).mean() - 1.0) < 0.05
+    assert np.all(a.peaks[a.flat] == -1) and np.all(a.peaks[~a.flat, 0] >= 0)
+    assert a.flat.sum() == round(0.2 * 14)
+    # a planted top peak lifts its token's logit by about 10 over its noise
+    rows = np.nonzero(~a.flat)[0]
+    L = X[rows].astype(np.float64) @ W.astype(np.float64).T
+    top = a.peaks[rows, 0]
+    assert np.all(L[np.arange(len(rows)), top] > np.median(L, axis=1) + 6.0)
