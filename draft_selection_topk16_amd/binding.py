@@ -23,11 +23,11 @@ WALKS = {"viterbi": 0, "greedy": 1}
 
 # df2_plan_knob
 PLAN_KNOBS = {"segment_wgs": 0, "chunk_vectors": 1, "merge_words": 2, "gate_slices": 3,
-              "conv_slices": 4, "launches": 5}
+              "conv_slices": 4, "launches": 5, "lm_ranges": 6}
 
 EXPORTED = (
     "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_select_noalloc",
-    "dflash2_topk",
+    "dflash2_topk", "dflash2_lmhead_topk",
     "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
     "dflash2_sample_walk", "dflash2_conv2", "dflash2_device_error", "dflash2_plan_override",
     "dflash2_release",
@@ -71,6 +71,7 @@ def load() -> ctypes.CDLL:
         "dflash2_select_sample": [dp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp,
                                   vp],
         "dflash2_topk": [vp, i64, i32, ctypes.c_int, i32, vp, vp, vp],
+        "dflash2_lmhead_topk": [vp, vp, i64, i32, i32, ctypes.c_int, i32, vp, vp, vp],
         "dflash2_project": [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp],
         "dflash2_pair_scores": [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp],
         "dflash2_viterbi": [vp, vp, i32, i32, i32, vp, vp, vp],
@@ -225,6 +226,25 @@ def topk(logits: torch.Tensor, K: int) -> Tuple[torch.Tensor, torch.Tensor]:
     val = torch.empty(logits.shape[:-1] + (K,), dtype=torch.float32, device=logits.device)
     _check(lib.dflash2_topk(_dev(logits, "logits"), rows, V, _dtype_code(logits), int(K),
                             _dev(idx, "idx"), _dev(val, "val"), _stream(logits.device)))
+    return idx, val
+
+
+def lmhead_topk(hidden: torch.Tensor, W_lm: torch.Tensor, K: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The LM head fused with top-K: for every row of hidden[..., d] (bf16),
+    the top K of W_lm [V, d] @ hidden without writing the logits:
+    (idx int32 [..., K], val float32 [..., K])."""
+    lib = load()
+    V, d = W_lm.shape
+    if hidden.shape[-1] != d:
+        raise ValueError("hidden [..., d] and W_lm [V, d] disagree on d")
+    if W_lm.dtype != hidden.dtype:
+        raise TypeError("W_lm must have the hidden dtype")
+    M = hidden.numel() // d if d else 0
+    idx = torch.empty(hidden.shape[:-1] + (K,), dtype=torch.int32, device=hidden.device)
+    val = torch.empty(hidden.shape[:-1] + (K,), dtype=torch.float32, device=hidden.device)
+    _check(lib.dflash2_lmhead_topk(_dev(hidden, "hidden"), _dev(W_lm, "W_lm"), M, V, d,
+                                   _dtype_code(hidden), int(K), _dev(idx, "idx"), _dev(val, "val"),
+                                   _stream(hidden.device)))
     return idx, val
 
 

@@ -46,6 +46,7 @@
 #include "common.hpp"
 #include "conv.hpp"
 #include "gate.hpp"
+#include "lmhead.hpp"
 #include "pairs.hpp"
 #include "topk.hpp"
 #include "walk.hpp"
@@ -577,6 +578,7 @@ struct Overrides {
     int gate_s = 0;       // gate slices of d (1..16)
     int conv_s = 0;       // k slices of the convolution's correction GEMM
     int launches = 0;     // dflash2_select: 1 = one fused launch, 2 = scan then tail
+    int lm_ranges = 0;    // vocabulary ranges of the LM head (1..256)
 };
 Overrides g_over;
 
@@ -1314,6 +1316,10 @@ df2_status dflash2_plan_override(df2_plan_knob knob, int32_t value) {
             if (value > 2) return fail(DF2_EINVAL, "launches must be 0, 1 or 2");
             g_over.launches = value;
             break;
+        case DF2_PLAN_LM_RANGES:
+            if (value > kLmMaxLists) return fail(DF2_EINVAL, "LM-head ranges must be in [0, 256]");
+            g_over.lm_ranges = value;
+            break;
         default: return fail(DF2_EINVAL, "unknown plan knob");
     }
     return DF2_OK;
@@ -1334,6 +1340,125 @@ df2_status dflash2_release(void) {
     }
     g_scratch.clear();
     return st;
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------------------
+// The drafter's LM head fused with top-K (k_lmhead, then k_lmhead_merge).
+// ----------------------------------------------------------------------------
+namespace {
+
+constexpr int kLmTiles[] = {1, 2, 4, 8, 12, 14, 16};   // m-blocks per tile with a kernel
+
+struct LmPlan {
+    int mb = 1, kmax = 16;
+    int n_mt = 1, n_vr = 1, nblk = 1;
+    size_t part_bytes = 0, merge_lds = 0;
+};
+
+// Tiles of up to 16 m-blocks (14 for K > 16 and 8 for K > 32, whose lists
+// take more LDS and registers), the smallest tile kernel that covers an even
+// split of the rows; then enough vocabulary ranges to give every CU one
+// workgroup.
+LmPlan plan_lmhead(int64_t M, int V, int K, int cus, const Overrides& ov) {
+    LmPlan pl;
+    pl.kmax = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
+    const int maxmb = pl.kmax == 16 ? 16 : (pl.kmax == 32 ? 14 : 8);
+    const int64_t nbm = (M + 15) / 16;
+    const int64_t nmt = (nbm + maxmb - 1) / maxmb;
+    const int64_t want = (nbm + nmt - 1) / nmt;
+    for (int t : kLmTiles)
+        if (t <= maxmb && t >= want) {
+            pl.mb = t;
+            break;
+        }
+    pl.n_mt = (int)((nbm + pl.mb - 1) / pl.mb);
+    pl.nblk = (V + 15) / 16;
+    int nvr = ov.lm_ranges > 0 ? ov.lm_ranges : (int)std::max<int64_t>(1, cus / pl.n_mt);
+    pl.n_vr = std::max(1, std::min(std::min(nvr, kLmMaxLists), pl.nblk));
+    pl.part_bytes = (size_t)M * pl.n_vr * pl.kmax * sizeof(uint64_t);
+    pl.merge_lds = (size_t)pl.n_vr * K * sizeof(uint64_t);
+    return pl;
+}
+
+df2_status launch_lmhead(const LmPlan& pl, const LmArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)pl.n_mt * pl.n_vr)), block(kWG);
+#define DF2_LM(MB_, KM_)                                                                   \
+    if (pl.mb == MB_ && pl.kmax == KM_) {                                                  \
+        hipLaunchKernelGGL((k_lmhead<MB_, KM_>), grid, block, 0, stream, a);               \
+        launched = true;                                                                   \
+    }
+    bool launched = false;
+    DF2_LM(1, 16) DF2_LM(2, 16) DF2_LM(4, 16) DF2_LM(8, 16) DF2_LM(12, 16) DF2_LM(14, 16)
+    DF2_LM(16, 16)
+    DF2_LM(1, 32) DF2_LM(2, 32) DF2_LM(4, 32) DF2_LM(8, 32) DF2_LM(12, 32) DF2_LM(14, 32)
+    DF2_LM(1, 64) DF2_LM(2, 64) DF2_LM(4, 64) DF2_LM(8, 64)
+#undef DF2_LM
+    if (!launched) return fail(DF2_EUNSUPPORTED, "no LM-head kernel for this tile");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "dflash2_lmhead_topk launch");
+    if (pl.merge_lds > 65536) {
+        static std::once_flag once;
+        static hipError_t attr = hipSuccess;
+        std::call_once(once, [] {
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lmhead_merge),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kLmMaxLists * 64 * sizeof(uint64_t)));
+        });
+        if (attr != hipSuccess) return hip_fail(attr, "hipFuncSetAttribute (LM-head merge)");
+    }
+    hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)a.M), block, pl.merge_lds, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "dflash2_lmhead_topk merge launch");
+    return DF2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+df2_status dflash2_lmhead_topk(const void* hidden, const void* W_lm, int64_t M, int32_t V,
+                               int32_t d, df2_dtype dtype, int32_t K, int32_t* out_idx,
+                               float* out_val, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != DF2_F32 && dtype != DF2_BF16) return fail(DF2_EINVAL, "unknown dtype");
+    if (dtype != DF2_BF16)
+        return fail(DF2_EUNSUPPORTED, "the LM head takes bf16 hidden states and weights");
+    if (M < 0) return fail(DF2_EINVAL, "M < 0");
+    if (V < 1) return fail(DF2_EINVAL, "V < 1");
+    df2_status st = check_k(K, V);
+    if (st != DF2_OK) return st;
+    if (d < 64 || d % 64 != 0 || d > 32768)
+        return fail(DF2_EUNSUPPORTED, "d must be a multiple of 64 in [64, 32768]");
+    if (M == 0) return DF2_OK;
+    if (M > (1 << 24)) return fail(DF2_EUNSUPPORTED, "M too large (at most 2^24 rows)");
+    if (!hidden || !W_lm || !out_idx || !out_val) return fail(DF2_EINVAL, "NULL pointer argument");
+    if (!aligned16(hidden) || !aligned16(W_lm))
+        return fail(DF2_EINVAL, "hidden and W_lm must be 16-byte aligned");
+    if (((uintptr_t)out_idx & 3u) || ((uintptr_t)out_val & 3u))
+        return fail(DF2_EINVAL, "outputs must be 4-byte aligned");
+    const LmPlan pl = plan_lmhead(M, V, K, cu_count(), overrides());
+    // the first 256 bytes keep the device flag word; the lists follow
+    void* base = nullptr;
+    if ((st = get_scratch(stream, 256 + pl.part_bytes, 4, &base)) != DF2_OK) return st;
+    note_layout(stream, 4);
+    LmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.X = reinterpret_cast<const uint16_t*>(hidden);
+    a.W = reinterpret_cast<const uint16_t*>(W_lm);
+    a.part = reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(base) + 256);
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    a.M = M;
+    a.V = V;
+    a.d = d;
+    a.K = K;
+    a.kstride = pl.kmax;
+    a.n_mt = pl.n_mt;
+    a.n_vr = pl.n_vr;
+    a.nblk = pl.nblk;
+    return launch_lmhead(pl, a, stream);
 }
 
 }  // extern "C"

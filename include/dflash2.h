@@ -80,7 +80,8 @@ typedef enum {
     DF2_PLAN_MERGE_WORDS = 2,   /* most candidate words one row merge takes (<= 1024) */
     DF2_PLAN_GATE_SLICES = 3,   /* slices of d of the gate projection (<= 16) */
     DF2_PLAN_CONV_SLICES = 4,   /* k slices of the convolution's correction GEMM */
-    DF2_PLAN_LAUNCHES = 5       /* dflash2_select: 1 = one fused launch, 2 = scan then tail */
+    DF2_PLAN_LAUNCHES = 5,      /* dflash2_select: 1 = one fused launch, 2 = scan then tail */
+    DF2_PLAN_LM_RANGES = 6      /* dflash2_lmhead_topk: vocabulary ranges (<= 256) */
 } df2_plan_knob;
 
 typedef enum {
@@ -206,6 +207,33 @@ df2_status dflash2_select_noalloc(const df2_dims* dims, const void* logits,
 df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V,
                         df2_dtype dtype, int32_t K, int32_t* out_idx,
                         float* out_val, hipStream_t stream);
+
+/*
+ * The drafter's LM head fused with top-K ("DFlash 2: Keep Drafting
+ * Parallel", section "A Lightweight Path Selector": the selector works on
+ * the drafter's own logits and needs no extra LM-head pass).  For each row m
+ *     U(m, v) = sum_k W_lm[v][k] * hidden[m][k]      (v = 0 .. V-1)
+ * is computed on the matrix cores (bf16 products, exact in fp32, summed in
+ * fp32) and only its top K leave the chip: the [M, V] logits are never
+ * written to memory.  The outputs are those of dflash2_topk applied to the
+ * fp32 logits, and feed dflash2_pair_scores like its outputs do.
+ *   hidden  [M, d] bf16   final hidden state of each draft position
+ *   W_lm    [V, d] bf16   LM-head weight, one row per token
+ *   out_idx [M, K] int32  candidate token ids, best first
+ *   out_val [M, K] float  their fp32 logits (a -0 logit is returned as +0)
+ * dtype must be DF2_BF16 (DF2_F32 returns DF2_EUNSUPPORTED).  1 <= K <=
+ * min(V, 64); d a multiple of 64 in [64, 32768]; M <= 2^24 (M == 0 enqueues
+ * nothing); hidden and W_lm 16-byte aligned, outputs 4-byte aligned.
+ * Top-K order as everywhere (value descending, equal values to the lower
+ * index); the fp32 sums differ from exact ones by at most a few units in
+ * the last place of sum_k |W_lm[v][k] hidden[m][k]|, so near-equal logits at
+ * the K-th place may order differently than in exact arithmetic.
+ * Non-finite hidden states or weights are outside the contract.  The
+ * per-range candidate lists go through the library's scratch.
+ */
+df2_status dflash2_lmhead_topk(const void* hidden, const void* W_lm, int64_t M, int32_t V,
+                               int32_t d, df2_dtype dtype, int32_t K, int32_t* out_idx,
+                               float* out_val, hipStream_t stream);
 
 /*
  * Gate projection H = W_H h for M rows ("DFlash 2: Keep Drafting Parallel",

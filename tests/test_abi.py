@@ -163,6 +163,33 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     assert lib.dflash2_conv2(FAKE, FAKE, FAKE, FAKE + 8, 2, 7, 512, 1, FAKE, None) == DF2_EINVAL
 
 
+def test_lmhead_topk_rejects_bad_arguments(lib):
+    f = lib.dflash2_lmhead_topk
+    # M == 0 enqueues nothing
+    assert f(FAKE, FAKE, 0, 151936, 5120, 1, 16, FAKE, FAKE, None) == DF2_OK
+    # bf16 only, d a multiple of 64 in [64, 32768]
+    assert f(FAKE, FAKE, 4, 1000, 128, 0, 16, FAKE, FAKE, None) == DF2_EUNSUPPORTED
+    assert b"bf16" in lib.dflash2_last_error()
+    assert f(FAKE, FAKE, 4, 1000, 128, 7, 16, FAKE, FAKE, None) == DF2_EINVAL
+    for d in (32, 96, 100, 32768 + 64):
+        assert f(FAKE, FAKE, 4, 1000, d, 1, 16, FAKE, FAKE, None) == DF2_EUNSUPPORTED
+    # K in [1, min(V, 64)]
+    for K, V in ((0, 1000), (65, 1000), (11, 10)):
+        assert f(FAKE, FAKE, 4, V, 128, 1, K, FAKE, FAKE, None) == DF2_EINVAL
+    assert f(FAKE, FAKE, -1, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
+    assert f(FAKE, FAKE, 4, 0, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
+    assert f(FAKE, FAKE, 1 << 25, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EUNSUPPORTED
+    # pointers and alignment
+    assert f(None, FAKE, 4, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
+    assert f(FAKE, FAKE, 4, 1000, 128, 1, 16, FAKE, None, None) == DF2_EINVAL
+    assert f(FAKE + 8, FAKE, 4, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
+    assert f(FAKE, FAKE + 2, 4, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
+    assert f(FAKE, FAKE, 4, 1000, 128, 1, 16, FAKE + 2, FAKE, None) == DF2_EINVAL
+    # its plan knob: vocabulary ranges in [0, 256]
+    assert lib.dflash2_plan_override(6, 257) == DF2_EINVAL
+    assert lib.dflash2_plan_override(6, 0) == DF2_OK
+
+
 def test_binding_rejects_unknown_walk_name():
     import torch
     S = torch.zeros(1, 2, 3, 3)
