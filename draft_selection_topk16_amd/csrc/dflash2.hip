@@ -1376,6 +1376,9 @@ LmPlan plan_lmhead(int64_t M, int V, int K, int cus, const Overrides& ov) {
     pl.n_mt = (int)((nbm + pl.mb - 1) / pl.mb);
     pl.nblk = (V + 15) / 16;
     int nvr = ov.lm_ranges > 0 ? ov.lm_ranges : (int)std::max<int64_t>(1, cus / pl.n_mt);
+    // a range spans fewer than 2^21 columns (its candidates encode the offset)
+    const int min_vr = (int)(((int64_t)pl.nblk * 16 + kLmMaxRangeCols - 1) / kLmMaxRangeCols);
+    nvr = std::max(nvr, min_vr);
     pl.n_vr = std::max(1, std::min(std::min(nvr, kLmMaxLists), pl.nblk));
     pl.part_bytes = (size_t)M * pl.n_vr * pl.kmax * sizeof(uint64_t);
     pl.merge_lds = (size_t)pl.n_vr * K * sizeof(uint64_t);
@@ -1433,6 +1436,7 @@ df2_status dflash2_lmhead_topk(const void* hidden, const void* W_lm, int64_t M, 
         return fail(DF2_EUNSUPPORTED, "d must be a multiple of 64 in [64, 32768]");
     if (M == 0) return DF2_OK;
     if (M > (1 << 24)) return fail(DF2_EUNSUPPORTED, "M too large (at most 2^24 rows)");
+    if (V > (1 << 29)) return fail(DF2_EUNSUPPORTED, "V too large for the LM head (at most 2^29)");
     if (!hidden || !W_lm || !out_idx || !out_val) return fail(DF2_EINVAL, "NULL pointer argument");
     if (!aligned16(hidden) || !aligned16(W_lm))
         return fail(DF2_EINVAL, "hidden and W_lm must be 16-byte aligned");

@@ -8,21 +8,21 @@
 //
 // k_lmhead: workgroup (mt, vr) multiplies M tile mt (up to 16 MB rows of X)
 // by the W_lm rows of vocabulary range vr on the matrix cores (bf16 operands,
-// fp32 sums).  The range's 16-column blocks are split evenly into chunks of
-// at most 16 blocks and, inside a chunk, evenly over the four waves, so every
-// wave owns at most four blocks (64 columns) of W_lm and streams them from
-// HBM straight into registers, five 64-deep k slices ahead (two for the
-// largest tile).  X reaches the
-// waves through LDS, one 64-deep k slice at a time: buffer loads write it
-// there directly, two slices ahead (three buffers).  Within a slice, lane
-// group g takes the 16 consecutive k of its 32-byte piece, eight per matrix
-// instruction, so that one wave's two loads cover whole 128-byte lines of W_lm.
+// fp32 sums).  The range's 16-column blocks are cut into chunks of 16 blocks
+// (the last one shorter), split evenly over the four waves, so every wave
+// owns at most four blocks (64 columns) of W_lm and streams them from
+// HBM straight into registers, three to seven 64-deep k slices ahead (more
+// for smaller tiles).  X reaches the waves through LDS, one 64-deep k slice
+// at a time, staged through registers two slices ahead (two buffers).
+// Within a slice, lane group g takes the 16 consecutive k of its 32-byte
+// piece, eight per matrix instruction, so that one wave's two loads cover
+// whole 128-byte lines of W_lm.
 // After the last slice of a chunk the waves spill their fp32 tiles to LDS
 // (where the X slices were), 32 columns at a time, and one thread per row
 // folds them, in column order, into that row's running list of its best KMAX
-// candidates (value keys and indices), which stays in LDS until the
-// workgroup ends.  A value enters only if it beats the list's last entry; an
-// insertion is a branch-free update of every entry at once.
+// candidates, which stays in LDS until the workgroup ends.  A value enters
+// only if it beats the list's last entry; an insertion is two min/max
+// operations per entry on an exact double that holds value key and column.
 //
 // k_lmhead_merge: one workgroup per row merges the row's n_vr sorted lists:
 // a bound that K words are known to reach (the best K-th word of any list,
@@ -42,10 +42,11 @@ constexpr int kLmChunkBlocks = kWaves * kLmWaveBlocks;    // 256 columns per chu
 constexpr int kLmSliceK = 64;                             // k per X slice
 // W slices held in registers per wave (also the unroll of the slice loop,
 // whose body is branch-free so that the compiler's memory-counter waits stay
-// exact and the loads of later slices stay in flight): six, three for the
-// largest tile, whose accumulators leave no room for more
-__host__ __device__ constexpr int lm_ring(int mb) { return mb >= 16 ? 3 : 6; }
-constexpr int kLmXBufs = 3;                               // X slice buffers in LDS
+// exact and the loads of later slices stay in flight): eight for tiles of up
+// to four m-blocks, six up to eight, four for the largest tiles, whose
+// accumulators leave less room
+__host__ __device__ constexpr int lm_ring(int mb) { return mb <= 4 ? 8 : (mb <= 8 ? 6 : 4); }
+constexpr int kLmXBufs = 2;                               // X slice buffers in LDS
 constexpr int kLmSlabCols = 32;                           // columns per epilogue pass
 constexpr int kLmSlabStride = kLmSlabCols + 1;
 constexpr int kLmMaxLists = 256;                          // vocabulary ranges per row
@@ -69,66 +70,66 @@ __host__ __device__ constexpr int lm_xrows(int mb) { return 16 * mb > 32 ? 16 * 
 template <int MB, int KMAX>
 struct LmLds {
     union {
-        // X slice: row, 16-byte piece; piece p of row r sits at p ^ (r & 7), so
-        // that the eight rows a matrix-operand read touches fall in distinct banks
+        // X slice: row, 16-byte slot; piece p of row r sits in slot
+        // p ^ ((r >> 1) & 7): the 16 rows one matrix-operand read touches
+        // then cover all 64 banks once (odd rows start 128 bytes in)
         u32x4_t xs[kLmXBufs][lm_xrows(MB)][8];
         // a chunk's fp32 tile, 32 columns at a time (between chunks)
         float slab[16 * MB][kLmSlabStride];
     };
-    // each row's running list of its best KMAX candidates, best first: value
-    // keys (0 = empty) and vocabulary indices; rows padded by 16 bytes so that
-    // 16-byte reads of consecutive rows fall in distinct banks
-    uint32_t lkey[16 * MB][KMAX + 4];
-    uint32_t lidx[16 * MB][KMAX + 4];
+    // each row's running list of its best KMAX candidates, best first, as
+    // lm_entry values (0 = empty); rows padded by 16 bytes so that 16-byte
+    // reads of consecutive rows fall in distinct banks
+    double lst[16 * MB][KMAX + 2];
 };
 
-// s_waitcnt immediate: vmcnt(n) (n <= 63), expcnt and lgkmcnt left alone
-__host__ __device__ constexpr int lm_vmcnt(int n) {
-    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
 
-// Blocks [b0, b1) of vocabulary range vr.
-__device__ __forceinline__ void lm_range(int nblk, int n_vr, int vr, int& b0, int& b1) {
-    b0 = (int)((int64_t)nblk * vr / n_vr);
-    b1 = (int)((int64_t)nblk * (vr + 1) / n_vr);
-}
 
-// Wave w's blocks [cb, cb + nbw) in chunk c of a range of R blocks from rb0
-// split into nch chunks.
-__device__ __forceinline__ void lm_wave_blocks(int rb0, int R, int nch, int c, int w, int& cb,
-                                               int& nbw) {
-    const int c0 = rb0 + (int)((int64_t)R * c / nch);
-    const int nb = rb0 + (int)((int64_t)R * (c + 1) / nch) - c0;
+// An even split of n items into parts: part k starts at k q + min(k, r) and
+// has q + (k < r) items, q = n / parts, r = n % parts (one division, once).
+struct LmSplit {
+    int q, r;
+    __device__ LmSplit(int n, int parts) : q(n / parts), r(n - (n / parts) * parts) {}
+    __device__ int start(int k) const { return k * q + min(k, r); }
+    __device__ int size(int k) const { return q + (k < r ? 1 : 0); }
+};
+
+// Wave w's blocks [cb, cb + nbw) of a chunk [c0, c0 + nb): an even split over
+// the four waves (nb <= 16).
+__device__ __forceinline__ void lm_wave_blocks(int c0, int nb, int w, int& cb, int& nbw) {
     cb = c0 + (nb * w) / kWaves;
     nbw = c0 + (nb * (w + 1)) / kWaves - cb;
 }
 
-// Insert (key xk, index xi) into a row's list, sorted by key, best first,
-// dropping the last entry.  The new index is larger than every listed one
-// (columns arrive in order), so an equal key stays ahead of it.  Every entry
-// decides on its own: those that stay ahead keep their place, the first one
-// that does not takes the new pair, the rest move down one.
-template <int KMAX>
-__device__ __forceinline__ void lm_insert(uint32_t (&lk)[KMAX], uint32_t (&li)[KMAX], uint32_t xk,
-                                          uint32_t xi) {
-    // all-ones where the entry stays ahead; bit selects keep this branch-free
-    uint32_t ahead[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) ahead[j] = 0u - (uint32_t)(lk[j] >= xk);
-#pragma unroll
-    for (int j = KMAX - 1; j > 0; --j) {
-        const uint32_t nk = (ahead[j - 1] & xk) | (~ahead[j - 1] & lk[j - 1]);
-        const uint32_t ni = (ahead[j - 1] & xi) | (~ahead[j - 1] & li[j - 1]);
-        lk[j] = (ahead[j] & lk[j]) | (~ahead[j] & nk);
-        li[j] = (ahead[j] & li[j]) | (~ahead[j] & ni);
-    }
-    lk[0] = (ahead[0] & lk[0]) | (~ahead[0] & xk);
-    li[0] = (ahead[0] & li[0]) | (~ahead[0] & xi);
+// A candidate as one exact double: its value key (order-preserving, so a
+// larger key is a larger value) times 2^21 plus 2^21 - 1 - its column offset
+// in the workgroup's range (< 2^21).  Comparing entries compares values, and
+// equal values put the lower column first; 53 bits hold both exactly.
+constexpr double kLmOffScale = 2097152.0;   // 2^21
+constexpr int kLmMaxRangeCols = 1 << 21;
+__device__ __forceinline__ double lm_entry(uint32_t key, int off) {
+    return (double)key * kLmOffScale + (double)(kLmMaxRangeCols - 1 - off);
+}
+__device__ __forceinline__ uint32_t lm_entry_key(double e) {
+    return (uint32_t)(e * (1.0 / kLmOffScale));      // exact: drops the offset part
 }
 
-// the value a candidate must beat to enter a list whose last key is `last`
-__device__ __forceinline__ float lm_floor(uint32_t last) {
-    return last ? value_of_key_f32(last) : -INFINITY;
+// Insert entry x into a row's list (best first), dropping the last entry:
+// entry j becomes the larger of itself and the smaller of x and entry j - 1.
+// Every entry is two independent min/max operations.
+template <int KMAX>
+__device__ __forceinline__ void lm_insert(double (&lw)[KMAX], double x) {
+    double nw[KMAX];
+    nw[0] = fmax(lw[0], x);
+#pragma unroll
+    for (int j = 1; j < KMAX; ++j) nw[j] = fmax(lw[j], fmin(lw[j - 1], x));
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) lw[j] = nw[j];
+}
+
+// the value a candidate must beat to enter a list whose last entry is `last`
+__device__ __forceinline__ float lm_floor(double last) {
+    return last > 0.0 ? value_of_key_f32(lm_entry_key(last)) : -INFINITY;
 }
 
 // Buffer resource over `bytes` bytes from `base` (raw, no stride): loads at
@@ -141,34 +142,37 @@ __device__ __forceinline__ u32x4_t lm_load(__amdgpu_buffer_rsrc_t r, uint32_t vo
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
-// X slices go from memory straight into LDS (buffer loads with the lds bit:
-// lane l of a wave's load writes the l-th 16 bytes of a 1 KB stretch).
-// Load q of wave w fills rows 8 (4 q + w) .. + 7 of a buffer; lane l takes
-// row 8 (4 q + w) + l / 8 and physical slot l % 8, which holds piece
-// (l % 8) ^ (row % 8) of the row.  The resource covers the tile's mrows rows,
-// so rows past M read as zero.
+// X pieces of one thread: piece q*256 + tid of a slice is row (q*256 + tid)/8,
+// 16-byte piece (q*256 + tid) % 8.  They are loaded into registers two
+// slices ahead and written to LDS with 16-byte stores.  The resource covers
+// the tile's mrows rows, so rows past M read as zero; rows past the tile
+// land in the spare rows of the buffer.
 template <int MB, int KMAX>
 struct LmX {
     static constexpr int XROWS = lm_xrows(MB);
-    static constexpr int NX = XROWS / 32;        // loads per wave per slice
-    static_assert(XROWS % 32 == 0, "whole 1 KB stretches per wave");
-    __device__ static void offsets(int d, uint32_t (&off)[NX]) {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    static constexpr int XP = XROWS * 8 / kWG;
+    static_assert(XROWS * 8 % kWG == 0, "whole pieces per thread");
+    __device__ static void offsets(int d, uint32_t (&off)[XP]) {
+        const int tid = threadIdx.x;
 #pragma unroll
-        for (int q = 0; q < NX; ++q) {
-            const int r = 8 * (4 * q + w) + (lane >> 3);
-            const int p = (lane & 7) ^ ((lane >> 3) & 7);
-            off[q] = (uint32_t)((r * d + p * 8) * 2);
+        for (int q = 0; q < XP; ++q) {
+            const int pi = q * kWG + tid;
+            off[q] = (uint32_t)(((pi >> 3) * d + (pi & 7) * 8) * 2);
         }
     }
-    __device__ static void load(__amdgpu_buffer_rsrc_t rx, const uint32_t (&off)[NX], int s,
-                                LmLds<MB, KMAX>& sm, int buf) {
-        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __device__ static void load(__amdgpu_buffer_rsrc_t rx, const uint32_t (&off)[XP], int s,
+                                u32x4_t (&xr)[XP]) {
 #pragma unroll
-        for (int q = 0; q < NX; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void*)&sm.xs[buf][8 * (4 * q + w)][0], 16,
-                (int)off[q], s * (kLmSliceK * 2), 0, 0);
+        for (int q = 0; q < XP; ++q) xr[q] = lm_load(rx, off[q], (uint32_t)s * (kLmSliceK * 2));
+    }
+    __device__ static void store(LmLds<MB, KMAX>& sm, int buf, const u32x4_t (&xr)[XP]) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int q = 0; q < XP; ++q) {
+            const int pi = q * kWG + tid;
+            const int r = pi >> 3, p = pi & 7;
+            sm.xs[buf][r][p ^ ((r >> 1) & 7)] = xr[q];
+        }
     }
 };
 
@@ -178,17 +182,13 @@ struct LmX {
 // rw covers the wave's rows of W_lm (rows past V read as zero).
 template <int MB, int KMAX, int NBW>
 __device__ __forceinline__ void lm_chunk(__amdgpu_buffer_rsrc_t rx,
-                                         const uint32_t (&xoff)[LmX<MB, KMAX>::NX],
+                                         const uint32_t (&xoff)[LmX<MB, KMAX>::XP],
                                          __amdgpu_buffer_rsrc_t rw, int d, LmLds<MB, KMAX>& sm,
                                          f32x4_t (&acc)[MB][kLmWaveBlocks]) {
     using XL = LmX<MB, KMAX>;
     constexpr int NB = NBW > 0 ? NBW : 1;
     constexpr int RING = lm_ring(MB);
-    static_assert(RING % kLmXBufs == 0, "the X buffers cycle inside the unroll");
-    // Loads a wave issues after slice s + 1's X: W of slices s - 1 + RING and
-    // s + RING, X of slice s + 2.  Waiting until no more are outstanding
-    // leaves slice s + 1 in LDS (memory counters complete in order).
-    constexpr int kWaitX = XL::NX + 4 * NBW;
+    static_assert(RING % kLmXBufs == 0, "the X buffers alternate inside the unroll");
     const int lane = threadIdx.x & 63;
     const int row = lane & 15, g = lane >> 4;
     const int ns = d / kLmSliceK;
@@ -204,63 +204,62 @@ __device__ __forceinline__ void lm_chunk(__amdgpu_buffer_rsrc_t rx,
             dst[j][1] = lm_load(rw, woff[j] + 16u, so);
         }
     };
-    // Step of slice s (ring slot u == s % RING, X buffer s % 3): load X slice
-    // s + 2, multiply (only for s < ns: past the end the loads repeat the last
-    // slice and nothing is added), load W slice s + RING into the slot just
-    // used, wait for X slice s + 1 and meet the other waves.
+    // Step of slice s (ring slot u == s % RING, X buffer s % 2): load X slice
+    // s + 2 into registers, multiply (only for s < ns: past the end the loads
+    // repeat the last slice and nothing is added), load W slice s + RING into
+    // the slot just used, write X slice s + 1 (loaded a step earlier) to the
+    // other buffer and meet the other waves.  X slice s + 1 was loaded before
+    // W slice s - 1 + RING, so waiting for it never waits for the W loads of
+    // the last two steps.
+    u32x4_t xr[2][XL::XP];
     auto step = [&](int s, int u) {
-        const int xb = u % kLmXBufs;
-        XL::load(rx, xoff, min(s + 2, ns - 1), sm, (u + 2) % kLmXBufs);
+        const int xb = u & 1;
+        XL::load(rx, xoff, min(s + 2, ns - 1), xr[xb]);
         if constexpr (NBW > 0) {
             if (s < ns) {
-                u32x4_t a0 = sm.xs[xb][row][(2 * g) ^ (row & 7)];
-                u32x4_t a1 = sm.xs[xb][row][(2 * g + 1) ^ (row & 7)];
+                u32x4_t a0 = sm.xs[xb][row][(2 * g) ^ ((row >> 1) & 7)];
+                u32x4_t a1 = sm.xs[xb][row][(2 * g + 1) ^ ((row >> 1) & 7)];
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
-                    // read block i + 1's operands while block i multiplies
+                    // read block i + 1's operands, then multiply block i; the
+                    // fences keep the reads a block ahead of their use
                     u32x4_t n0 = a0, n1 = a1;
                     if (i + 1 < MB) {
-                        n0 = sm.xs[xb][16 * (i + 1) + row][(2 * g) ^ (row & 7)];
-                        n1 = sm.xs[xb][16 * (i + 1) + row][(2 * g + 1) ^ (row & 7)];
+                        n0 = sm.xs[xb][16 * (i + 1) + row][(2 * g) ^ ((row >> 1) & 7)];
+                        n1 = sm.xs[xb][16 * (i + 1) + row][(2 * g + 1) ^ ((row >> 1) & 7)];
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // the two k halves of one block go to different
+                    // accumulators first, so no product waits for the last
 #pragma unroll
-                    for (int j = 0; j < NBW; ++j) {
+                    for (int j = 0; j < NBW; ++j)
                         acc[i][j] = mfma_bf16(as_bf16x8(a0), as_bf16x8(wr[u][j][0]), acc[i][j]);
+#pragma unroll
+                    for (int j = 0; j < NBW; ++j)
                         acc[i][j] = mfma_bf16(as_bf16x8(a1), as_bf16x8(wr[u][j][1]), acc[i][j]);
-                    }
-                    if (i + 1 < MB) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // 2 LDS reads
-                        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NBW, 0);  // products
-                    }
+                    __builtin_amdgcn_sched_barrier(0);
                     a0 = n0;
                     a1 = n1;
                 }
             }
             load_w(s + RING, wr[u]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(lm_vmcnt(kWaitX));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        XL::store(sm, xb ^ 1, xr[xb ^ 1]);
+        __syncthreads();
     };
 
-    // prologue: X slices 0 and 1, then W slices 0 .. RING-1; X slice 0 waited for
-    XL::load(rx, xoff, 0, sm, 0);
-    XL::load(rx, xoff, min(1, ns - 1), sm, 1);
+    // prologue: W slices 0 .. RING-1; X slice 0 to LDS, slice 1 in registers
 #pragma unroll
     for (int u = 0; u < RING; ++u) load_w(u, wr[u]);
-    constexpr int kWait0 = XL::NX + 2 * NBW * RING < 63 ? XL::NX + 2 * NBW * RING : 63;
-    __builtin_amdgcn_s_waitcnt(lm_vmcnt(kWait0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    XL::load(rx, xoff, 0, xr[0]);
+    XL::load(rx, xoff, min(1, ns - 1), xr[1]);
+    XL::store(sm, 0, xr[0]);
+    __syncthreads();
 
     for (int s0 = 0; s0 < ns; s0 += RING) {
 #pragma unroll
         for (int u = 0; u < RING; ++u) step(s0 + u, u);
     }
-    // the last steps' loads land before the buffers are reused
-    __builtin_amdgcn_s_waitcnt(lm_vmcnt(0));
-    __syncthreads();
 }
 
 template <int MB, int KMAX>
@@ -281,22 +280,25 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
     const int vr = item / a.n_mt, mt = item - vr * a.n_mt;
     const int64_t m0 = (int64_t)mt * ROWS;
     const int mrows = (int)min<int64_t>(ROWS, a.M - m0);
-    int rb0, rb1;
-    lm_range(a.nblk, a.n_vr, vr, rb0, rb1);
-    const int R = rb1 - rb0;
+    // vocabulary range vr: blocks [rb0, rb0 + R), cut into whole chunks of
+    // 16 blocks and a last, shorter one (every wave multiplies four blocks
+    // in a whole chunk, so no wave waits for another at the barriers)
+    const LmSplit ranges(a.nblk, a.n_vr);
+    const int rb0 = ranges.start(vr), R = ranges.size(vr);
     const int nch = (R + kLmChunkBlocks - 1) / kLmChunkBlocks;
     const int d = a.d;
-    const int col_end = min(16 * rb1, a.V);
+    const int col0 = 16 * rb0, col_end = min(16 * (rb0 + R), a.V);
 
     const __amdgpu_buffer_rsrc_t rx = lm_rsrc(a.X + m0 * d, (uint32_t)(mrows * d * 2));
-    uint32_t xoff[XL::NX];
+    uint32_t xoff[XL::XP];
     XL::offsets(d, xoff);
 
-    for (int e = tid; e < ROWS * (KMAX + 4); e += kWG) (&sm.lkey[0][0])[e] = 0u;
+    for (int e = tid; e < ROWS * (KMAX + 2); e += kWG) (&sm.lst[0][0])[e] = 0.0;
 
     for (int c = 0; c < nch; ++c) {
+        const int c0 = rb0 + c * kLmChunkBlocks, nbc = min(kLmChunkBlocks, R - c * kLmChunkBlocks);
         int cb, nbw;
-        lm_wave_blocks(rb0, R, nch, c, __builtin_amdgcn_readfirstlane(w), cb, nbw);
+        lm_wave_blocks(c0, nbc, __builtin_amdgcn_readfirstlane(w), cb, nbw);
         // the wave's W_lm rows 16 cb .. 16 (cb + nbw), cut at V
         const int wrows = max(0, min(16 * nbw, a.V - 16 * cb));
         const __amdgpu_buffer_rsrc_t rw =
@@ -318,15 +320,10 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
         // ---- epilogue: fold this chunk's columns into the row lists, in
         // column order (so a value equal to a kept one never displaces it) ----
         const int trow = min(tid, ROWS - 1);
-        uint32_t lk[KMAX], li[KMAX];
+        double lw[KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; j += 4) {
-            const u32x4_t k4 = *reinterpret_cast<const u32x4_t*>(&sm.lkey[trow][j]);
-            const u32x4_t i4 = *reinterpret_cast<const u32x4_t*>(&sm.lidx[trow][j]);
-            lk[j] = k4.x; lk[j + 1] = k4.y; lk[j + 2] = k4.z; lk[j + 3] = k4.w;
-            li[j] = i4.x; li[j + 1] = i4.y; li[j + 2] = i4.z; li[j + 3] = i4.w;
-        }
-        float floor_v = lm_floor(lk[KMAX - 1]);
+        for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[trow][j];
+        float floor_v = lm_floor(lw[KMAX - 1]);
         for (int p = 0; p < 2 * kWaves; ++p) {
             const int pw = p >> 1, h = p & 1;
             if (w == pw) {
@@ -341,7 +338,7 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
                                 h ? acc[i][2 + jj][v] : acc[i][jj][v];
             }
             int pcb, pnb;
-            lm_wave_blocks(rb0, R, nch, c, pw, pcb, pnb);
+            lm_wave_blocks(c0, nbc, pw, pcb, pnb);
             const int v0 = 16 * (pcb + 2 * h);
             const int ncols = max(0, min(min(pnb - 2 * h, 2) * 16, col_end - v0));
             __syncthreads();
@@ -360,8 +357,8 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
                     flagged &= flagged - 1u;
                     const float x = srow[cc];
                     if (x > floor_v) {
-                        lm_insert<KMAX>(lk, li, key_f32(__float_as_uint(x)), (uint32_t)(v0 + cc));
-                        floor_v = lm_floor(lk[KMAX - 1]);
+                        lm_insert<KMAX>(lw, lm_entry(key_f32(__float_as_uint(x)), v0 + cc - col0));
+                        floor_v = lm_floor(lw[KMAX - 1]);
                     }
                 }
             }
@@ -369,10 +366,7 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
         }
         if (tid < mrows) {
 #pragma unroll
-            for (int j = 0; j < KMAX; j += 4) {
-                *reinterpret_cast<u32x4_t*>(&sm.lkey[tid][j]) = u32x4_t{lk[j], lk[j + 1], lk[j + 2], lk[j + 3]};
-                *reinterpret_cast<u32x4_t*>(&sm.lidx[tid][j]) = u32x4_t{li[j], li[j + 1], li[j + 2], li[j + 3]};
-            }
+            for (int j = 0; j < KMAX; ++j) sm.lst[tid][j] = lw[j];
         }
         // the lists and the tile are read before the next chunk's X lands
         __syncthreads();
@@ -383,11 +377,16 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
         uint64_t* plist = a.part + ((m0 + tid) * a.n_vr + vr) * (int64_t)KMAX;
 #pragma unroll
         for (int j = 0; j < KMAX; j += 2) {
-            const uint32_t k0 = sm.lkey[tid][j], k1 = sm.lkey[tid][j + 1];
-            const uint64_t w0 = k0 ? cand_word(k0, sm.lidx[tid][j]) : 0ull;
-            const uint64_t w1 = k1 ? cand_word(k1, sm.lidx[tid][j + 1]) : 0ull;
-            *reinterpret_cast<u32x4_t*>(plist + j) =
-                u32x4_t{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+            uint64_t wd[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const double e = sm.lst[tid][j + q];
+                const uint32_t key = lm_entry_key(e);
+                const int off = kLmMaxRangeCols - 1 - (int)(e - (double)key * kLmOffScale);
+                wd[q] = key ? cand_word(key, (uint32_t)(col0 + off)) : 0ull;
+            }
+            *reinterpret_cast<u32x4_t*>(plist + j) = u32x4_t{
+                (uint32_t)wd[0], (uint32_t)(wd[0] >> 32), (uint32_t)wd[1], (uint32_t)(wd[1] >> 32)};
         }
     }
 }

@@ -222,8 +222,9 @@ df2_status dflash2_topk(const void* logits, int64_t rows, int32_t V,
  *   out_idx [M, K] int32  candidate token ids, best first
  *   out_val [M, K] float  their fp32 logits (a -0 logit is returned as +0)
  * dtype must be DF2_BF16 (DF2_F32 returns DF2_EUNSUPPORTED).  1 <= K <=
- * min(V, 64); d a multiple of 64 in [64, 32768]; M <= 2^24 (M == 0 enqueues
- * nothing); hidden and W_lm 16-byte aligned, outputs 4-byte aligned.
+ * min(V, 64); V <= 2^29; d a multiple of 64 in [64, 32768]; M <= 2^24
+ * (M == 0 enqueues nothing); hidden and W_lm 16-byte aligned, outputs
+ * 4-byte aligned.
  * Top-K order as everywhere (value descending, equal values to the lower
  * index); the fp32 sums differ from exact ones by at most a few units in
  * the last place of sum_k |W_lm[v][k] hidden[m][k]|, so near-equal logits at

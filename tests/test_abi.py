@@ -179,6 +179,7 @@ def test_lmhead_topk_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, -1, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
     assert f(FAKE, FAKE, 4, 0, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
     assert f(FAKE, FAKE, 1 << 25, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EUNSUPPORTED
+    assert f(FAKE, FAKE, 4, (1 << 29) + 1, 128, 1, 16, FAKE, FAKE, None) == DF2_EUNSUPPORTED
     # pointers and alignment
     assert f(None, FAKE, 4, 1000, 128, 1, 16, FAKE, FAKE, None) == DF2_EINVAL
     assert f(FAKE, FAKE, 4, 1000, 128, 1, 16, FAKE, None, None) == DF2_EINVAL
