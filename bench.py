@@ -33,6 +33,12 @@ Prints ONE JSON line:
               the eager outputs;
   project     the gate projection alone at the timed workload's shape: µs per
               call and TFLOP/s against the bf16 matrix-core peak;
+  lmhead      the drafter's LM head fused with top-K (dflash2_lmhead_topk) at
+              the concurrency-32 and batch-1 shapes: µs per call (HIP events,
+              both launches), its roofline on the bytes it must read (the
+              V x d bf16 weight once, plus hidden states and outputs) and
+              TFLOP/s against the bf16 matrix-core peak, with the CPU oracle
+              on a few sampled rows;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, one
               thread per usable host core (at most 16), and single-threaded.
 """
@@ -55,6 +61,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("common.hpp", "topk.hpp", "gate.hpp", "pairs.hpp", "walk.hpp", "dflash2.hip")
+LMHEAD_SOURCES = ("common.hpp", "lmhead.hpp")
 
 
 def log(*a):
@@ -75,24 +82,32 @@ def algorithmic_bytes(wl) -> int:
     return logits + hidden + w + rows + out
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str = "select") -> str:
+    """Hash of the device code a family of kernels is built from (for the
+    selector, dflash2.hip up to its host-side part), so that counter runs are
+    only reused while that code is unchanged."""
+    files = {"select": KERNEL_SOURCES, "lmhead": LMHEAD_SOURCES}[family]
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "draft_selection_topk16_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            data = fh.read()
+        if f == "dflash2.hip":
+            data = data.split(b"// Host side.")[0]
+        h.update(data)
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, family: str = "select"):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
+    were taken on the current kernel sources; else None.  LM-head entries are
+    keyed "lmhead/<workload>"."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    entry = t.get(workload)
-    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+    entry = t.get(workload if family == "select" else "lmhead/" + workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash(family):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -365,6 +380,68 @@ def time_project(wl, steps: int, warmup: int, rotate_mb: float):
             "algorithmic_bytes": ab, "hbm_frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def lmhead_algorithmic_bytes(M: int, V: int, d: int, K: int) -> int:
+    """Bytes the fused LM head must move: the weight once, the hidden states,
+    and the candidate outputs (index and value)."""
+    return 2 * V * d + 2 * M * d + 8 * M * K
+
+
+def time_lmhead(name: str, steps: int, warmup: int, cpu_rows: int = 2):
+    """dflash2_lmhead_topk on the LM-head inputs of workload `name` (hidden
+    states [B*P, d] and W_lm [V, d], bf16); HIP events around each call on
+    the launch stream.  The weight (>= 0.78 GB) is far beyond the Infinity
+    Cache, so it streams from HBM on every call without rotation."""
+    import torch
+    import numpy as np
+    import oracle
+    import draft_selection_topk16_amd as df2
+    from draft_selection_topk16_amd import synth
+    wl = synth.WORKLOADS[name]
+    if wl.dtype != "bf16":
+        wl = wl.with_(dtype="bf16")
+    li = synth.make_lmhead_inputs(wl)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    X, W = dev(li.X), dev(li.W_lm)
+    M, V, d, K = wl.rows, wl.V, wl.d, wl.K
+    for _ in range(warmup):
+        df2.lmhead_topk(X, W, K)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        df2.lmhead_topk(X, W, K)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    us = statistics.fmean(times)
+    ab = lmhead_algorithmic_bytes(M, V, d, K)
+    flops = 2.0 * M * V * d
+    achieved = ab / (us * 1e-6) / 1e9
+    # the oracle on a few rows (float64 dot products and a full sort per row)
+    X32, W32 = li.f32()
+    rows = np.arange(min(cpu_rows, M))
+    t0 = time.time()
+    oracle.lmhead_topk(X32, W32, K, rows=rows)
+    et = time.time() - t0
+    del X, W
+    torch.cuda.empty_cache()
+    return {"workload": "%s LM head + top-%d: M=B*P=%d V=%d d=%d bf16, fp32 accumulation"
+                        % (name, K, M, V, d),
+            "us_per_call": us, "us_min": min(times), "positions_per_s": M / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(name, "lmhead"),
+                         "kernel": "k_lmhead + k_lmhead_merge (one dflash2_lmhead_topk call)",
+                         "algorithmic_bytes_per_launch": ab},
+            "tflops": flops / (us * 1e-6) / 1e12, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "cpu_oracle": {"value": len(rows) / et, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                           "sample": "%d rows of the same workload, %.1f s" % (len(rows), et)}}
+
+
 def copy_calibration(mb: float, reps: int):
     """A plain device-to-device copy of known size, for scaling counters."""
     import torch
@@ -392,7 +469,9 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch-8 and stress lines")
     ap.add_argument("--no-project", action="store_true")
-    ap.add_argument("--only", choices=["project"], default=None,
+    ap.add_argument("--no-lmhead", action="store_true")
+    ap.add_argument("--lmhead-steps", type=int, default=20)
+    ap.add_argument("--only", choices=["project", "lmhead"], default=None,
                     help="time one stage alone (for counter runs) and print its JSON object")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
     args = ap.parse_args()
@@ -419,6 +498,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if args.only == "project":
         print(json.dumps(time_project(wl, args.steps, args.warmup, args.rotate_mb)), flush=True)
+        return
+    if args.only == "lmhead":
+        print(json.dumps(time_lmhead(wl.name, args.steps, args.warmup, cpu_rows=1)), flush=True)
         return
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
     walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy", "sample")
@@ -517,6 +599,11 @@ def main():
     if not args.no_project:
         log("timing the gate projection alone at %s" % wl.name)
         out["project"] = time_project(wl, args.steps, args.warmup, args.rotate_mb)
+    if not args.no_lmhead:
+        out["lmhead"] = {}
+        for key, name in (("b32", args.workload), ("b1", args.b1_workload)):
+            log("timing the LM head fused with top-K at %s" % name)
+            out["lmhead"][key] = time_lmhead(name, args.lmhead_steps, 3)
     if not args.no_conv:
         out["conv"] = {}
         for name in synth.CONV_WORKLOADS:

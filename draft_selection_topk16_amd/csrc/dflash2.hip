@@ -1401,17 +1401,26 @@ df2_status launch_lmhead(const LmPlan& pl, const LmArgs& a, hipStream_t stream) 
     if (!launched) return fail(DF2_EUNSUPPORTED, "no LM-head kernel for this tile");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "dflash2_lmhead_topk launch");
+    const void* merge_fn = pl.kmax == 16 ? reinterpret_cast<const void*>(&k_lmhead_merge<16>)
+                           : pl.kmax == 32 ? reinterpret_cast<const void*>(&k_lmhead_merge<32>)
+                                           : reinterpret_cast<const void*>(&k_lmhead_merge<64>);
     if (pl.merge_lds > 65536) {
-        static std::once_flag once;
-        static hipError_t attr = hipSuccess;
-        std::call_once(once, [] {
-            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lmhead_merge),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(kLmMaxLists * 64 * sizeof(uint64_t)));
-        });
-        if (attr != hipSuccess) return hip_fail(attr, "hipFuncSetAttribute (LM-head merge)");
+        static std::mutex mu;
+        static std::map<const void*, hipError_t> done;
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = done.find(merge_fn);
+        if (it == done.end())
+            it = done.emplace(merge_fn, hipFuncSetAttribute(merge_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                            (int)(kLmMaxLists * 64 * sizeof(uint64_t))))
+                     .first;
+        if (it->second != hipSuccess) return hip_fail(it->second, "hipFuncSetAttribute (LM-head merge)");
     }
-    hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)a.M), block, pl.merge_lds, stream, a);
+    if (pl.kmax == 16)
+        hipLaunchKernelGGL(k_lmhead_merge<16>, dim3((unsigned)a.M), block, pl.merge_lds, stream, a);
+    else if (pl.kmax == 32)
+        hipLaunchKernelGGL(k_lmhead_merge<32>, dim3((unsigned)a.M), block, pl.merge_lds, stream, a);
+    else
+        hipLaunchKernelGGL(k_lmhead_merge<64>, dim3((unsigned)a.M), block, pl.merge_lds, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "dflash2_lmhead_topk merge launch");
     return DF2_OK;

@@ -18,11 +18,16 @@
 // piece, eight per matrix instruction, so that one wave's two loads cover
 // whole 128-byte lines of W_lm.
 // After the last slice of a chunk the waves spill their fp32 tiles to LDS
-// (where the X slices were), 32 columns at a time, and one thread per row
-// folds them, in column order, into that row's running list of its best KMAX
-// candidates, which stays in LDS until the workgroup ends.  A value enters
-// only if it beats the list's last entry; an insertion is two min/max
-// operations per entry on an exact double that holds value key and column.
+// and one thread per row folds them, in column order, into that row's
+// running list of its best KMAX candidates, which stays in LDS until the
+// workgroup ends.  Tiles of up to 64 rows: every wave folds its own 64
+// columns into its own lists (one lane per row, no workgroup barrier), and
+// the four lists of a row are merged at the end; larger tiles: the waves
+// spill 32 columns at a time where the X slices were, and one thread per row
+// folds them all.  An empty list is filled by sorting 32 columns at once;
+// after that a value enters only if it beats the list's last entry, and an
+// insertion is two min/max operations per entry on an exact double that
+// holds value key and column.
 //
 // k_lmhead_merge: one workgroup per row merges the row's n_vr sorted lists:
 // a bound that K words are known to reach (the best K-th word of any list,
@@ -47,8 +52,12 @@ constexpr int kLmSliceK = 64;                             // k per X slice
 // accumulators leave less room
 __host__ __device__ constexpr int lm_ring(int mb) { return mb <= 4 ? 8 : (mb <= 8 ? 6 : 4); }
 constexpr int kLmXBufs = 2;                               // X slice buffers in LDS
-constexpr int kLmSlabCols = 32;                           // columns per epilogue pass
-constexpr int kLmSlabStride = kLmSlabCols + 1;
+constexpr int kLmSlabCols = 32;                           // columns per fold
+// tiles of up to four m-blocks (64 rows; two for 64-entry lists, whose four
+// copies would not fit in LDS): every wave folds its own columns into its
+// own lists, one lane per row; larger tiles: one thread per row folds the
+// whole chunk, 32 columns at a time
+__host__ __device__ constexpr bool lm_wide(int mb, int kmax) { return mb <= (kmax <= 32 ? 4 : 2); }
 constexpr int kLmMaxLists = 256;                          // vocabulary ranges per row
 
 struct LmArgs {
@@ -74,16 +83,17 @@ struct LmLds {
         // p ^ ((r >> 1) & 7): the 16 rows one matrix-operand read touches
         // then cover all 64 banks once (odd rows start 128 bytes in)
         u32x4_t xs[kLmXBufs][lm_xrows(MB)][8];
-        // a chunk's fp32 tile, 32 columns at a time (between chunks)
-        float slab[16 * MB][kLmSlabStride];
+        // large tiles: the chunk's fp32 tile, 32 columns at a time
+        float slab[lm_wide(MB, KMAX) ? 1 : 16 * MB][kLmSlabCols + 1];
     };
-    // each row's running list of its best KMAX candidates, best first, as
+    // small tiles: each wave's own 64 columns of the chunk and its own
+    // candidate lists (folded without workgroup barriers)
+    float wslab[lm_wide(MB, KMAX) ? kWaves : 1][lm_wide(MB, KMAX) ? 16 * MB : 1][16 * kLmWaveBlocks + 1];
+    // each row's running list(s) of its best KMAX candidates, best first, as
     // lm_entry values (0 = empty); rows padded by 16 bytes so that 16-byte
     // reads of consecutive rows fall in distinct banks
-    double lst[16 * MB][KMAX + 2];
+    double lst[lm_wide(MB, KMAX) ? kWaves : 1][16 * MB][KMAX + 2];
 };
-
-
 
 // An even split of n items into parts: part k starts at k q + min(k, r) and
 // has q + (k < r) items, q = n / parts, r = n % parts (one division, once).
@@ -140,6 +150,79 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t lm_rsrc(const void* base, uint
 }
 __device__ __forceinline__ u32x4_t lm_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// Sort 32 entries, best first (bitonic network: every compare-exchange is
+// one max and one min, the exchanges of a stage independent).
+__device__ __forceinline__ void lm_sort32(double (&e)[32]) {
+#pragma unroll
+    for (int k = 2; k <= 32; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const double hi = fmax(e[i], e[l]), lo = fmin(e[i], e[l]);
+                    const bool desc = (i & k) == 0;
+                    e[i] = desc ? hi : lo;
+                    e[l] = desc ? lo : hi;
+                }
+            }
+}
+
+// Best KMAX of two sorted lists (best first), into a: the elementwise larger
+// of a and reversed b holds them as a bitonic sequence, which a half-cleaner
+// network sorts.  b is read through `bk(j)`.
+template <int KMAX, typename BK>
+__device__ __forceinline__ void lm_merge_top(double (&a)[KMAX], BK&& bk) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) a[j] = fmax(a[j], bk(KMAX - 1 - j));
+#pragma unroll
+    for (int h = KMAX / 2; h > 0; h >>= 1)
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i)
+            if ((i & h) == 0) {
+                const double hi = fmax(a[i], a[i + h]), lo = fmin(a[i], a[i + h]);
+                a[i] = hi;
+                a[i + h] = lo;
+            }
+}
+
+// Fold 32 consecutive columns of one row (ncols of them valid; column cc has
+// offset off0 + cc in the workgroup's range) into the row's list.  An empty
+// list is filled by sorting the 32 at once; otherwise each column that
+// beats the list's last entry is inserted, in column order.
+template <int KMAX>
+__device__ __forceinline__ void lm_fold32(double (&lw)[KMAX], float& floor_v,
+                                          const float* __restrict__ srow, int ncols, int off0) {
+    float xv[kLmSlabCols];
+#pragma unroll
+    for (int cc = 0; cc < kLmSlabCols; ++cc) xv[cc] = srow[cc];
+    if (lw[0] == 0.0) {
+        double e[kLmSlabCols];
+#pragma unroll
+        for (int cc = 0; cc < kLmSlabCols; ++cc)
+            e[cc] = cc < ncols ? lm_entry(key_f32(__float_as_uint(xv[cc])), off0 + cc) : 0.0;
+        lm_sort32(e);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) lw[j] = j < kLmSlabCols ? e[j] : 0.0;
+        floor_v = lm_floor(lw[KMAX - 1]);
+        return;
+    }
+    uint32_t flagged = 0;
+#pragma unroll
+    for (int cc = 0; cc < kLmSlabCols; ++cc)
+        flagged |= (cc < ncols && xv[cc] > floor_v) ? (1u << cc) : 0u;
+    while (flagged) {
+        const int cc = __builtin_ctz(flagged);
+        flagged &= flagged - 1u;
+        const float x = srow[cc];
+        if (x > floor_v) {
+            lm_insert<KMAX>(lw, lm_entry(key_f32(__float_as_uint(x)), off0 + cc));
+            floor_v = lm_floor(lw[KMAX - 1]);
+        }
+    }
 }
 
 // X pieces of one thread: piece q*256 + tid of a slice is row (q*256 + tid)/8,
@@ -268,7 +351,6 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
     constexpr int ROWS = 16 * MB;
     using XL = LmX<MB, KMAX>;
     __shared__ LmLds<MB, KMAX> sm;
-    static_assert(sizeof(sm.slab) <= sizeof(sm.xs), "the tile fits where the X slices were");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int row = lane & 15, g = lane >> 4;
 
@@ -293,7 +375,7 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
     uint32_t xoff[XL::XP];
     XL::offsets(d, xoff);
 
-    for (int e = tid; e < ROWS * (KMAX + 2); e += kWG) (&sm.lst[0][0])[e] = 0.0;
+    for (int e = tid; e < (int)(sizeof(sm.lst) / sizeof(double)); e += kWG) (&sm.lst[0][0][0])[e] = 0.0;
 
     for (int c = 0; c < nch; ++c) {
         const int c0 = rb0 + c * kLmChunkBlocks, nbc = min(kLmChunkBlocks, R - c * kLmChunkBlocks);
@@ -319,57 +401,83 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
 
         // ---- epilogue: fold this chunk's columns into the row lists, in
         // column order (so a value equal to a kept one never displaces it) ----
-        const int trow = min(tid, ROWS - 1);
-        double lw[KMAX];
+        if constexpr (lm_wide(MB, KMAX)) {
+            // the wave spills its blocks to its own slab; value v of block
+            // (i, j): row 16 i + 4 g + v, column 16 j + row.  Lane l then folds
+            // row l of it into its list of that row.
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[trow][j];
-        float floor_v = lm_floor(lw[KMAX - 1]);
-        for (int p = 0; p < 2 * kWaves; ++p) {
-            const int pw = p >> 1, h = p & 1;
-            if (w == pw) {
-                // value v of block (i, j): row 16 i + 4 g + v, column 16 j + row
+            for (int j = 0; j < kLmWaveBlocks; ++j) {
+                if (j < nbw) {
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
+                    for (int i = 0; i < MB; ++i)
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            sm.slab[16 * i + 4 * g + v][16 * jj + row] =
-                                h ? acc[i][2 + jj][v] : acc[i][jj][v];
-            }
-            int pcb, pnb;
-            lm_wave_blocks(c0, nbc, pw, pcb, pnb);
-            const int v0 = 16 * (pcb + 2 * h);
-            const int ncols = max(0, min(min(pnb - 2 * h, 2) * 16, col_end - v0));
-            __syncthreads();
-            if (tid < mrows && ncols > 0) {
-                // all 32 columns at once (columns past ncols are never flagged)
-                const float* srow = sm.slab[tid];
-                float xv[kLmSlabCols];
-#pragma unroll
-                for (int cc = 0; cc < kLmSlabCols; ++cc) xv[cc] = srow[cc];
-                uint32_t flagged = 0;
-#pragma unroll
-                for (int cc = 0; cc < kLmSlabCols; ++cc)
-                    flagged |= (cc < ncols && xv[cc] > floor_v) ? (1u << cc) : 0u;
-                while (flagged) {
-                    const int cc = __builtin_ctz(flagged);
-                    flagged &= flagged - 1u;
-                    const float x = srow[cc];
-                    if (x > floor_v) {
-                        lm_insert<KMAX>(lw, lm_entry(key_f32(__float_as_uint(x)), v0 + cc - col0));
-                        floor_v = lm_floor(lw[KMAX - 1]);
-                    }
+                            sm.wslab[w][16 * i + 4 * g + v][16 * j + row] = acc[i][j][v];
                 }
             }
-            __syncthreads();
-        }
-        if (tid < mrows) {
+            wave_sync();
+            if (lane < mrows) {
+                double lw[KMAX];
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j) sm.lst[tid][j] = lw[j];
+                for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[w][lane][j];
+                float floor_v = lm_floor(lw[KMAX - 1]);
+                const int wcols = min(16 * nbw, col_end - 16 * cb);   // the wave's valid columns
+                for (int q = 0; q * kLmSlabCols < wcols; ++q)
+                    lm_fold32<KMAX>(lw, floor_v, &sm.wslab[w][lane][q * kLmSlabCols],
+                                    min(kLmSlabCols, wcols - q * kLmSlabCols),
+                                    16 * cb - col0 + q * kLmSlabCols);
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) sm.lst[w][lane][j] = lw[j];
+            }
+        } else {
+            const int trow = min(tid, ROWS - 1);
+            double lw[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[0][trow][j];
+            float floor_v = lm_floor(lw[KMAX - 1]);
+            for (int p = 0; p < 2 * kWaves; ++p) {
+                const int pw = p >> 1, h = p & 1;
+                if (w == pw) {
+                    // value v of block (i, j): row 16 i + 4 g + v, column 16 j + row
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                sm.slab[16 * i + 4 * g + v][16 * jj + row] =
+                                    h ? acc[i][2 + jj][v] : acc[i][jj][v];
+                }
+                int pcb, pnb;
+                lm_wave_blocks(c0, nbc, pw, pcb, pnb);
+                const int v0 = 16 * (pcb + 2 * h);
+                const int ncols = max(0, min(min(pnb - 2 * h, 2) * 16, col_end - v0));
+                __syncthreads();
+                if (tid < mrows && ncols > 0) lm_fold32<KMAX>(lw, floor_v, sm.slab[tid], ncols, v0 - col0);
+                __syncthreads();
+            }
+            if (tid < mrows) {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) sm.lst[0][tid][j] = lw[j];
+            }
         }
         // the lists and the tile are read before the next chunk's X lands
         __syncthreads();
+    }
+
+    // small tiles: merge each row's four wave lists into the first
+    if constexpr (lm_wide(MB, KMAX)) {
+        __syncthreads();
+        if (tid < mrows) {
+            double lw[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[0][tid][j];
+#pragma unroll
+            for (int u = 1; u < kWaves; ++u)
+                lm_merge_top<KMAX>(lw, [&](int j) { return sm.lst[u][tid][j]; });
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) sm.lst[0][tid][j] = lw[j];
+        }
     }
 
     // hand the lists to the merge as candidate words (0 = empty)
@@ -380,7 +488,7 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
             uint64_t wd[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const double e = sm.lst[tid][j + q];
+                const double e = sm.lst[0][tid][j + q];
                 const uint32_t key = lm_entry_key(e);
                 const int off = kLmMaxRangeCols - 1 - (int)(e - (double)key * kLmOffScale);
                 wd[q] = key ? cand_word(key, (uint32_t)(col0 + off)) : 0ull;
@@ -398,59 +506,61 @@ struct LmMergeLds {
     uint32_t m;
 };
 
+// One workgroup per row; thread l holds list l whole (one round of loads).
+template <int KMAX>
 __global__ __launch_bounds__(kWG) void k_lmhead_merge(LmArgs a) {
     extern __shared__ uint64_t surv[];      // up to n_vr * K words
     __shared__ LmMergeLds sm;
     const int tid = threadIdx.x;
     const int64_t mrow = blockIdx.x;
-    const int nl = a.n_vr, K = a.K, ks = a.kstride;
-    const uint64_t* __restrict__ L = a.part + mrow * nl * (int64_t)ks;
+    const int nl = a.n_vr, K = a.K;
+    const uint64_t* __restrict__ L = a.part + mrow * nl * (int64_t)KMAX;
     if (tid == 0) {
         sm.tk = 0ull;
         sm.th = 0ull;
         sm.m = 0u;
     }
+    uint64_t x[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) x[j] = 0ull;
+    if (tid < nl) {
+#pragma unroll
+        for (int j = 0; j < KMAX; j += 2) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(L + (int64_t)tid * KMAX + j);
+            x[j] = ((uint64_t)v.y << 32) | v.x;
+            x[j + 1] = ((uint64_t)v.w << 32) | v.z;
+        }
+    }
+    uint64_t kth = 0ull;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) kth = (j == K - 1) ? x[j] : kth;
+    const uint64_t head = x[0];
     __syncthreads();
     // bound 1: the best K-th word of any list (K words reach it)
-    uint64_t head = 0ull;
-    if (tid < nl) {
-        head = L[(int64_t)tid * ks];
-        const uint64_t kth = L[(int64_t)tid * ks + K - 1];
-        __hip_atomic_fetch_max(&sm.tk, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    if (tid < nl) __hip_atomic_fetch_max(&sm.tk, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     sm.heads[tid] = head;
     __syncthreads();
     // bound 2: the K-th best head (K heads reach it)
     if (nl >= K && tid < nl) {
+        // all 256 slots (empty lists have head 0, which ranks no head)
         int rank = 0;
-        for (int u = 0; u < nl; ++u) rank += sm.heads[u] > head ? 1 : 0;
+#pragma unroll 32
+        for (int u = 0; u < kLmMaxLists; ++u) rank += sm.heads[u] > head ? 1 : 0;
         if (rank == K - 1) sm.th = head;
     }
     __syncthreads();
     uint64_t T = sm.tk > sm.th ? sm.tk : sm.th;
     T = T ? T : 1ull;
-    // each list that reaches the bound hands on its words that reach it (a
-    // prefix: lists are sorted), eight at a time
-    if (tid < nl && head >= T) {
-        const uint64_t* lp = L + (int64_t)tid * ks;
-        for (int k0 = 0; k0 < K; k0 += 8) {
-            uint64_t x[8];
+    // each list hands on its words that reach the bound (a prefix of it)
+    int c = 0;
 #pragma unroll
-            for (int q = 0; q < 8; q += 2) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lp + k0 + q);
-                x[q] = ((uint64_t)v.y << 32) | v.x;
-                x[q + 1] = ((uint64_t)v.w << 32) | v.z;
-            }
-            int c = 0;
+    for (int j = 0; j < KMAX; ++j) c += (j < K && x[j] >= T) ? 1 : 0;
+    if (c > 0) {
+        const uint32_t base = __hip_atomic_fetch_add(&sm.m, (uint32_t)c, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) c += (k0 + q < K && x[q] >= T) ? 1 : 0;
-            const uint32_t base = __hip_atomic_fetch_add(&sm.m, (uint32_t)c, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (q < c) surv[base + q] = x[q];
-            if (c < 8) break;
-        }
+        for (int j = 0; j < KMAX; ++j)
+            if (j < c) surv[base + j] = x[j];
     }
     __syncthreads();
     const int m = (int)sm.m;
@@ -458,7 +568,10 @@ __global__ __launch_bounds__(kWG) void k_lmhead_merge(LmArgs a) {
         const int si = s0 + tid;
         const uint64_t y = (si < m) ? surv[si] : 0ull;
         int rank = 0;
-        for (int u = 0; u < m; ++u) rank += surv[u] > y ? 1 : 0;
+        for (int u0 = 0; u0 < m; u0 += 16) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) rank += (u0 + u < m && surv[min(u0 + u, m - 1)] > y) ? 1 : 0;
+        }
         if (si < m && rank < K) {
             a.out_idx[mrow * K + rank] = (int32_t)cand_index(y);
             a.out_val[mrow * K + rank] = value_of_key_f32((uint32_t)(y >> 32));
