@@ -23,7 +23,7 @@ WALKS = {"viterbi": 0, "greedy": 1}
 
 # df2_plan_knob
 PLAN_KNOBS = {"segment_wgs": 0, "chunk_vectors": 1, "merge_words": 2, "gate_slices": 3,
-              "conv_slices": 4, "launches": 5, "lm_ranges": 6}
+              "conv_slices": 4, "launches": 5, "lm_ranges": 6, "gate_giveup": 7}
 
 EXPORTED = (
     "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_select_noalloc",

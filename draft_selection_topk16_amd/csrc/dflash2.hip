@@ -95,6 +95,11 @@ struct Params {
     const float* u;       // [B, P] uniforms of the sampling walk
     float* out_q;         // [B, P] probabilities of the sampled choices
     float inv_tau;        // 1 / temperature of the sampling walk
+    // The row merges' gate wait: the arrivals it needs beyond the gate's own
+    // (0; 1 only to force a give-up when testing failure handling) and its
+    // bound in sleeps.
+    uint32_t gate_extra = 0;
+    uint32_t gate_spins = 1u << 20;
 };
 
 // Walk modes inside the launch: the two of df2_walk, and the sampling walk.
@@ -215,7 +220,7 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
     // now), its S partials are loaded while the merge runs and summed in
     // slice order.
     const int mt = (int)(row / p.gm_rows);
-    const uint32_t need = (uint32_t)(p.ntiles * p.S);
+    const uint32_t need = (uint32_t)(p.ntiles * p.S) + p.gate_extra;
     const int S = p.S;
     uint32_t hp[kMaxFusedSlices];
     auto issue_h = [&](int k) {
@@ -243,7 +248,7 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
                     uint32_t it = 0;
                     while (xload(&p.gate_cnt[mt]) < need) {
                         __builtin_amdgcn_s_sleep(2);
-                        if (++it > (1u << 20)) {
+                        if (++it > p.gate_spins) {
                             atomicOr(p.err, 4u);
                             break;
                         }
@@ -579,6 +584,7 @@ struct Overrides {
     int conv_s = 0;       // k slices of the convolution's correction GEMM
     int launches = 0;     // dflash2_select: 1 = one fused launch, 2 = scan then tail
     int lm_ranges = 0;    // vocabulary ranges of the LM head (1..256)
+    int gate_giveup = 0;  // 1: the row merges' gate wait gives up (failure-handling tests)
 };
 Overrides g_over;
 
@@ -702,6 +708,8 @@ void plan_gate(Plan& pl, int64_t M, int d, int r, const Overrides& ov) {
     if (ov.gate_s >= 1 && ov.gate_s <= std::min(KS, kMaxFusedSlices)) S = ov.gate_s;
     p.S = S;
     p.n_gate = p.mtiles * p.ntiles * S;
+    p.gate_extra = ov.gate_giveup ? 1u : 0u;
+    p.gate_spins = ov.gate_giveup ? 64u : (1u << 20);
     p.d = d;
     p.r = r;
 }
@@ -1319,6 +1327,10 @@ df2_status dflash2_plan_override(df2_plan_knob knob, int32_t value) {
         case DF2_PLAN_LM_RANGES:
             if (value > kLmMaxLists) return fail(DF2_EINVAL, "LM-head ranges must be in [0, 256]");
             g_over.lm_ranges = value;
+            break;
+        case DF2_PLAN_GATE_GIVEUP:
+            if (value > 1) return fail(DF2_EINVAL, "gate give-up must be 0 or 1");
+            g_over.gate_giveup = value;
             break;
         default: return fail(DF2_EINVAL, "unknown plan knob");
     }

@@ -81,7 +81,11 @@ typedef enum {
     DF2_PLAN_GATE_SLICES = 3,   /* slices of d of the gate projection (<= 16) */
     DF2_PLAN_CONV_SLICES = 4,   /* k slices of the convolution's correction GEMM */
     DF2_PLAN_LAUNCHES = 5,      /* dflash2_select: 1 = one fused launch, 2 = scan then tail */
-    DF2_PLAN_LM_RANGES = 6      /* dflash2_lmhead_topk: vocabulary ranges (<= 256) */
+    DF2_PLAN_LM_RANGES = 6,     /* dflash2_lmhead_topk: vocabulary ranges (<= 256) */
+    DF2_PLAN_GATE_GIVEUP = 7    /* failure-handling tests only: 1 = in dflash2_select
+                                   the row merges wait for one gate arrival more than
+                                   will come, give up after 64 sleeps and raise flag
+                                   bit 2; that call's outputs are not valid */
 } df2_plan_knob;
 
 typedef enum {
@@ -334,7 +338,10 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base,
  * [0, V) was replaced by 0; bit 1: a cand_idx entry outside [0, V) was
  * replaced by 0; bit 2: a pair-score job of dflash2_select gave up waiting
  * for its gate rows, which only a fault elsewhere can cause, and its scores
- * are then unreliable).  Returns DF2_OK, or DF2_EHIP.
+ * are then unreliable).  A raised flag can leave a late gate arrival
+ * counted in the stream's scratch, so after reporting one the next call on
+ * that stream clears all its arrival counters before it launches.  Returns
+ * DF2_OK, or DF2_EHIP.
  */
 df2_status dflash2_device_error(hipStream_t stream, uint32_t* flags);
 

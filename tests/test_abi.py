@@ -223,3 +223,20 @@ def test_select_noalloc_checks_arguments_like_select(lib):
     dims = Dims(0, 7, 32000, 1024, 256, 1)
     assert lib.dflash2_select_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
                                       FAKE, FAKE, None) == DF2_OK
+
+
+def test_plan_knobs_match_header_and_reject_bad_values(lib):
+    import re
+    from draft_selection_topk16_amd.binding import PLAN_KNOBS
+    text = open(HEADER).read()
+    body = text[text.index("typedef enum {\n    DF2_PLAN_SEGMENT_WGS"):]
+    body = body[:body.index("} df2_plan_knob;")]
+    declared = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"DF2_PLAN_(\w+) = (\d+)", body)}
+    assert declared == PLAN_KNOBS
+    assert lib.dflash2_plan_override(max(PLAN_KNOBS.values()) + 1, 1) == DF2_EINVAL   # unknown knob
+    assert lib.dflash2_plan_override(0, -1) == DF2_EINVAL                             # negative
+    assert lib.dflash2_plan_override(PLAN_KNOBS["launches"], 3) == DF2_EINVAL
+    assert lib.dflash2_plan_override(PLAN_KNOBS["chunk_vectors"], 3) == DF2_EINVAL
+    assert lib.dflash2_plan_override(PLAN_KNOBS["gate_giveup"], 2) == DF2_EINVAL
+    for k in PLAN_KNOBS.values():
+        assert lib.dflash2_plan_override(k, 0) == DF2_OK

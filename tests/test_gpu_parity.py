@@ -482,6 +482,30 @@ def test_prev_tok_out_of_range_sets_flag():
     check_select(path.cpu().numpy(), score.cpu().numpy(), run_oracle(x), TOL["f32"], "bad prev")
 
 
+@pytest.mark.parametrize("launches", [1, 2])
+def test_gate_wait_give_up_then_recovery(launches):
+    """A gate wait that gives up, forced from the host (the row merges wait
+    for one gate arrival more than will come, for 64 sleeps, so every kernel
+    still exits), raises flag bit 2; the calls after it on the stream equal a
+    clean run bit for bit: once the flag is reported, the next call clears
+    the arrival counters a late gate slice can leave behind."""
+    say("select gate give-up and recovery, launches=%d" % launches)
+    x = inputs("t27b_b8")
+    t = to_device(x)
+    args = (t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], 16)
+    with df2.plan(launches=launches):
+        ref = [a.clone() for a in df2.select(*args)]
+        assert flags_clear()
+        with df2.plan(gate_giveup=1):
+            df2.select(*args)
+            torch.cuda.synchronize()
+        assert df2.device_error() == 4
+        for _ in range(3):
+            p, s = df2.select(*args)
+            assert torch.equal(p, ref[0]) and torch.equal(s, ref[1])
+        assert flags_clear()
+
+
 def test_stages_compose_to_select():
     """topk -> project -> pair_scores -> viterbi gives the fused result."""
     x = inputs("qwen3_4b_b1")
