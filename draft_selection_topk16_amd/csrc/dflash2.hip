@@ -1361,7 +1361,7 @@ df2_status dflash2_release(void) {
 // ----------------------------------------------------------------------------
 namespace {
 
-constexpr int kLmTiles[] = {1, 2, 4, 8, 12, 14, 16};   // m-blocks per tile with a kernel
+constexpr int kLmTiles[] = {1, 2, 4, 8, 12, 14};   // m-blocks per tile with a kernel
 
 struct LmPlan {
     int mb = 1, kmax = 16;
@@ -1376,7 +1376,7 @@ struct LmPlan {
 LmPlan plan_lmhead(int64_t M, int V, int K, int cus, const Overrides& ov) {
     LmPlan pl;
     pl.kmax = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
-    const int maxmb = pl.kmax == 16 ? 16 : (pl.kmax == 32 ? 14 : 8);
+    const int maxmb = pl.kmax == 64 ? 8 : 14;
     const int64_t nbm = (M + 15) / 16;
     const int64_t nmt = (nbm + maxmb - 1) / maxmb;
     const int64_t want = (nbm + nmt - 1) / nmt;
@@ -1406,7 +1406,6 @@ df2_status launch_lmhead(const LmPlan& pl, const LmArgs& a, hipStream_t stream) 
     }
     bool launched = false;
     DF2_LM(1, 16) DF2_LM(2, 16) DF2_LM(4, 16) DF2_LM(8, 16) DF2_LM(12, 16) DF2_LM(14, 16)
-    DF2_LM(16, 16)
     DF2_LM(1, 32) DF2_LM(2, 32) DF2_LM(4, 32) DF2_LM(8, 32) DF2_LM(12, 32) DF2_LM(14, 32)
     DF2_LM(1, 64) DF2_LM(2, 64) DF2_LM(4, 64) DF2_LM(8, 64)
 #undef DF2_LM

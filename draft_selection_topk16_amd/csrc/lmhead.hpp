@@ -6,28 +6,27 @@
 // Computing them here, beside the top-K, keeps the [M, V] logits out of HBM:
 // the one large read is W_lm itself (V x d bf16), streamed exactly once.
 //
-// k_lmhead: workgroup (mt, vr) multiplies M tile mt (up to 16 MB rows of X)
-// by the W_lm rows of vocabulary range vr on the matrix cores (bf16 operands,
-// fp32 sums).  The range's 16-column blocks are cut into chunks of 16 blocks
-// (the last one shorter), split evenly over the four waves, so every wave
-// owns at most four blocks (64 columns) of W_lm and streams them from
-// HBM straight into registers, three to seven 64-deep k slices ahead (more
-// for smaller tiles).  X reaches the waves through LDS, one 64-deep k slice
-// at a time, staged through registers two slices ahead (two buffers).
-// Within a slice, lane group g takes the 16 consecutive k of its 32-byte
-// piece, eight per matrix instruction, so that one wave's two loads cover
-// whole 128-byte lines of W_lm.
+// k_lmhead: workgroup (mt, vr) multiplies M tile mt (up to 14 m-blocks of 16
+// rows of X) by the W_lm rows of vocabulary range vr on the matrix cores
+// (bf16 operands, fp32 sums).  The range's 16-column blocks are cut into
+// chunks of 16 blocks (the last one shorter), split evenly over the four
+// waves, so every wave owns at most four blocks (64 columns) of W_lm and
+// streams them from HBM straight into registers, a ring of three to six
+// 64-deep k slices.  X reaches the waves through LDS, one 64-deep k slice at
+// a time, staged through registers two to four slices ahead; every X load is
+// issued before the W loads of its step, so that waiting for an X slice never
+// waits for a W slice needed later.
 // After the last slice of a chunk the waves spill their fp32 tiles to LDS
-// and one thread per row folds them, in column order, into that row's
-// running list of its best KMAX candidates, which stays in LDS until the
-// workgroup ends.  Tiles of up to 64 rows: every wave folds its own 64
-// columns into its own lists (one lane per row, no workgroup barrier), and
-// the four lists of a row are merged at the end; larger tiles: the waves
-// spill 32 columns at a time where the X slices were, and one thread per row
-// folds them all.  An empty list is filled by sorting 32 columns at once;
-// after that a value enters only if it beats the list's last entry, and an
-// insertion is two min/max operations per entry on an exact double that
-// holds value key and column.
+// and the columns are folded, in column order, into running per-row lists of
+// the best KMAX candidates, which stay in LDS until the workgroup ends.
+// Tiles of up to 64 rows: every wave folds its own 64 columns into its own
+// lists, with one to four lanes per row (each lane its own list over its
+// share of the columns), and the lists of a row are merged at the end;
+// larger tiles: the waves spill 32 columns at a time where the X slices
+// were, and one thread per row folds them all.  An empty list is filled by
+// sorting 16 or 32 columns at once; after that a column enters only if it
+// beats the list's last entry, four such columns per sorted merge.  An entry
+// is one exact double that holds value key and column.
 //
 // k_lmhead_merge: one workgroup per row merges the row's n_vr sorted lists:
 // a bound that K words are known to reach (the best K-th word of any list,
@@ -47,10 +46,22 @@ constexpr int kLmChunkBlocks = kWaves * kLmWaveBlocks;    // 256 columns per chu
 constexpr int kLmSliceK = 64;                             // k per X slice
 // W slices held in registers per wave (also the unroll of the slice loop,
 // whose body is branch-free so that the compiler's memory-counter waits stay
-// exact and the loads of later slices stay in flight): eight for tiles of up
-// to four m-blocks, six up to eight, four for the largest tiles, whose
-// accumulators leave less room
-__host__ __device__ constexpr int lm_ring(int mb) { return mb <= 4 ? 8 : (mb <= 8 ? 6 : 4); }
+// exact and the loads of later slices stay in flight).  Four slices keep
+// 128 KB per CU in flight; a plain stream of W in this pattern reads HBM no
+// faster with more, and slower with eight.  Six for eight m-blocks.
+__host__ __device__ constexpr int lm_ring(int mb) { return mb <= 4 ? 4 : (mb <= 8 ? 6 : 4); }
+// X slices held in registers ahead of their store to LDS.  Memory-counter
+// waits complete in order, so waiting for X slice s + 1 also waits for every
+// W load issued before it: a W slice gets as many steps in flight as X is
+// staged ahead, whatever the depth of the W ring.  Small tiles stage X a
+// whole ring ahead (one or two 16-byte pieces per thread per slice); large
+// tiles have registers for two slices only.
+__host__ __device__ constexpr int lm_xahead(int mb) { return mb <= 4 ? 4 : (mb <= 8 ? 3 : 2); }
+// the slice loop's unroll: W slots, X slots and the two LDS buffers all
+// cycle inside it
+__host__ __device__ constexpr int lm_gcd(int a, int b) { return b == 0 ? a : lm_gcd(b, a % b); }
+__host__ __device__ constexpr int lm_lcm(int a, int b) { return a / lm_gcd(a, b) * b; }
+__host__ __device__ constexpr int lm_unroll(int mb) { return lm_lcm(lm_lcm(lm_ring(mb), lm_xahead(mb)), 2); }
 constexpr int kLmXBufs = 2;                               // X slice buffers in LDS
 constexpr int kLmSlabCols = 32;                           // columns per fold
 // tiles of up to four m-blocks (64 rows; two for 64-entry lists, whose four
@@ -58,6 +69,12 @@ constexpr int kLmSlabCols = 32;                           // columns per fold
 // own lists, one lane per row; larger tiles: one thread per row folds the
 // whole chunk, 32 columns at a time
 __host__ __device__ constexpr bool lm_wide(int mb, int kmax) { return mb <= (kmax <= 32 ? 4 : 2); }
+// small tiles, lists of up to 32: the wave's 64 lanes cover its rows several
+// times over (four lanes per row for one m-block, two for two), each lane
+// keeping its own list of its share of the columns (16 or 32 per chunk)
+__host__ __device__ constexpr int lm_lpr(int mb, int kmax) {
+    return (lm_wide(mb, kmax) && kmax <= 32) ? 64 / (16 * mb) : 1;
+}
 constexpr int kLmMaxLists = 256;                          // vocabulary ranges per row
 
 struct LmArgs {
@@ -87,12 +104,13 @@ struct LmLds {
         float slab[lm_wide(MB, KMAX) ? 1 : 16 * MB][kLmSlabCols + 1];
     };
     // small tiles: each wave's own 64 columns of the chunk and its own
-    // candidate lists (folded without workgroup barriers)
+    // candidate lists, lm_lpr of them per row (folded without workgroup
+    // barriers)
     float wslab[lm_wide(MB, KMAX) ? kWaves : 1][lm_wide(MB, KMAX) ? 16 * MB : 1][16 * kLmWaveBlocks + 1];
     // each row's running list(s) of its best KMAX candidates, best first, as
     // lm_entry values (0 = empty); rows padded by 16 bytes so that 16-byte
     // reads of consecutive rows fall in distinct banks
-    double lst[lm_wide(MB, KMAX) ? kWaves : 1][16 * MB][KMAX + 2];
+    double lst[lm_wide(MB, KMAX) ? kWaves * lm_lpr(MB, KMAX) : 1][16 * MB][KMAX + 2];
 };
 
 // An even split of n items into parts: part k starts at k q + min(k, r) and
@@ -124,17 +142,19 @@ __device__ __forceinline__ uint32_t lm_entry_key(double e) {
     return (uint32_t)(e * (1.0 / kLmOffScale));      // exact: drops the offset part
 }
 
-// Insert entry x into a row's list (best first), dropping the last entry:
-// entry j becomes the larger of itself and the smaller of x and entry j - 1.
-// Every entry is two independent min/max operations.
-template <int KMAX>
-__device__ __forceinline__ void lm_insert(double (&lw)[KMAX], double x) {
-    double nw[KMAX];
-    nw[0] = fmax(lw[0], x);
-#pragma unroll
-    for (int j = 1; j < KMAX; ++j) nw[j] = fmax(lw[j], fmin(lw[j - 1], x));
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) lw[j] = nw[j];
+// Larger and smaller of two list entries.  Entries are never NaN (0 or a
+// finite positive key), so the plain instructions are exact; fmax/fmin would
+// first quiet both operands (one more double operation each) because the
+// compiler cannot see that.
+__device__ __forceinline__ double lm_max(double a, double b) {
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ double lm_min(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
 }
 
 // the value a candidate must beat to enter a list whose last entry is `last`
@@ -152,18 +172,19 @@ __device__ __forceinline__ u32x4_t lm_load(__amdgpu_buffer_rsrc_t r, uint32_t vo
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
-// Sort 32 entries, best first (bitonic network: every compare-exchange is
+// Sort N entries, best first (bitonic network: every compare-exchange is
 // one max and one min, the exchanges of a stage independent).
-__device__ __forceinline__ void lm_sort32(double (&e)[32]) {
+template <int N>
+__device__ __forceinline__ void lm_sort(double (&e)[N]) {
 #pragma unroll
-    for (int k = 2; k <= 32; k <<= 1)
+    for (int k = 2; k <= N; k <<= 1)
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1)
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < N; ++i) {
                 const int l = i ^ j;
                 if (l > i) {
-                    const double hi = fmax(e[i], e[l]), lo = fmin(e[i], e[l]);
+                    const double hi = lm_max(e[i], e[l]), lo = lm_min(e[i], e[l]);
                     const bool desc = (i & k) == 0;
                     e[i] = desc ? hi : lo;
                     e[l] = desc ? lo : hi;
@@ -177,51 +198,84 @@ __device__ __forceinline__ void lm_sort32(double (&e)[32]) {
 template <int KMAX, typename BK>
 __device__ __forceinline__ void lm_merge_top(double (&a)[KMAX], BK&& bk) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) a[j] = fmax(a[j], bk(KMAX - 1 - j));
+    for (int j = 0; j < KMAX; ++j) a[j] = lm_max(a[j], bk(KMAX - 1 - j));
 #pragma unroll
     for (int h = KMAX / 2; h > 0; h >>= 1)
 #pragma unroll
         for (int i = 0; i < KMAX; ++i)
             if ((i & h) == 0) {
-                const double hi = fmax(a[i], a[i + h]), lo = fmin(a[i], a[i + h]);
+                const double hi = lm_max(a[i], a[i + h]), lo = lm_min(a[i], a[i + h]);
                 a[i] = hi;
                 a[i + h] = lo;
             }
 }
 
-// Fold 32 consecutive columns of one row (ncols of them valid; column cc has
-// offset off0 + cc in the workgroup's range) into the row's list.  An empty
-// list is filled by sorting the 32 at once; otherwise each column that
-// beats the list's last entry is inserted, in column order.
+// Merge four entries e (best first; 0 = none) into a sorted list: the last
+// four entries of the list become the larger of themselves and e reversed,
+// which leaves a bitonic sequence holding the best KMAX, and the half-cleaner
+// network sorts it (as in lm_merge_top, without the entries that cannot
+// change).
 template <int KMAX>
-__device__ __forceinline__ void lm_fold32(double (&lw)[KMAX], float& floor_v,
-                                          const float* __restrict__ srow, int ncols, int off0) {
-    float xv[kLmSlabCols];
+__device__ __forceinline__ void lm_merge4(double (&a)[KMAX], const double (&e)[4]) {
 #pragma unroll
-    for (int cc = 0; cc < kLmSlabCols; ++cc) xv[cc] = srow[cc];
+    for (int k = 0; k < 4; ++k) a[KMAX - 4 + k] = lm_max(a[KMAX - 4 + k], e[3 - k]);
+#pragma unroll
+    for (int h = KMAX / 2; h > 0; h >>= 1)
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i)
+            if ((i & h) == 0) {
+                const double hi = lm_max(a[i], a[i + h]), lo = lm_min(a[i], a[i + h]);
+                a[i] = hi;
+                a[i + h] = lo;
+            }
+}
+
+// Fold NC consecutive columns of one row (ncols of them valid; column cc has
+// offset off0 + cc in the workgroup's range) into the row's list.  An empty
+// list is filled by sorting the NC at once; otherwise the columns that beat
+// the list's last entry are merged in four at a time (one LDS round trip,
+// one merge and one new floor per four: each step is a chain of dependent
+// operations at one wave per SIMD).  Entries carry their column, so the list
+// does not depend on the order of insertion.
+template <int KMAX, int NC>
+__device__ __forceinline__ void lm_fold(double (&lw)[KMAX], float& floor_v,
+                                        const float* __restrict__ srow, int ncols, int off0) {
+    float xv[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) xv[cc] = srow[cc];
     if (lw[0] == 0.0) {
-        double e[kLmSlabCols];
+        double e[NC];
 #pragma unroll
-        for (int cc = 0; cc < kLmSlabCols; ++cc)
+        for (int cc = 0; cc < NC; ++cc)
             e[cc] = cc < ncols ? lm_entry(key_f32(__float_as_uint(xv[cc])), off0 + cc) : 0.0;
-        lm_sort32(e);
+        lm_sort<NC>(e);
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) lw[j] = j < kLmSlabCols ? e[j] : 0.0;
+        for (int j = 0; j < KMAX; ++j) lw[j] = j < NC ? e[j] : 0.0;
         floor_v = lm_floor(lw[KMAX - 1]);
         return;
     }
     uint32_t flagged = 0;
 #pragma unroll
-    for (int cc = 0; cc < kLmSlabCols; ++cc)
+    for (int cc = 0; cc < NC; ++cc)
         flagged |= (cc < ncols && xv[cc] > floor_v) ? (1u << cc) : 0u;
     while (flagged) {
-        const int cc = __builtin_ctz(flagged);
-        flagged &= flagged - 1u;
-        const float x = srow[cc];
-        if (x > floor_v) {
-            lm_insert<KMAX>(lw, lm_entry(key_f32(__float_as_uint(x)), off0 + cc));
-            floor_v = lm_floor(lw[KMAX - 1]);
+        int c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c[k] = flagged ? __builtin_ctz(flagged) : -1;
+            flagged &= flagged - 1u;
         }
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = srow[c[k] < 0 ? 0 : c[k]];
+        double e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            e[k] = (c[k] >= 0 && x[k] > floor_v) ? lm_entry(key_f32(__float_as_uint(x[k])), off0 + c[k])
+                                                 : 0.0;
+        lm_sort<4>(e);
+        lm_merge4<KMAX>(lw, e);
+        floor_v = lm_floor(lw[KMAX - 1]);
     }
 }
 
@@ -271,7 +325,6 @@ __device__ __forceinline__ void lm_chunk(__amdgpu_buffer_rsrc_t rx,
     using XL = LmX<MB, KMAX>;
     constexpr int NB = NBW > 0 ? NBW : 1;
     constexpr int RING = lm_ring(MB);
-    static_assert(RING % kLmXBufs == 0, "the X buffers alternate inside the unroll");
     const int lane = threadIdx.x & 63;
     const int row = lane & 15, g = lane >> 4;
     const int ns = d / kLmSliceK;
@@ -288,16 +341,21 @@ __device__ __forceinline__ void lm_chunk(__amdgpu_buffer_rsrc_t rx,
         }
     };
     // Step of slice s (ring slot u == s % RING, X buffer s % 2): load X slice
-    // s + 2 into registers, multiply (only for s < ns: past the end the loads
-    // repeat the last slice and nothing is added), load W slice s + RING into
-    // the slot just used, write X slice s + 1 (loaded a step earlier) to the
-    // other buffer and meet the other waves.  X slice s + 1 was loaded before
-    // W slice s - 1 + RING, so waiting for it never waits for the W loads of
-    // the last two steps.
-    u32x4_t xr[2][XL::XP];
+    // s + XA into the registers X slice s left (it reached LDS a step ago),
+    // multiply (only for s < ns: past the end the loads repeat the last slice
+    // and nothing is added), load W slice s + RING into the slot just used,
+    // write X slice s + 1 to the other buffer and meet the other waves.
+    // Every X load is issued before the W loads of the same step, so waiting
+    // for X slice s + 1 at the end of step s waits for no W slice that is
+    // needed later than XA steps after its load.
+    constexpr int XA = lm_xahead(MB);
+    constexpr int U = lm_unroll(MB);
+    static_assert(XA >= 2, "X slice s + 1 is in registers while slice s is read from LDS");
+    u32x4_t xr[XA][XL::XP];
     auto step = [&](int s, int u) {
         const int xb = u & 1;
-        XL::load(rx, xoff, min(s + 2, ns - 1), xr[xb]);
+        const int wu = u % RING;
+        XL::load(rx, xoff, min(s + XA, ns - 1), xr[u % XA]);
         if constexpr (NBW > 0) {
             if (s < ns) {
                 u32x4_t a0 = sm.xs[xb][row][(2 * g) ^ ((row >> 1) & 7)];
@@ -316,32 +374,35 @@ __device__ __forceinline__ void lm_chunk(__amdgpu_buffer_rsrc_t rx,
                     // accumulators first, so no product waits for the last
 #pragma unroll
                     for (int j = 0; j < NBW; ++j)
-                        acc[i][j] = mfma_bf16(as_bf16x8(a0), as_bf16x8(wr[u][j][0]), acc[i][j]);
+                        acc[i][j] = mfma_bf16(as_bf16x8(a0), as_bf16x8(wr[wu][j][0]), acc[i][j]);
 #pragma unroll
                     for (int j = 0; j < NBW; ++j)
-                        acc[i][j] = mfma_bf16(as_bf16x8(a1), as_bf16x8(wr[u][j][1]), acc[i][j]);
+                        acc[i][j] = mfma_bf16(as_bf16x8(a1), as_bf16x8(wr[wu][j][1]), acc[i][j]);
                     __builtin_amdgcn_sched_barrier(0);
                     a0 = n0;
                     a1 = n1;
                 }
             }
-            load_w(s + RING, wr[u]);
+            load_w(s + RING, wr[wu]);
         }
-        XL::store(sm, xb ^ 1, xr[xb ^ 1]);
+        XL::store(sm, xb ^ 1, xr[(u + 1) % XA]);
         __syncthreads();
     };
 
-    // prologue: W slices 0 .. RING-1; X slice 0 to LDS, slice 1 in registers
+    // prologue: X slices 0 .. XA-1 and W slices 0 .. RING-1, interleaved so
+    // that waiting for X slice k waits only for the W slices before it; X
+    // slice 0 to LDS
 #pragma unroll
-    for (int u = 0; u < RING; ++u) load_w(u, wr[u]);
-    XL::load(rx, xoff, 0, xr[0]);
-    XL::load(rx, xoff, min(1, ns - 1), xr[1]);
+    for (int u = 0; u < (RING > XA ? RING : XA); ++u) {
+        if (u < XA) XL::load(rx, xoff, min(u, ns - 1), xr[u]);
+        if (u < RING) load_w(u, wr[u]);
+    }
     XL::store(sm, 0, xr[0]);
     __syncthreads();
 
-    for (int s0 = 0; s0 < ns; s0 += RING) {
+    for (int s0 = 0; s0 < ns; s0 += U) {
 #pragma unroll
-        for (int u = 0; u < RING; ++u) step(s0 + u, u);
+        for (int u = 0; u < U; ++u) step(s0 + u, u);
     }
 }
 
@@ -403,8 +464,12 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
         // column order (so a value equal to a kept one never displaces it) ----
         if constexpr (lm_wide(MB, KMAX)) {
             // the wave spills its blocks to its own slab; value v of block
-            // (i, j): row 16 i + 4 g + v, column 16 j + row.  Lane l then folds
-            // row l of it into its list of that row.
+            // (i, j): row 16 i + 4 g + v, column 16 j + row.  Lane (sub, r)
+            // then folds its share of row r (columns SUBC sub .. SUBC (sub +
+            // 1)) into its own list of that row.
+            constexpr int LPR = lm_lpr(MB, KMAX);
+            constexpr int SUBC = 16 * kLmWaveBlocks / LPR;
+            constexpr int NC = SUBC < kLmSlabCols ? SUBC : kLmSlabCols;
 #pragma unroll
             for (int j = 0; j < kLmWaveBlocks; ++j) {
                 if (j < nbw) {
@@ -416,18 +481,22 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
                 }
             }
             wave_sync();
-            if (lane < mrows) {
+            const int r = lane % ROWS, sub = lane / ROWS;
+            if (r < mrows) {
                 double lw[KMAX];
 #pragma unroll
-                for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[w][lane][j];
+                for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[w * LPR + sub][r][j];
                 float floor_v = lm_floor(lw[KMAX - 1]);
                 const int wcols = min(16 * nbw, col_end - 16 * cb);   // the wave's valid columns
-                for (int q = 0; q * kLmSlabCols < wcols; ++q)
-                    lm_fold32<KMAX>(lw, floor_v, &sm.wslab[w][lane][q * kLmSlabCols],
-                                    min(kLmSlabCols, wcols - q * kLmSlabCols),
-                                    16 * cb - col0 + q * kLmSlabCols);
 #pragma unroll
-                for (int j = 0; j < KMAX; ++j) sm.lst[w][lane][j] = lw[j];
+                for (int q = 0; q < SUBC / NC; ++q) {
+                    const int cq = SUBC * sub + NC * q;
+                    const int nc = min(NC, wcols - cq);
+                    if (nc > 0)
+                        lm_fold<KMAX, NC>(lw, floor_v, &sm.wslab[w][r][cq], nc, 16 * cb - col0 + cq);
+                }
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) sm.lst[w * LPR + sub][r][j] = lw[j];
             }
         } else {
             const int trow = min(tid, ROWS - 1);
@@ -453,7 +522,7 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
                 const int v0 = 16 * (pcb + 2 * h);
                 const int ncols = max(0, min(min(pnb - 2 * h, 2) * 16, col_end - v0));
                 __syncthreads();
-                if (tid < mrows && ncols > 0) lm_fold32<KMAX>(lw, floor_v, sm.slab[tid], ncols, v0 - col0);
+                if (tid < mrows && ncols > 0) lm_fold<KMAX, kLmSlabCols>(lw, floor_v, sm.slab[tid], ncols, v0 - col0);
                 __syncthreads();
             }
             if (tid < mrows) {
@@ -465,16 +534,31 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
         __syncthreads();
     }
 
-    // small tiles: merge each row's four wave lists into the first
+    // small tiles: merge each row's lists into the first, those of one wave
+    // first (in parallel over the waves), then the four waves' results
     if constexpr (lm_wide(MB, KMAX)) {
+        constexpr int LPR = lm_lpr(MB, KMAX);
         __syncthreads();
+        if constexpr (LPR > 1) {
+            if (lane < mrows) {
+                double lw[KMAX];
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[w * LPR][lane][j];
+#pragma unroll
+                for (int u = 1; u < LPR; ++u)
+                    lm_merge_top<KMAX>(lw, [&](int j) { return sm.lst[w * LPR + u][lane][j]; });
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) sm.lst[w * LPR][lane][j] = lw[j];
+            }
+            __syncthreads();
+        }
         if (tid < mrows) {
             double lw[KMAX];
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) lw[j] = sm.lst[0][tid][j];
 #pragma unroll
             for (int u = 1; u < kWaves; ++u)
-                lm_merge_top<KMAX>(lw, [&](int j) { return sm.lst[u][tid][j]; });
+                lm_merge_top<KMAX>(lw, [&](int j) { return sm.lst[u * LPR][tid][j]; });
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) sm.lst[0][tid][j] = lw[j];
         }
