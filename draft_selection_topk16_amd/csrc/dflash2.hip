@@ -1369,10 +1369,10 @@ struct LmPlan {
     size_t part_bytes = 0, merge_lds = 0;
 };
 
-// Tiles of up to 16 m-blocks (14 for K > 16 and 8 for K > 32, whose lists
-// take more LDS and registers), the smallest tile kernel that covers an even
-// split of the rows; then enough vocabulary ranges to give every CU one
-// workgroup.
+// Tiles of up to 14 m-blocks (16 would spill registers; 8 for K > 32,
+// whose lists take more LDS and registers), the smallest tile kernel that
+// covers an even split of the rows; then enough vocabulary ranges to give
+// every CU one workgroup.
 LmPlan plan_lmhead(int64_t M, int V, int K, int cus, const Overrides& ov) {
     LmPlan pl;
     pl.kmax = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
