@@ -74,12 +74,13 @@ struct Params {
     float* cval;          // [rows, K]
     float* ppart;         // [S, M, r] gate partials
     float* Sb;            // [rows, K, K] pair scores
-    float* Hb;            // [rows, r] gate rows, summed by the row merges
+    float* Hb;            // [rows, r] gate rows (summed by the row merges, or by each
+                          // gate tile's last slice in two launches with M <= 16)
     uint32_t* err;        // device input-error flags
     uint32_t* row_cnt;    // [rows] segments done
     uint32_t* edge_cnt;   // [rows] rows ready of transition t - 1 -> t
     uint32_t* seq_cnt;    // [B] transitions scored
-    uint32_t* gate_cnt;   // [mtiles] gate slices done
+    uint32_t* gate_cnt;   // [mtiles] gate slices done (M <= 16 in two launches: tiles summed)
     uint32_t* rd_cnt;     // [mtiles] pair jobs past the gate wait
     // sizes
     int B, P, V, d, r, K;
@@ -100,6 +101,7 @@ struct Params {
     // bound in sleeps.
     uint32_t gate_extra = 0;
     uint32_t gate_spins = 1u << 20;
+    uint32_t* tile_cnt;   // [mtiles * ntiles] slices of a gate tile done (tile sums)
 };
 
 // Walk modes inside the launch: the two of df2_walk, and the sampling walk.
@@ -123,17 +125,69 @@ struct GateShape {
     static constexpr int NB = MB == 1 ? 4 : 2;
 };
 
-// One slice of one gate tile, counted on the tile row's counter once its
-// partial is stored.
-template <bool BF16, int MB>
+// One slice of one gate tile.  HSUM (the two-launch kernels with a gate of
+// one m-block, M <= 16 rows): the tile's last slice to finish sums the S
+// partials in slice order into the gate rows Hb, so that a row merge loads
+// one row of H instead of S partial rows, and counts the tile on its tile
+// row.  Otherwise each slice counts itself on the tile row and every row
+// merge sums its own row's partials (at M = 56 and 224 the tile sums
+// lengthened the scan launch by 5-6 us).  Either way the sum runs in slice
+// order, so the result never depends on timing.
+template <bool BF16, int MB, bool HSUM>
 __device__ void gate_role(const Params& p, int gb, GateLds& sm) {
     const int s = gb % p.S, tile = gb / p.S;
     const int mt = tile / p.ntiles, nt = tile % p.ntiles;
     gate_slice<BF16, MB, GateShape<MB>::NB>(p.hidden, p.W, (int)p.rows, p.d, p.r, mt, nt, s, p.S,
                                             p.ppart, sm);
-    drain_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) arrive(&p.gate_cnt[mt]);
+    if constexpr (!HSUM) {
+        drain_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) arrive(&p.gate_cnt[mt]);
+    } else {
+        __shared__ uint32_t last;
+        if (!block_arrive_last(&p.tile_cnt[tile], (uint32_t)p.S, &last)) return;
+        const int tid = threadIdx.x;
+        if (tid == 0) reset_counter(&p.tile_cnt[tile]);
+        // thread: CG consecutive columns of one tile row (8, or 4 for the
+        // 1024-value tiles of one m-block); the partials come in rounds of four
+        // slices, all loads of a round in flight at once
+        constexpr int TR = 16 * MB, TC = 16 * GateShape<MB>::NB;
+        constexpr int CG = TR * TC > 1024 ? 8 : 4;
+        static_assert(TR * TC / CG <= kWG, "one group of columns per thread");
+        if (tid < TR * TC / CG) {
+            const int64_t m = (int64_t)mt * TR + tid / (TC / CG);
+            const int c = nt * TC + (tid % (TC / CG)) * CG;
+            if (m < p.rows) {
+                float h[CG];
+    #pragma unroll
+                for (int e = 0; e < CG; ++e) h[e] = 0.f;
+                for (int s0 = 0; s0 < p.S; s0 += 4) {
+                    uint64_t v[4][CG / 2];
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint64_t* q = reinterpret_cast<const uint64_t*>(
+                            p.ppart + ((int64_t)min(s0 + u, p.S - 1) * p.rows + m) * p.r + c);
+    #pragma unroll
+                        for (int i = 0; i < CG / 2; ++i) v[u][i] = xload(q + i);
+                    }
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (s0 + u < p.S) {
+    #pragma unroll
+                            for (int i = 0; i < CG / 2; ++i) {
+                                h[2 * i] += __uint_as_float((uint32_t)v[u][i]);
+                                h[2 * i + 1] += __uint_as_float((uint32_t)(v[u][i] >> 32));
+                            }
+                        }
+                }
+    #pragma unroll
+                for (int e = 0; e < CG; ++e) xstore(p.Hb + m * p.r + c + e, h[e]);
+            }
+        }
+        drain_stores();
+        __syncthreads();
+        if (tid == 0) arrive(&p.gate_cnt[mt]);
+    }
 }
 
 template <bool BF16, int NV, bool LDSR = false>
@@ -210,7 +264,7 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
 // the pair scores of the transitions the row completes, and the walk of the
 // sequence whose last transition it scores.  Every thread of the workgroup
 // calls.
-template <bool BF16, int MB, bool SAMPLE>
+template <bool BF16, int MB, bool SAMPLE, bool HSUM>
 __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll& sm,
                                          uint32_t& flag) {
     const int tid = threadIdx.x;
@@ -218,21 +272,27 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
     // The row's gate H_t: once the gate tile row is complete (its workgroups
     // were dispatched first and never wait; this is almost always so by
     // now), its S partials are loaded while the merge runs and summed in
-    // slice order.
+    // slice order, or (HSUM) its row of Hb, which the gate's tile sums wrote.
     const int mt = (int)(row / p.gm_rows);
-    const uint32_t need = (uint32_t)(p.ntiles * p.S) + p.gate_extra;
+    const uint32_t need = (HSUM ? (uint32_t)p.ntiles : (uint32_t)(p.ntiles * p.S)) + p.gate_extra;
     const int S = p.S;
-    uint32_t hp[kMaxFusedSlices];
+    constexpr int NH = HSUM ? 1 : kMaxFusedSlices;
+    uint32_t hp[NH];
     auto issue_h = [&](int k) {
+        if constexpr (HSUM) {
+            hp[0] = xload(reinterpret_cast<const uint32_t*>(p.Hb) + row * r + min(k, r - 1));
+        } else {
 #pragma unroll
-        for (int s = 0; s < kMaxFusedSlices; ++s)
-            hp[s] = xload(reinterpret_cast<const uint32_t*>(p.ppart) +
-                          ((int64_t)min(s, S - 1) * p.rows + row) * r + min(k, r - 1));
+            for (int s = 0; s < NH; ++s)
+                hp[s] = xload(reinterpret_cast<const uint32_t*>(p.ppart) +
+                              ((int64_t)min(s, S - 1) * p.rows + row) * r + min(k, r - 1));
+        }
     };
     auto sum_h = [&]() {
+        if constexpr (HSUM) return __uint_as_float(hp[0]);
         float h = 0.f;
 #pragma unroll
-        for (int s = 0; s < kMaxFusedSlices; ++s)
+        for (int s = 0; s < NH; ++s)
             if (s < S) h += __uint_as_float(hp[s]);
         return h;
     };
@@ -265,10 +325,12 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
         issue_h(tid + kWG);
         hown[1] = sum_h();
     }
-    // publish H_t for the pair job of the next position
+    // publish H_t for the pair job of the next position (HSUM: already there)
+    if constexpr (!HSUM) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-        if (tid + u * kWG < r) xstore(p.Hb + row * r + tid + u * kWG, hown[u]);
+        for (int u = 0; u < 2; ++u)
+            if (tid + u * kWG < r) xstore(p.Hb + row * r + tid + u * kWG, hown[u]);
+    }
     // arrive on the transitions into and out of this row
     const int b = (int)(row / P), t = (int)(row % P);
     drain_stores();
@@ -330,7 +392,7 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
         // the gate and everything after a segment are on the critical path;
         // the streaming waves that share the SIMDs mostly wait on memory
         __builtin_amdgcn_s_setprio(3);
-        gate_role<BF16, MB>(p, (int)g, sm.g);
+        gate_role<BF16, MB, false>(p, (int)g, sm.g);
         return;
     }
     const int64_t sb = g - p.n_gate;
@@ -339,7 +401,7 @@ __global__ __launch_bounds__(kWG, 5) void k_select(Params p) {
     if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
     __builtin_amdgcn_s_setprio(3);
     if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
-    row_tail<BF16, MB, SAMPLE>(p, row, sm, flag);
+    row_tail<BF16, MB, SAMPLE, false>(p, row, sm, flag);
 }
 
 // The selector in two launches: k_scan runs the gate slices and the segments
@@ -351,7 +413,7 @@ __global__ __launch_bounds__(kWG, 5) void k_scan(Params p) {
     __shared__ SharedAll sm;
     const int64_t g = blockIdx.x;
     if (g < p.n_gate) {
-        gate_role<BF16, MB>(p, (int)g, sm.g);
+        gate_role<BF16, MB, MB == 1>(p, (int)g, sm.g);
         return;
     }
     const int64_t sb = g - p.n_gate;
@@ -362,7 +424,7 @@ template <bool BF16, int MB, bool SAMPLE>
 __global__ __launch_bounds__(kWG, 5) void k_tail(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
-    row_tail<BF16, MB, SAMPLE>(p, (int64_t)blockIdx.x, sm, flag);
+    row_tail<BF16, MB, SAMPLE, MB == 1>(p, (int64_t)blockIdx.x, sm, flag);
 }
 
 // Top-K alone: segments, then the row merge on last arrival.
@@ -715,10 +777,11 @@ void plan_gate(Plan& pl, int64_t M, int d, int r, const Overrides& ov) {
 }
 
 // Scratch layout: counters first (err, rows, transitions, sequences, gate
-// tile rows, gate readers), then data.
+// tile rows, gate readers, gate tiles), then data.
 void plan_layout(Plan& pl, int64_t rows, int64_t M, int B, bool pairs) {
     Params& p = pl.p;
-    const size_t ncnt = 1 + 2 * (size_t)rows + (size_t)B + 2 * (size_t)p.mtiles;
+    const size_t ncnt = 1 + 2 * (size_t)rows + (size_t)B + 2 * (size_t)p.mtiles +
+                        (size_t)p.mtiles * p.ntiles;
     pl.counter_bytes = align_up(ncnt * 4, 256);
     size_t off = pl.counter_bytes;
     pl.off_part = off;
@@ -746,6 +809,7 @@ void bind_scratch(Plan& pl, void* base, int64_t rows, int B) {
     p.seq_cnt = p.edge_cnt + rows;
     p.gate_cnt = p.seq_cnt + B;
     p.rd_cnt = p.gate_cnt + p.mtiles;
+    p.tile_cnt = p.rd_cnt + p.mtiles;
     p.part = reinterpret_cast<uint64_t*>(c + pl.off_part);
     p.cand = reinterpret_cast<int32_t*>(c + pl.off_cand);
     p.cval = reinterpret_cast<float*>(c + pl.off_cval);
