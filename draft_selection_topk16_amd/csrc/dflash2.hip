@@ -10,12 +10,14 @@
 // in one (k_select), as the plan decides.  Workgroups are dealt out in index
 // order, and each one's job follows from its index:
 //   * the first n_gate compute one slice of one gate tile (a partial of H)
-//     and count it on the tile row's counter;
-//   * every other one streams one contiguous vocabulary segment of one
-//     logits row, leaving a sorted list of K candidates; in the single
-//     launch it then arrives on the row's counter, and the last to arrive
-//     goes on with the row (row_tail); in two launches k_scan ends here and
-//     k_tail runs row_tail for every row, one workgroup per row.
+//     and count it on the tile row's counter (in two launches with M <= 16
+//     rows, the tile's last slice sums the partials into H and counts the
+//     tile instead);
+//   * every other one streams one segment of one logits row (every nseg-th
+//     chunk of it), leaving a sorted list of K candidates per wave; in the
+//     single launch it then arrives on the row's counter, and the last to
+//     arrive goes on with the row (row_tail); in two launches k_scan ends
+//     here and k_tail runs row_tail for every row, one workgroup per row.
 // The work after the segments is handed on by "last arrival": nobody waits
 // for a producer except for the gate, below.
 //   row:      the last segment of a row merges the row's lists into its
@@ -24,10 +26,11 @@
 //   pairs:    the second row of a transition to arrive scores it (the first
 //             transition of a sequence needs only its own row);
 //   walk:     the last transition of a sequence to be scored walks it.
-// The pair scores sum H_t from the gate partials; they wait (bounded spin)
-// for the gate tile row to be complete.  Gate workgroups have the lowest
-// indexes and never wait, so they have all been dispatched by the time any
-// pair job runs, and every wait ends.
+// The row merge sums H_t from the gate partials in slice order (or loads
+// the tile sums' row of H); it waits (bounded spin) for the gate tile row to
+// be complete.  Gate workgroups have the lowest indexes and never wait, so
+// they have all been dispatched by the time any row merge runs, and every
+// wait ends.
 // Counters live in the scratch buffer and are reset by the workgroup that
 // consumes them, so every launch starts from zero without a memset.
 #include <hip/hip_runtime.h>

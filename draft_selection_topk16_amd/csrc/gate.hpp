@@ -15,8 +15,10 @@
 // loads of a group before its first product, so a slice of 4 * KB steps
 // costs one memory round trip.  The four waves' tiles are summed
 // in LDS in wave order and the slice is written as a partial [S, M, r]
-// (or straight into H when S == 1).  Whoever needs H_t sums the S partials of
-// its row in slice order, so results never depend on timing.
+// (or straight into H when S == 1).  The S partials are summed in slice order
+// by whoever needs H_t (a row merge, or in the selector's two launches with a
+// one-m-block gate the tile's last slice to finish), so results never depend
+// on timing.
 #pragma once
 
 #include "common.hpp"

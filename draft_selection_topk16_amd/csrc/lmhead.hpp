@@ -11,13 +11,13 @@
 // (bf16 operands, fp32 sums).  The range's 16-column blocks are cut into
 // chunks of 16 blocks (the last one shorter), split evenly over the four
 // waves, so every wave owns at most four blocks (64 columns) of W_lm and
-// streams them from HBM straight into registers, a ring of three to six
+// streams them from HBM straight into registers, a ring of four or six
 // 64-deep k slices.  X reaches the waves through LDS, one 64-deep k slice at
 // a time, staged through registers two to four slices ahead; every X load is
 // issued before the W loads of its step, so that waiting for an X slice never
 // waits for a W slice needed later.
 // After the last slice of a chunk the waves spill their fp32 tiles to LDS
-// and the columns are folded, in column order, into running per-row lists of
+// and the columns are folded into running per-row lists of
 // the best KMAX candidates, which stay in LDS until the workgroup ends.
 // Tiles of up to 64 rows: every wave folds its own 64 columns into its own
 // lists, with one to four lanes per row (each lane its own list over its
@@ -28,11 +28,12 @@
 // beats the list's last entry, four such columns per sorted merge.  An entry
 // is one exact double that holds value key and column.
 //
-// k_lmhead_merge: one workgroup per row merges the row's n_vr sorted lists:
-// a bound that K words are known to reach (the best K-th word of any list,
-// and the K-th best head), compaction of the words that reach it (read only
-// from the lists whose head reaches it), and ranks by counting.  Candidate words (key << 32 | ~index) are distinct within a
-// row, so results do not depend on timing or on the launch plan.
+// k_lmhead_merge: one workgroup per row merges the row's n_vr sorted lists
+// (one list per thread, loaded whole): a bound that K words are known to
+// reach (the best K-th word of any list, and the K-th best head), compaction
+// of the words that reach it (a prefix of each list), and ranks by counting.
+// Candidate words (key << 32 | ~index) are distinct within a row, so results
+// do not depend on timing or on the launch plan.
 #pragma once
 
 #include <math.h>
@@ -460,8 +461,9 @@ __global__ __launch_bounds__(kWG, 1) void k_lmhead(LmArgs a) {
             default: lm_chunk<MB, KMAX, 4>(rx, xoff, rw, d, sm, acc); break;
         }
 
-        // ---- epilogue: fold this chunk's columns into the row lists, in
-        // column order (so a value equal to a kept one never displaces it) ----
+        // ---- epilogue: fold this chunk's columns into the row lists (an
+        // entry carries its column, so equal values keep the lower column
+        // first whatever the order of folding) ----
         if constexpr (lm_wide(MB, KMAX)) {
             // the wave spills its blocks to its own slab; value v of block
             // (i, j): row 16 i + 4 g + v, column 16 j + row.  Lane (sub, r)
