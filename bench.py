@@ -82,18 +82,44 @@ def algorithmic_bytes(wl) -> int:
     return logits + hidden + w + rows + out
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed
+    (string literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(family: str = "select") -> str:
     """Hash of the device code a family of kernels is built from (for the
-    selector, dflash2.hip up to its host-side part), so that counter runs are
-    only reused while that code is unchanged."""
+    selector, dflash2.hip up to its host-side part; comments and layout
+    ignored), so that counter runs are only reused while that code is
+    unchanged."""
     files = {"select": KERNEL_SOURCES, "lmhead": LMHEAD_SOURCES}[family]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "draft_selection_topk16_amd", "csrc", f), "rb") as fh:
+        with open(os.path.join(ROOT, "draft_selection_topk16_amd", "csrc", f), encoding="utf-8") as fh:
             data = fh.read()
         if f == "dflash2.hip":
-            data = data.split(b"// Host side.")[0]
-        h.update(data)
+            data = data.split("// Host side.")[0]
+        h.update(_code_only(data).encode())
     return h.hexdigest()[:16]
 
 

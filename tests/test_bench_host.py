@@ -74,3 +74,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_kernel_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
+    src = tmp_path / "draft_selection_topk16_amd" / "csrc"
+    src.mkdir(parents=True)
+    (src / "common.hpp").write_text("int f(int x) { return x + 1; }\n")
+    (src / "lmhead.hpp").write_text('const char* s = "a // b";\n')
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash("lmhead")
+    (src / "common.hpp").write_text("// the successor\nint f(int x)  {\n  return x + 1;  /* one more */ }\n")
+    assert bench.kernel_source_hash("lmhead") == h0
+    (src / "lmhead.hpp").write_text('const char* s = "a // c";\n')      # inside a string: code
+    assert bench.kernel_source_hash("lmhead") != h0
+    (src / "lmhead.hpp").write_text('const char* s = "a // b";\n')
+    (src / "common.hpp").write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash("lmhead") != h0
