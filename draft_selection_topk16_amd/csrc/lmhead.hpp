@@ -622,8 +622,16 @@ __global__ __launch_bounds__(kWG) void k_lmhead_merge(LmArgs a) {
     for (int j = 0; j < KMAX; ++j) kth = (j == K - 1) ? x[j] : kth;
     const uint64_t head = x[0];
     __syncthreads();
-    // bound 1: the best K-th word of any list (K words reach it)
-    if (tid < nl) __hip_atomic_fetch_max(&sm.tk, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // bound 1: the best K-th word of any list (K words reach it): a maximum
+    // within each wave, then one LDS atomic per wave (atomics of all 256
+    // threads on one word serialise, about 4 us; lists past nl hold 0)
+    uint64_t wk = kth;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t y = __shfl_xor(wk, o);
+        wk = y > wk ? y : wk;
+    }
+    if ((tid & 63) == 0) __hip_atomic_fetch_max(&sm.tk, wk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     sm.heads[tid] = head;
     __syncthreads();
     // bound 2: the K-th best head (K heads reach it)
