@@ -6,31 +6,35 @@
 // adjacent pair with S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, and walks
 // the scores once from the last verified token.
 //
-// dflash2_select runs in two launches by default (k_scan, then k_tail), or
-// in one (k_select), as the plan decides.  Workgroups are dealt out in index
-// order, and each one's job follows from its index:
-//   * the first n_gate compute one slice of one gate tile (a partial of H)
-//     and count it on the tile row's counter (in two launches with M <= 16
-//     rows, the tile's last slice sums the partials into H and counts the
-//     tile instead);
+// dflash2_select runs in two launches by default, k_scanm and then
+// k_pairs_walk (three stages: scan with the row merges, pairs, walk); the
+// plan can also run it as k_scan then k_tail, or as the single k_select.
+// Workgroups are dealt out in index order, and each one's job follows from
+// its index:
+//   * the first n_gate compute one slice of one gate tile (a partial of H);
+//     with M <= 16 rows (outside the fused launch) the tile's last slice sums
+//     the partials into H;
 //   * every other one streams one segment of one logits row (every nseg-th
-//     chunk of it), leaving a sorted list of K candidates per wave; in the
-//     single launch it then arrives on the row's counter, and the last to
-//     arrive goes on with the row (row_tail); in two launches k_scan ends
-//     here and k_tail runs row_tail for every row, one workgroup per row.
+//     chunk of it), leaving a sorted list of K candidates per wave, and (in
+//     k_scanm and k_select) arrives on the row's counter.
 // The work after the segments is handed on by "last arrival": nobody waits
-// for a producer except for the gate, below.
+// for a producer except the fused launch's row merges for the gate, below.
 //   row:      the last segment of a row merges the row's lists into its
-//             top-K (ids and logits) and arrives on the counters of the two
-//             transitions the row takes part in (t - 1 -> t and t -> t + 1);
-//   pairs:    the second row of a transition to arrive scores it (the first
-//             transition of a sequence needs only its own row);
+//             top-K (ids and logits).  In k_scanm that is all; k_pairs_walk
+//             then scores the transition into every row (one workgroup per
+//             row), taking H_t from the tile sums or summing the partials.
+//             In k_select and k_tail the row merge also sums H_t and arrives
+//             on the counters of the two transitions the row takes part in
+//             (t - 1 -> t and t -> t + 1);
+//   pairs:    (k_select, k_tail) the second row of a transition to arrive
+//             scores it (the first transition of a sequence needs only its
+//             own row);
 //   walk:     the last transition of a sequence to be scored walks it.
-// The row merge sums H_t from the gate partials in slice order (or loads
-// the tile sums' row of H); it waits (bounded spin) for the gate tile row to
-// be complete.  Gate workgroups have the lowest indexes and never wait, so
-// they have all been dispatched by the time any row merge runs, and every
-// wait ends.
+// In k_select and k_tail the row merge sums H_t from the gate partials in
+// slice order (or loads the tile sums' row of H) and waits (bounded spin)
+// for the gate tile row to be complete; in k_tail it already is.  Gate
+// workgroups have the lowest indexes and never wait, so they have all been
+// dispatched by the time any row merge runs, and every wait ends.
 // Counters live in the scratch buffer and are reset by the workgroup that
 // consumes them, so every launch starts from zero without a memset.
 #include <hip/hip_runtime.h>
@@ -78,12 +82,12 @@ struct Params {
     float* ppart;         // [S, M, r] gate partials
     float* Sb;            // [rows, K, K] pair scores
     float* Hb;            // [rows, r] gate rows (summed by the row merges, or by each
-                          // gate tile's last slice in two launches with M <= 16)
+                          // gate tile's last slice with M <= 16 outside k_select)
     uint32_t* err;        // device input-error flags
     uint32_t* row_cnt;    // [rows] segments done
     uint32_t* edge_cnt;   // [rows] rows ready of transition t - 1 -> t
     uint32_t* seq_cnt;    // [B] transitions scored
-    uint32_t* gate_cnt;   // [mtiles] gate slices done (M <= 16 in two launches: tiles summed)
+    uint32_t* gate_cnt;   // [mtiles] gate slices done (M <= 16: tiles summed; unused by k_scanm)
     uint32_t* rd_cnt;     // [mtiles] pair jobs past the gate wait
     // sizes
     int B, P, V, d, r, K;
@@ -130,22 +134,25 @@ struct GateShape {
 
 // One slice of one gate tile.  HSUM (the two-launch kernels with a gate of
 // one m-block, M <= 16 rows): the tile's last slice to finish sums the S
-// partials in slice order into the gate rows Hb, so that a row merge loads
-// one row of H instead of S partial rows, and counts the tile on its tile
-// row.  Otherwise each slice counts itself on the tile row and every row
-// merge sums its own row's partials (at M = 56 and 224 the tile sums
-// lengthened the scan launch by 5-6 us).  Either way the sum runs in slice
-// order, so the result never depends on timing.
-template <bool BF16, int MB, bool HSUM>
+// partials in slice order into the gate rows Hb, so that a reader loads one
+// row of H instead of S partial rows, and counts the tile on its tile row.
+// Otherwise each slice counts itself on the tile row and every reader sums
+// its own row's partials (at M = 56 and 224 the tile sums lengthened the
+// scan launch by 5-6 us).  Either way the sum runs in slice order, so the
+// result never depends on timing.  ARRIVE = false (k_scanm, whose readers
+// run in the next launch): no count at all.
+template <bool BF16, int MB, bool HSUM, bool ARRIVE = true>
 __device__ void gate_role(const Params& p, int gb, GateLds& sm) {
     const int s = gb % p.S, tile = gb / p.S;
     const int mt = tile / p.ntiles, nt = tile % p.ntiles;
     gate_slice<BF16, MB, GateShape<MB>::NB>(p.hidden, p.W, (int)p.rows, p.d, p.r, mt, nt, s, p.S,
                                             p.ppart, sm);
     if constexpr (!HSUM) {
-        drain_stores();
-        __syncthreads();
-        if (threadIdx.x == 0) arrive(&p.gate_cnt[mt]);
+        if constexpr (ARRIVE) {
+            drain_stores();
+            __syncthreads();
+            if (threadIdx.x == 0) arrive(&p.gate_cnt[mt]);
+        }
     } else {
         __shared__ uint32_t last;
         if (!block_arrive_last(&p.tile_cnt[tile], (uint32_t)p.S, &last)) return;
@@ -187,9 +194,11 @@ __device__ void gate_role(const Params& p, int gb, GateLds& sm) {
                 for (int e = 0; e < CG; ++e) xstore(p.Hb + m * p.r + c + e, h[e]);
             }
         }
-        drain_stores();
-        __syncthreads();
-        if (tid == 0) arrive(&p.gate_cnt[mt]);
+        if constexpr (ARRIVE) {
+            drain_stores();
+            __syncthreads();
+            if (tid == 0) arrive(&p.gate_cnt[mt]);
+        }
     }
 }
 
@@ -212,7 +221,7 @@ __device__ __forceinline__ int32_t checked_id(int32_t id, int V, uint32_t* err, 
 // Pair scores of positions e0 .. e0 + ne - 1 of sequence b (fused launch).
 // own: the row this workgroup merged; hown: its gate row (floats tid and
 // tid + 256 of this thread).  The other position's gate row comes from Hb.
-template <bool BF16>
+template <bool BF16, bool SUMH = false>
 __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
                             const float (&hown)[2], PairLds& sm) {
     const int tid = threadIdx.x, K = p.K, r = p.r;
@@ -225,11 +234,13 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
     const bool cur_row = tid >= 64 && tid < 64 + ne * K;
     const int x = cur_row ? tid - 64 : 0, q = x / K, k = x % K;
     float hv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    if constexpr (!SUMH) {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int64_t grow = min(rb + e0 + qq, (int64_t)p.rows - 1);
-        hv[qq][0] = xload(p.Hb + grow * r + min(tid, r - 1));
-        if (r > kWG) hv[qq][1] = xload(p.Hb + grow * r + min(tid + kWG, r - 1));
+        for (int qq = 0; qq < 2; ++qq) {
+            const int64_t grow = min(rb + e0 + qq, (int64_t)p.rows - 1);
+            hv[qq][0] = xload(p.Hb + grow * r + min(tid, r - 1));
+            if (r > kWG) hv[qq][1] = xload(p.Hb + grow * r + min(tid + kWG, r - 1));
+        }
     }
     const int64_t crow = prev_row ? rb + max(e0 - 1, 0) : rb + e0 + q;
     const int ck = prev_row ? tid : k;
@@ -253,14 +264,35 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
         sm.ids[1 + q][k] = checked_id(id, p.V, p.err, 2u);
         sm.u[q][k] = uval;
     }
+    if constexpr (SUMH) {
+        pair_sum_gate(p.ppart, p.S, p.rows, r, rb + e0, ne, sm);
+    } else {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
+        for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            if (qq < ne && tid + u * kWG < r)
-                sm.H[qq][tid + u * kWG] = (rb + e0 + qq == own) ? hown[u] : hv[qq][u];
+            for (int u = 0; u < 2; ++u)
+                if (qq < ne && tid + u * kWG < r)
+                    sm.H[qq][tid + u * kWG] = (rb + e0 + qq == own) ? hown[u] : hv[qq][u];
+    }
     __syncthreads();
     pair_tiles<BF16>(p.A, p.Bt, K, r, e0, ne, p.Sb + (rb + e0) * K * K, sm, [] {});
+}
+
+// The walk of sequence b over its scored transitions, in the launch's walk
+// mode.  Every thread of the workgroup calls.
+template <bool SAMPLE>
+__device__ __forceinline__ void walk_of(const Params& p, int b, SharedAll& sm) {
+    const int K = p.K, P = p.P;
+    const int64_t rb = (int64_t)b * P;
+    const float* Sq = p.Sb + rb * K * K;
+    const int32_t* ids = p.cand + rb * K;
+    if constexpr (SAMPLE)
+        chain_seq<kChainSample>(Sq, ids, p.u + rb, p.inv_tau, P, K, p.out_path + rb, p.out_q + rb,
+                                p.out_score + b, sm.wk);
+    else if (p.walk == kWalkGreedy)
+        chain_seq<kChainGreedy>(Sq, ids, nullptr, 0.f, P, K, p.out_path + rb, nullptr, p.out_score + b, sm.wk);
+    else
+        walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
 // Everything after a row's segments: the row merge (with the gate row H_t),
@@ -373,16 +405,40 @@ __device__ __forceinline__ void row_tail(const Params& p, int64_t row, SharedAll
     __syncthreads();
     if (!flag) return;
     if (tid == 0) reset_counter(&p.seq_cnt[b]);
-    const int64_t rb = (int64_t)b * P;
-    const float* Sq = p.Sb + rb * K * K;
-    const int32_t* ids = p.cand + rb * K;
-    if constexpr (SAMPLE)
-        chain_seq<kChainSample>(Sq, ids, p.u + rb, p.inv_tau, P, K, p.out_path + rb, p.out_q + rb,
-                                p.out_score + b, sm.wk);
-    else if (p.walk == kWalkGreedy)
-        chain_seq<kChainGreedy>(Sq, ids, nullptr, 0.f, P, K, p.out_path + rb, nullptr, p.out_score + b, sm.wk);
-    else
-        walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+    walk_of<SAMPLE>(p, b, sm);
+}
+
+// The three-stage plan's scan launch: the last segment of a row merges its
+// lists and leaves the row's candidates for the pair launch.  Nothing here
+// waits on the gate: the pair launch takes H_t once the whole scan is done.
+template <bool BF16>
+__device__ __forceinline__ void row_merge_only(const Params& p, int64_t row, SharedAll& sm) {
+    merge_row<BF16>(p.part + (size_t)row * p.nseg * kWaves * p.K, p.nseg * kWaves, p.K,
+                    p.cand + row * p.K, p.cval + row * p.K, sm.m);
+}
+
+// The three-stage plan's second launch, one workgroup per row t of sequence
+// b: the pair scores of the transition into t (every input is in memory
+// already: no hand-off before it), then the last transition of the sequence
+// to be scored walks it.
+template <bool BF16, bool SAMPLE, bool HSUM>
+__device__ __forceinline__ void pairs_walk(const Params& p, int64_t row, SharedAll& sm,
+                                           uint32_t& flag) {
+    const int tid = threadIdx.x, P = p.P;
+    const int b = (int)(row / P), t = (int)(row % P);
+    const float hz[2] = {0.f, 0.f};
+    pairs_fused<BF16, !HSUM>(p, b, t, 1, -1, hz, sm.pr);
+    drain_stores();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&p.seq_cnt[b], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        flag = (old + 1u == (uint32_t)P) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!flag) return;
+    if (tid == 0) reset_counter(&p.seq_cnt[b]);
+    walk_of<SAMPLE>(p, b, sm);
 }
 
 // The whole selector in one launch.
@@ -428,6 +484,33 @@ __global__ __launch_bounds__(kWG, 5) void k_tail(Params p) {
     __shared__ SharedAll sm;
     __shared__ uint32_t flag;
     row_tail<BF16, MB, SAMPLE, MB == 1>(p, (int64_t)blockIdx.x, sm, flag);
+}
+
+// The selector in three stages over two launches: k_scanm runs the gate
+// slices, the segments and, on a row's last arrival, its merge; k_pairs_walk
+// scores every transition (one workgroup per row) and walks each sequence.
+template <bool BF16, int NV, int MB>
+__global__ __launch_bounds__(kWG, 5) void k_scanm(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    const int64_t g = blockIdx.x;
+    if (g < p.n_gate) {
+        gate_role<BF16, MB, MB == 1, false>(p, (int)g, sm.g);
+        return;
+    }
+    const int64_t sb = g - p.n_gate;
+    const int64_t row = sb / p.nseg;
+    segment_of<BF16, NV, true>(p, row, (int)(sb % p.nseg), sm.c);
+    if (!block_arrive_last(&p.row_cnt[row], (uint32_t)p.nseg, &flag)) return;
+    if (threadIdx.x == 0) reset_counter(&p.row_cnt[row]);
+    row_merge_only<BF16>(p, row, sm);
+}
+
+template <bool BF16, int MB, bool SAMPLE>
+__global__ __launch_bounds__(kWG, 5) void k_pairs_walk(Params p) {
+    __shared__ SharedAll sm;
+    __shared__ uint32_t flag;
+    pairs_walk<BF16, SAMPLE, MB == 1>(p, (int64_t)blockIdx.x, sm, flag);
 }
 
 // Top-K alone: segments, then the row merge on last arrival.
@@ -647,7 +730,8 @@ struct Overrides {
     int mwords = 0;       // most candidate words one row merge takes (<= 1024)
     int gate_s = 0;       // gate slices of d (1..16)
     int conv_s = 0;       // k slices of the convolution's correction GEMM
-    int launches = 0;     // dflash2_select: 1 = one fused launch, 2 = scan then tail
+    int launches = 0;     // dflash2_select: 1 = one fused launch, 2 = scan then tail,
+                          // 3 = scan with the row merges, then pairs and walk
     int lm_ranges = 0;    // vocabulary ranges of the LM head (1..256)
     int gate_giveup = 0;  // 1: the row merges' gate wait gives up (failure-handling tests)
 };
@@ -698,6 +782,7 @@ int cu_count() {
 struct Plan {
     Params p;
     bool two = false;           // scan and tail as two launches
+    bool three = false;         // two launches, the row merges in the first
     int nv = 1;
     int mb = 4;                 // gate tile: 16*mb rows x 16*(mb == 1 ? 4 : 2) columns
     bool bf16 = true;
@@ -853,6 +938,14 @@ void launch_select(const Plan& pl, hipStream_t stream) {
     dim3 block(kWG);
 #define DF2_SEL_W(BF, NV_, MB_, SM)                                                            \
     do {                                                                                       \
+        if (pl.three) {                                                                        \
+            hipLaunchKernelGGL((k_scanm<BF, NV_, MB_>),                                        \
+                               dim3((unsigned)(pl.p.n_gate + pl.n_chunk_blocks)), block, 0,    \
+                               stream, pl.p);                                                  \
+            hipLaunchKernelGGL((k_pairs_walk<BF, MB_, SM>), dim3((unsigned)pl.p.rows), block, 0,    \
+                               stream, pl.p);                                                  \
+            break;                                                                             \
+        }                                                                                      \
         if (pl.two) {                                                                          \
             hipLaunchKernelGGL((k_scan<BF, NV_, MB_>),                                         \
                                dim3((unsigned)(pl.p.n_gate + pl.n_chunk_blocks)), block, 0,    \
@@ -967,19 +1060,22 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = bf16;
     plan_gate(pl, rows, dims->d, dims->r, ov);
-    // Two launches (k_scan, then k_tail) when the gate and one segment per
-    // row fit one resident wave of workgroups; otherwise the single fused
-    // launch, whose row tails overlap the streaming of later waves (B = 256,
-    // P = 15, V = 262144: 490 us fused against 523 us in two launches; at
-    // batch 32, 35.2 us in two launches against 37.8 fused).  The launches
-    // plan knob forces either.  Segment workgroups: about three per CU for the scan
-    // launch, two and a half for the fused one, within what the gate leaves
-    // of one resident wave.  Measured at V = 151936, d = 5120 (bf16): two
-    // launches at batch 32 ran 35.2 us per cycle with 3 segments per row
-    // against 36.3 with 2; the fused launch ran 2 per row 1.5 us faster than
-    // 3 (and 11 to 14 per row at batch 8 4 us faster than 16).
+    // Three stages in two launches by default: k_scanm (gate slices,
+    // segments, and each row's merge on its last segment's arrival), then
+    // k_pairs_walk.  Nothing in k_scanm waits: a row merge that waited there
+    // for its gate tile row slowed the gate slices on its CU (at batch 32 the
+    // slowest slices went from 16 to 27 us).  Measured at V = 151936 (bf16,
+    // us per call, three stages / scan then tail / fused): batch 1 (d = 2560)
+    // 18.2 / 19.6 / 20.8, batch 8 (d = 5120) 22.3 / 23.4 / 26.4, batch 32
+    // 31.9 / 33.8 / 37.0; B = 256, P = 15, V = 262144: 481 / 527 / 488.  The
+    // launches plan knob forces any of the three.  Segment workgroups: about
+    // three per CU for the two-launch plans, two and a half for the fused one,
+    // within what the gate leaves of one resident wave (batch 32, three
+    // stages: 31.8 us with 3 segments per row, 33.0 with 2, 34.2 with 4).
     const int64_t cap = select_capacity();
-    pl.two = ov.launches ? ov.launches == 2 : pl.p.n_gate + rows <= cap;
+    const int mode = ov.launches ? ov.launches : 3;
+    pl.two = mode >= 2;
+    pl.three = mode == 3;
     const int64_t cus = cu_count();
     const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, pl.two ? 3 * cus : (5 * cus) / 2);
     plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target), ov);
@@ -1388,7 +1484,7 @@ df2_status dflash2_plan_override(df2_plan_knob knob, int32_t value) {
         case DF2_PLAN_GATE_SLICES: g_over.gate_s = value; break;
         case DF2_PLAN_CONV_SLICES: g_over.conv_s = value; break;
         case DF2_PLAN_LAUNCHES:
-            if (value > 2) return fail(DF2_EINVAL, "launches must be 0, 1 or 2");
+            if (value > 3) return fail(DF2_EINVAL, "launches must be 0, 1, 2 or 3");
             g_over.launches = value;
             break;
         case DF2_PLAN_LM_RANGES:

@@ -80,12 +80,16 @@ typedef enum {
     DF2_PLAN_MERGE_WORDS = 2,   /* most candidate words one row merge takes (<= 1024) */
     DF2_PLAN_GATE_SLICES = 3,   /* slices of d of the gate projection (<= 16) */
     DF2_PLAN_CONV_SLICES = 4,   /* k slices of the convolution's correction GEMM */
-    DF2_PLAN_LAUNCHES = 5,      /* dflash2_select: 1 = one fused launch, 2 = scan then tail */
+    DF2_PLAN_LAUNCHES = 5,      /* dflash2_select: 1 = one fused launch, 2 = scan, then
+                                   merges, pairs and walk, 3 (automatic) = scan with the
+                                   row merges, then pairs and walk */
     DF2_PLAN_LM_RANGES = 6,     /* dflash2_lmhead_topk: vocabulary ranges (<= 256) */
     DF2_PLAN_GATE_GIVEUP = 7    /* failure-handling tests only: 1 = in dflash2_select
-                                   the row merges wait for one gate arrival more than
-                                   will come, give up after 64 sleeps and raise flag
-                                   bit 2; that call's outputs are not valid */
+                                   under launches 1 or 2 (the plans whose row merges
+                                   wait for the gate) the row merges wait for one gate
+                                   arrival more than will come, give up after 64
+                                   sleeps and raise flag bit 2; that call's outputs
+                                   are not valid */
 } df2_plan_knob;
 
 typedef enum {
@@ -112,10 +116,11 @@ typedef struct df2_dims {
 
 /*
  * The whole selector ("A Lightweight Path Selector": top-K, pair scores, one
- * walk from the last verified token), enqueued as two kernel launches (the
- * vocabulary scan with the gate, then the merges, pair scores and walks) or,
- * for batches too large for one resident wave of workgroups, as one fused
- * launch; the results are the same bits either way.
+ * walk from the last verified token), enqueued as two kernel launches: the
+ * vocabulary scan with the gate and the row merges, then the pair scores and
+ * walks.  The plan knob DF2_PLAN_LAUNCHES can move the row merges into the
+ * second launch or fuse everything into one; the results are the same bits
+ * in every plan.
  *   logits   [B, P, V]   drafter logits U_t
  *   hidden   [B, P, d]   drafter hidden states h_t
  *   A_tab    [V, r]      predecessor embeddings A(.)
@@ -336,9 +341,9 @@ df2_status dflash2_conv2(const void* x, const void* x_prev, const void* base,
  * scratch buffer and of the current device's no-allocation scratch: *flags
  * receives a bit mask (bit 0: a prev_tok outside
  * [0, V) was replaced by 0; bit 1: a cand_idx entry outside [0, V) was
- * replaced by 0; bit 2: a pair-score job of dflash2_select gave up waiting
- * for its gate rows, which only a fault elsewhere can cause, and its scores
- * are then unreliable).  A raised flag can leave a late gate arrival
+ * replaced by 0; bit 2: a row merge of dflash2_select gave up waiting for
+ * its gate rows (launches 1 or 2 only), which only a fault elsewhere can
+ * cause, and its scores are then unreliable).  A raised flag can leave a late gate arrival
  * counted in the stream's scratch, so after reporting one the next call on
  * that stream clears all its arrival counters before it launches.  Returns
  * DF2_OK, or DF2_EHIP.

@@ -391,13 +391,14 @@ def test_select_edge_shapes(B, P, V, K, d, dtype):
 
 
 @pytest.mark.parametrize("r", [320, 512])
-@pytest.mark.parametrize("launches", [1, 2])
+@pytest.mark.parametrize("launches", [1, 2, 3])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_select_wide_gate(r, launches, dtype):
     """Gate ranks above one value per thread (r > 256, up to the 512 the
     library accepts): the row merge sums a second gate value per thread, the
     pair job loads a second one per position and takes 16 k steps, in the
-    fused launch and in the two-launch path."""
+    fused launch and in both two-launch plans (in the three-stage one the
+    pair job takes H from the gate tile sums)."""
     say("select wide gate %s r=%d launches=%d" % (dtype, r, launches))
     wl = synth.Workload("wide", 1, B=3, P=5, V=3000, d=128, K=16, r=r, dtype=dtype, pair_scale=4.0)
     x = synth.make_inputs(wl, seed=r + 7)
@@ -421,12 +422,12 @@ def test_select_empty_batch():
 @pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1", "stress_b256"])
 def test_select_same_result_under_any_segment_plan(name):
     """The segment plan (segments per row, chunk width, words per merge) and
-    the choice of one fused launch or two (scan, then tail) change neither
-    the gate sums nor any comparison: candidate words are exact and the merge
-    is independent of how a row was cut, so path and score are bit-identical
-    across plans.  The stress workload defaults to the fused launch; forcing
-    two launches there gives a tail grid of 3840 rows, more than one
-    resident wave."""
+    the choice of launches (one fused, scan then tail, or the three-stage
+    default) change neither the gate sums nor any comparison: candidate words
+    are exact, the merge is independent of how a row was cut, and every plan
+    sums H in slice order, so path and score are bit-identical across plans.
+    At the stress workload the scan grid and the 3840-row second launch are
+    each more than one resident wave."""
     say("select under segment plans %s" % name)
     x = inputs(name)
     t = to_device(x)
@@ -436,7 +437,8 @@ def test_select_same_result_under_any_segment_plan(name):
     for knobs in ({"segment_wgs": 64}, {"segment_wgs": 700}, {"chunk_vectors": 1},
                   {"chunk_vectors": 2, "segment_wgs": 300}, {"merge_words": 256},
                   {"launches": 1}, {"launches": 1, "segment_wgs": 300},
-                  {"launches": 2}, {"launches": 2, "segment_wgs": 300}):
+                  {"launches": 2}, {"launches": 2, "segment_wgs": 300},
+                  {"launches": 3, "segment_wgs": 300}, {"launches": 3, "merge_words": 256}):
         with df2.plan(**knobs):
             p, s = df2.select(*args)
             torch.cuda.synchronize()
@@ -504,6 +506,24 @@ def test_gate_wait_give_up_then_recovery(launches):
             p, s = df2.select(*args)
             assert torch.equal(p, ref[0]) and torch.equal(s, ref[1])
         assert flags_clear()
+
+
+def test_gate_giveup_knob_inert_in_three_stage_plan():
+    """The three-stage plan has no gate wait (its pair jobs run after the
+    whole scan): with the give-up knob set it still returns the clean result
+    and raises no flag."""
+    say("select three-stage plan with the give-up knob")
+    x = inputs("t27b_b8")
+    t = to_device(x)
+    args = (t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], 16)
+    with df2.plan(launches=3):
+        ref = [a.clone() for a in df2.select(*args)]
+        assert flags_clear()
+        with df2.plan(gate_giveup=1):
+            p, s = df2.select(*args)
+            torch.cuda.synchronize()
+        assert flags_clear()
+        assert torch.equal(p, ref[0]) and torch.equal(s, ref[1])
 
 
 def test_stages_compose_to_select():
