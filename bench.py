@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the DFlash 2 path selector on one MI355X.
 
-One step = one dflash2_select call over one batch (two launches: the scan,
-then the tail): top-K of every logits row, the gate projection, all pair
-scores and the walk.  Inputs are seeded
+One step = one dflash2_select call over one batch (two launches: the scan
+with the row merges, then the pair scores and walks): top-K of every logits
+row, the gate projection, all pair scores and the walk.  Inputs are seeded
 synthetic data resident in HBM; several copies of the per-cycle inputs
 (logits, hidden) are rotated so that the 256 MB Infinity Cache cannot serve
 them from the previous step.
@@ -560,7 +560,7 @@ def main():
         "timing": res,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(wl.name),
-                     "kernel": "k_scan + k_tail (one dflash2_select call: scan launch, then tail launch)",
+                     "kernel": "k_scanm + k_pairs_walk (one dflash2_select call: the scan with the row merges, then pairs and walks)",
                      "algorithmic_bytes_per_launch": abytes},
     }
     if not args.no_greedy:
