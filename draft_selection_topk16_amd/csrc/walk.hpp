@@ -34,23 +34,31 @@ constexpr int kWalkIds = 1024;      // candidate ids kept in LDS (P * K at most)
 
 struct WalkLds {
     float ST[kWalkS];               // [t][j][i] over Kp x Kp, zero padded
-    uint8_t psi[kMaxP * kMaxK];
+    uint8_t psi[kMaxP * kMaxK];     // Viterbi: [j][t], row j of kMaxP positions
     int32_t ids[kWalkIds];
     int32_t rank[kMaxP];
     float qpick[kMaxP];             // sampling walk: probability of each choice
 };
+
+// The larger of two floats, as the plain instruction (fmaxf quiets each
+// operand first; a NaN never decides a choice here).
+__device__ __forceinline__ float walk_max(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // Best of one lane's values v[0..16) (predecessors i0 .. i0 + 15): the
 // largest value by a max tree, then its smallest index.
 __device__ __forceinline__ void best_of16(const float (&v)[16], int i0, float& best, int& arg) {
     float m8[8], m4[4], m2[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) m8[u] = fmaxf(v[2 * u], v[2 * u + 1]);
+    for (int u = 0; u < 8; ++u) m8[u] = walk_max(v[2 * u], v[2 * u + 1]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) m4[u] = fmaxf(m8[2 * u], m8[2 * u + 1]);
+    for (int u = 0; u < 4; ++u) m4[u] = walk_max(m8[2 * u], m8[2 * u + 1]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) m2[u] = fmaxf(m4[2 * u], m4[2 * u + 1]);
-    best = fmaxf(m2[0], m2[1]);
+    for (int u = 0; u < 2; ++u) m2[u] = walk_max(m4[2 * u], m4[2 * u + 1]);
+    best = walk_max(m2[0], m2[1]);
     arg = i0 + 15;
 #pragma unroll
     for (int u = 14; u >= 0; --u) arg = (v[u] == best) ? i0 + u : arg;
@@ -101,9 +109,67 @@ __device__ float walk_steps(int t0, int t1, int K, float delta, WalkLds& sm) {
         }
         delta = __int_as_float((int)((__float_as_int(best) & keep) | (ninf & ~keep)));
         // arg < K for finite scores; the clamp keeps NaN inputs in bounds
-        if (jv) sm.psi[t * K + j] = (uint8_t)min(arg, K - 1);
+        if (jv) sm.psi[j * kMaxP + t] = (uint8_t)min(arg, K - 1);
     }
     return delta;
+}
+
+// One quad_perm DPP move: lane l of each group of four takes lane sel[l].
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_mov(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadSwap1 = 0xB1;    // lanes 1, 0, 3, 2
+constexpr int kQuadSwap2 = 0x4E;    // lanes 2, 3, 0, 1
+
+// Wave 0, K <= 16: delta over positions [t0, t1) of a group held in sm.ST
+// (Kp = 16), four lanes per candidate.  Lane 4 j + q takes predecessors
+// 4 q .. 4 q + 3 of candidate j: delta_{t-1} of those four comes from the
+// lanes that hold it (ds_bpermute from lanes 16 q + 4 k), the column piece
+// S_t(4q .. 4q + 3, j) with one 16-byte LDS read one step ahead, and the
+// quad combines its four partial results by DPP: the largest value, then
+// the smallest predecessor that reaches it.  Lane 4 j writes psi_t(j).
+// dl: delta(j) of the position before t0 in every lane of quad j (any value
+// when t0 = 0); returns it for the group's last position.  Candidates j >= K
+// hold -inf.
+__device__ float walk_steps_quad(int t0, int t1, int K, float dl, WalkLds& sm) {
+    const int lane = lane_id();
+    const int j = lane >> 2, q = lane & 3;
+    const bool jv = j < K;
+    const float* col = sm.ST + j * 16 + 4 * q;
+    const int src = 64 * q;                     // byte address of lane 16 q
+    float4 s = *reinterpret_cast<const float4*>(col);
+#pragma unroll 1
+    for (int t = t0; t < t1; ++t) {
+        if (t == 0) {
+            // delta_0(j) = S_0(prev, j): row 0 of the first block
+            dl = jv ? s.x : -INFINITY;
+            s = *reinterpret_cast<const float4*>(col + min(1, t1 - 1 - t0) * 256);
+            continue;
+        }
+        const int di = __float_as_int(dl);
+        const float dx = __int_as_float(__builtin_amdgcn_ds_bpermute(src, di));
+        const float dy = __int_as_float(__builtin_amdgcn_ds_bpermute(src + 16, di));
+        const float dz = __int_as_float(__builtin_amdgcn_ds_bpermute(src + 32, di));
+        const float dw = __int_as_float(__builtin_amdgcn_ds_bpermute(src + 48, di));
+        const float4 sn = *reinterpret_cast<const float4*>(col + min(t + 1 - t0, t1 - 1 - t0) * 256);
+        const float v0 = s.x + dx, v1 = s.y + dy, v2 = s.z + dz, v3 = s.w + dw;
+        const float m = walk_max(walk_max(v0, v1), walk_max(v2, v3));
+        int a = 3;
+        a = (v2 == m) ? 2 : a;
+        a = (v1 == m) ? 1 : a;
+        a = (v0 == m) ? 0 : a;
+        float mq = walk_max(m, __uint_as_float(quad_mov<kQuadSwap1>(__float_as_uint(m))));
+        mq = walk_max(mq, __uint_as_float(quad_mov<kQuadSwap2>(__float_as_uint(mq))));
+        uint32_t c = (m == mq) ? (uint32_t)(4 * q + a) : 255u;
+        c = min(c, quad_mov<kQuadSwap1>(c));
+        c = min(c, quad_mov<kQuadSwap2>(c));
+        dl = jv ? mq : -INFINITY;
+        // c < K for finite scores; the clamp keeps NaN inputs in bounds
+        if (q == 0 && jv) sm.psi[j * kMaxP + t] = (uint8_t)min((int)c, K - 1);
+        s = sn;
+    }
+    return dl;
 }
 
 // The walk of one sequence.  S: [P, K, K] scores (row i = predecessor rank,
@@ -144,7 +210,7 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
         }
         __syncthreads();
         if (w == 0) {
-            if (KP == 16) delta = walk_steps<16>(t0, t1, K, delta, sm);
+            if (KP == 16) delta = walk_steps_quad(t0, t1, K, delta, sm);
             else if (KP == 32) delta = walk_steps<32>(t0, t1, K, delta, sm);
             else delta = walk_steps<64>(t0, t1, K, delta, sm);
         } else if (t0 == 0 && ids_lds) {
@@ -164,38 +230,51 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
     }
     if (w != 0) return;
     // final pick (smaller rank on ties): every lane reduces the broadcast
-    // deltas, then backtracks through psi
+    // deltas (candidate j in lane 4 j with K <= 16, else in lane j), then
+    // backtracks through psi
     float m = -INFINITY;
     int jb = 0;
-    for (int c = 0; c < K; c += 16) {
+    if (KP == 16) {
+        // candidates j >= K already hold -inf
         float v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-            v[u] = (c + u < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), min(c + u, 63)))
-                               : -INFINITY;
-        float cb;
-        int ca;
-        best_of16(v, c, cb, ca);
-        if (c == 0 || cb > m) {
-            m = cb;
-            jb = ca;
+        for (int u = 0; u < 16; ++u) v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), 4 * u));
+        best_of16(v, 0, m, jb);
+    } else {
+        for (int c = 0; c < K; c += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = (c + u < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), min(c + u, 63)))
+                                   : -INFINITY;
+            float cb;
+            int ca;
+            best_of16(v, c, cb, ca);
+            if (c == 0 || cb > m) {
+                m = cb;
+                jb = ca;
+            }
         }
     }
-    // backtrack (jj is uniform)
-    int jj = min(jb, K - 1);
-    for (int t = P - 1; t > 0; --t) {
-        if (lane == 0) sm.rank[t] = jj;
-        jj = sm.psi[t * K + jj];
+    // backtrack (jj is uniform): lane j holds psi_t(j) of sixteen positions
+    // (one 16-byte read of its row), each step is one readlane, and lane t
+    // keeps the rank chosen at position t (P <= 64)
+    int jj = __builtin_amdgcn_readfirstlane(min(jb, K - 1));
+    int rk = 0;
+    for (int g = (P - 1) & ~15; g >= 0; g -= 16) {
+        const uint4 pw = *reinterpret_cast<const uint4*>(sm.psi + lane * kMaxP + g);
+#pragma unroll
+        for (int u = 15; u >= 0; --u) {
+            const int t = g + u;
+            if (t > P - 1 || t < 1) continue;
+            rk = (lane == t) ? jj : rk;
+            const uint32_t wd = u < 4 ? pw.x : (u < 8 ? pw.y : (u < 12 ? pw.z : pw.w));
+            jj = (int)((__builtin_amdgcn_readlane(wd, jj) >> (8 * (u & 3))) & 0xffu);
+        }
     }
-    if (lane == 0) {
-        sm.rank[0] = jj;
-        *out_score = m;
-    }
-    wave_sync();
-    for (int t = lane; t < P; t += 64) {
-        const int rk = sm.rank[t];
-        out_path[t] = ids_lds ? sm.ids[t * K + rk] : xload(ids + (int64_t)t * K + rk);
-    }
+    rk = (lane == 0) ? jj : rk;
+    if (lane == 0) *out_score = m;
+    if (lane < P) out_path[lane] = ids_lds ? sm.ids[lane * K + rk] : xload(ids + (int64_t)lane * K + rk);
 }
 
 // Walks whose choice at t depends only on the row of the token chosen at

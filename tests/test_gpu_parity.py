@@ -262,11 +262,17 @@ def test_viterbi_stage(K, P):
         assert abs(score[b] - sc[b]) <= 1e-5 * P * 4
 
 
-def test_viterbi_integer_ties_exact():
+@pytest.mark.parametrize("K,P", [(8, 6), (16, 7), (13, 20), (16, 64), (4, 33), (1, 3), (32, 17), (64, 5)])
+def test_viterbi_integer_ties_exact(K, P):
     """Small-integer scores are exact in fp32: ties must break exactly like
-    the oracle (smaller predecessor rank, smaller final rank)."""
-    rng = np.random.default_rng(42)
-    B, P, K = 16, 6, 8
+    the oracle (smaller predecessor rank, smaller final rank).  K <= 16 runs
+    four lanes per candidate (K = 13 and 4 leave some quads idle and pad the
+    predecessors with -inf;
+    P = 20, 33 and 64 span two to four groups of sixteen positions in LDS and
+    of the backtrack); K = 32 and 64 one lane per candidate."""
+    say("viterbi integer ties K=%d P=%d" % (K, P))
+    rng = np.random.default_rng(42 + K * 1000 + P)
+    B = 16
     S = rng.integers(-2, 3, size=(B, P, K, K)).astype(np.float32)
     S[:, 0, 1:, :] = S[:, 0, :1, :]
     cand = np.tile(np.arange(K, dtype=np.int32), (B, P, 1)) + 1000
