@@ -500,9 +500,13 @@ __device__ __forceinline__ void segment_topk(const void* __restrict__ row, int V
 // descending, zero padded; written by other workgroups, read with xload);
 // nl * K <= kMergeMax.  emit(rank, word) runs once for every rank < K, in
 // the thread that holds the word.  Every thread of the workgroup calls.
-// The bound is the larger of the best K-th word of any list and the
-// smallest c-th word over all lists (c = ceil(K / nl)): at least K words
-// reach either.
+// The bound, with c = ceil(K / nl): when nl * c <= 64, the K-th largest value
+// key among the first ch = max(c, min(K, 64 / nl)) words of every list (at
+// least K words reach it; every list's first c words reach its c-th word, so
+// this is never below the smallest c-th word), and with fewer lists than K
+// also the best K-th word of any list; otherwise the larger of the best K-th
+// word of any list and the smallest c-th word over all lists (at least K
+// words reach either).
 // pre() runs right after the list loads are issued and mid() right after the
 // first barrier, so that a caller can overlap loads of its own with the merge.
 template <typename Emit, typename Pre, typename Mid>
@@ -523,18 +527,23 @@ __device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, in
     pre();
     __syncthreads();
     mid();
-    // Few lists: the best K-th word of any list and the smallest c-th word
-    // (LDS atomics, at most 2 nl of them).  Many lists (K <= nl <= 64): the
-    // K-th largest head key, which is much sharper and avoids contended
-    // atomics.
-    const bool heads = nl >= K && nl <= 64;
+    // Up to 64 heads (the first ch words of each list): the K-th largest
+    // head key, found by one wave, which is much sharper than the list
+    // bounds (at batch 32, 12 lists of 16: 56 words survived the list
+    // bounds).  Otherwise the best K-th word of any list and the smallest
+    // c-th word (LDS atomics, at most 2 nl of them).
+    const bool heads = nl * c <= 64;
+    const int ch = heads ? max(c, min(K, 64 / nl)) : c;
+    const int nh = nl * ch;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int e = q * kWG + tid;
         if (e < n) {
             const int k = e % K;
             if (heads) {
-                if (k == 0) sm.surv[e / K] = x[q];
+                if (k < ch) sm.surv[(e / K) * ch + k] = x[q];
+                if (nl < K && k == K - 1)
+                    __hip_atomic_fetch_max(&sm.tk, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             } else {
                 if (k == K - 1)
                     __hip_atomic_fetch_max(&sm.tk, x[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -544,12 +553,12 @@ __device__ void block_merge_lists(const uint64_t* __restrict__ lists, int nl, in
         }
     }
     __syncthreads();
-    uint64_t T = heads ? 0ull : (sm.tk > sm.tc ? sm.tk : sm.tc);
+    uint64_t T = heads ? sm.tk : (sm.tk > sm.tc ? sm.tk : sm.tc);
     if (heads) {
-        // With many lists: the K-th largest value key among the lists'
-        // heads (K heads reach it), by a bitwise search over ballot counts.
+        // The K-th largest value key among the heads (K heads reach it), by
+        // a bitwise search over ballot counts.
         if (tid < 64) {
-            const uint32_t hk = (lane < nl) ? (uint32_t)(sm.surv[lane] >> 32) : 0u;
+            const uint32_t hk = (lane < nh) ? (uint32_t)(sm.surv[lane] >> 32) : 0u;
             uint32_t th = 0;
             for (int bit = keybits - 1; bit >= 0; --bit) {
                 const uint32_t cb = th | (1u << bit);
