@@ -798,7 +798,7 @@ struct Plan {
 // that about `target` workgroups stream in total; a row's segment lists
 // must fit one merge.
 void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logits,
-               int64_t target, const Overrides& ov) {
+               int64_t target, const Overrides& ov, int mwords_default = kMergeMax) {
     Params& p = pl.p;
     pl.bf16 = bf16;
     const int pv = bf16 ? 8 : 4;
@@ -817,9 +817,9 @@ void plan_topk(Plan& pl, int64_t rows, int V, int K, bool bf16, const void* logi
     p.C = chunks(nv);
     if (ov.wgs > 0) target = ov.wgs;
     target = std::max<int64_t>(1, std::min<int64_t>(target, 1 << 30));
-    // at most kMergeMax words per row merge; fewer lists also make the merge
-    // bound sharper
-    const int mwords = ov.mwords > 0 ? std::min(kMergeMax, ov.mwords) : kMergeMax;
+    // at most mwords_default (the knob: at most kMergeMax) words per row
+    // merge; fewer lists also make the merge bound sharper
+    const int mwords = std::min(kMergeMax, ov.mwords > 0 ? ov.mwords : mwords_default);
     const int max_segs = std::max(1, mwords / (kWaves * K));
     int nseg = (int)std::min<int64_t>(p.C, std::max<int64_t>(1, target / rows));
     p.nseg = std::min(nseg, max_segs);
@@ -933,6 +933,8 @@ df2_status launch_checked(F&& f, const char* what) {
 }
 
 // One fused launch (k_select), or the scan launch and then the tail launch.
+constexpr int kSelectMergeWords = 768;
+
 void launch_select(const Plan& pl, hipStream_t stream) {
     const int64_t n2 = pl.p.n_gate + pl.n_chunk_blocks;
     dim3 block(kWG);
@@ -1060,6 +1062,9 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     std::memset(&pl.p, 0, sizeof(pl.p));
     pl.bf16 = bf16;
     plan_gate(pl, rows, dims->d, dims->r, ov);
+    // Row merges of the selector take at most 768 words (12 segments per row
+    // at K = 16): at batch 8 (V = 151936, d = 5120) 21.1 us per call against
+    // 21.6 with 13 segments per row (832 words), batch 1 and 32 unchanged.
     // Three stages in two launches by default: k_scanm (gate slices,
     // segments, and each row's merge on its last segment's arrival), then
     // k_pairs_walk.  Nothing in k_scanm waits: a row merge that waited there
@@ -1078,7 +1083,7 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     pl.three = mode == 3;
     const int64_t cus = cu_count();
     const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, pl.two ? 3 * cus : (5 * cus) / 2);
-    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target), ov);
+    plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target), ov, kSelectMergeWords);
     if (pl.p.n_gate + pl.n_chunk_blocks > 0x7FFFFFFF) return fail(DF2_EUNSUPPORTED, "problem too large");
     plan_layout(pl, rows, rows, dims->B, true);
     Params& p = pl.p;

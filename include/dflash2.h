@@ -77,7 +77,8 @@ typedef enum { DF2_WALK_VITERBI = 0, DF2_WALK_GREEDY = 1 } df2_walk;
 typedef enum {
     DF2_PLAN_SEGMENT_WGS = 0,   /* target count of top-K segment workgroups */
     DF2_PLAN_CHUNK_VECTORS = 1, /* 16-byte vectors per lane per chunk: 1, 2 or 4 */
-    DF2_PLAN_MERGE_WORDS = 2,   /* most candidate words one row merge takes (<= 1024) */
+    DF2_PLAN_MERGE_WORDS = 2,   /* most candidate words one row merge takes (<= 1024;
+                                   automatic: 768 in dflash2_select, 1024 in dflash2_topk) */
     DF2_PLAN_GATE_SLICES = 3,   /* slices of d of the gate projection (<= 16) */
     DF2_PLAN_CONV_SLICES = 4,   /* k slices of the convolution's correction GEMM */
     DF2_PLAN_LAUNCHES = 5,      /* dflash2_select: 1 = one fused launch, 2 = scan, then
