@@ -234,7 +234,16 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
     const bool cur_row = tid >= 64 && tid < 64 + ne * K;
     const int x = cur_row ? tid - 64 : 0, q = x / K, k = x % K;
     float hv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    if constexpr (!SUMH) {
+    // SUMH (one position, ne == 1): thread t takes the pair of H_t values
+    // 2t, 2t + 1 (r <= 512), all S partials of it loaded with the ids
+    uint64_t hpv[SUMH ? kMaxFusedSlices : 1];
+    const int hk = 2 * min(tid, r / 2 - 1);
+    if constexpr (SUMH) {
+        const uint64_t* hsrc = reinterpret_cast<const uint64_t*>(p.ppart + (rb + e0) * r + hk);
+        const int64_t hstride = p.rows * r / 2;         // one slice, in pairs
+#pragma unroll
+        for (int s = 0; s < kMaxFusedSlices; ++s) hpv[s] = xload(hsrc + (int64_t)min(s, p.S - 1) * hstride);
+    } else {
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             const int64_t grow = min(rb + e0 + qq, (int64_t)p.rows - 1);
@@ -265,7 +274,19 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
         sm.u[q][k] = uval;
     }
     if constexpr (SUMH) {
-        pair_sum_gate(p.ppart, p.S, p.rows, r, rb + e0, ne, sm);
+        // summed in slice order, as every other reader of the partials
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int s = 0; s < kMaxFusedSlices; ++s) {
+            if (s < p.S) {
+                lo += __uint_as_float((uint32_t)hpv[s]);
+                hi += __uint_as_float((uint32_t)(hpv[s] >> 32));
+            }
+        }
+        if (tid < r / 2) {
+            sm.H[0][hk] = lo;
+            sm.H[0][hk + 1] = hi;
+        }
     } else {
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
