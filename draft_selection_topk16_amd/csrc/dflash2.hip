@@ -534,6 +534,25 @@ __global__ __launch_bounds__(kWG, 5) void k_pairs_walk(Params p) {
     pairs_walk<BF16, SAMPLE, MB == 1>(p, (int64_t)blockIdx.x, sm, flag);
 }
 
+// The three-stage plan with the walks in a launch of their own (rows beyond
+// one resident wave of workgroups): the pair scores of the transition into
+// every row, then one workgroup per sequence walks.  A walk that fell to the
+// last pair job of its sequence landed on the slowest XCD, filled its CUs
+// and held back the dispatch of its remaining rows.
+template <bool BF16, int MB>
+__global__ __launch_bounds__(kWG, 5) void k_pairs(Params p) {
+    __shared__ SharedAll sm;
+    const int64_t row = blockIdx.x;
+    const float hz[2] = {0.f, 0.f};
+    pairs_fused<BF16, MB != 1>(p, (int)(row / p.P), (int)(row % p.P), 1, -1, hz, sm.pr);
+}
+
+template <bool SAMPLE>
+__global__ __launch_bounds__(kWG, 5) void k_walks(Params p) {
+    __shared__ SharedAll sm;
+    walk_of<SAMPLE>(p, (int)blockIdx.x, sm);
+}
+
 // Top-K alone: segments, then the row merge on last arrival.
 template <bool BF16, int NV>
 __global__ __launch_bounds__(kWG, 5) void k_topk(Params p) {
@@ -804,6 +823,7 @@ struct Plan {
     Params p;
     bool two = false;           // scan and tail as two launches
     bool three = false;         // two launches, the row merges in the first
+    bool walks = false;         // three-stage, the walks in a third launch
     int nv = 1;
     int mb = 4;                 // gate tile: 16*mb rows x 16*(mb == 1 ? 4 : 2) columns
     bool bf16 = true;
@@ -965,6 +985,13 @@ void launch_select(const Plan& pl, hipStream_t stream) {
             hipLaunchKernelGGL((k_scanm<BF, NV_, MB_>),                                        \
                                dim3((unsigned)(pl.p.n_gate + pl.n_chunk_blocks)), block, 0,    \
                                stream, pl.p);                                                  \
+            if (pl.walks) {                                                                    \
+                hipLaunchKernelGGL((k_pairs<BF, MB_>), dim3((unsigned)pl.p.rows), block, 0,    \
+                                   stream, pl.p);                                              \
+                hipLaunchKernelGGL((k_walks<SM>), dim3((unsigned)pl.p.B), block, 0, stream,    \
+                                   pl.p);                                                      \
+                break;                                                                         \
+            }                                                                                  \
             hipLaunchKernelGGL((k_pairs_walk<BF, MB_, SM>), dim3((unsigned)pl.p.rows), block, 0,    \
                                stream, pl.p);                                                  \
             break;                                                                             \
@@ -1099,9 +1126,10 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     // within what the gate leaves of one resident wave (batch 32, three
     // stages: 31.8 us with 3 segments per row, 33.0 with 2, 34.2 with 4).
     const int64_t cap = select_capacity();
-    const int mode = ov.launches ? ov.launches : 3;
+    const int mode = ov.launches ? ov.launches : (rows > cap ? 4 : 3);
     pl.two = mode >= 2;
-    pl.three = mode == 3;
+    pl.three = mode >= 3;
+    pl.walks = mode == 4;
     const int64_t cus = cu_count();
     const int64_t target = std::min<int64_t>(cap - pl.p.n_gate, pl.two ? 3 * cus : (5 * cus) / 2);
     plan_topk(pl, rows, dims->V, K, bf16, logits, std::max<int64_t>(rows, target), ov, kSelectMergeWords);
@@ -1510,7 +1538,7 @@ df2_status dflash2_plan_override(df2_plan_knob knob, int32_t value) {
         case DF2_PLAN_GATE_SLICES: g_over.gate_s = value; break;
         case DF2_PLAN_CONV_SLICES: g_over.conv_s = value; break;
         case DF2_PLAN_LAUNCHES:
-            if (value > 3) return fail(DF2_EINVAL, "launches must be 0, 1, 2 or 3");
+            if (value > 4) return fail(DF2_EINVAL, "launches must be 0 to 4");
             g_over.launches = value;
             break;
         case DF2_PLAN_LM_RANGES:

@@ -82,8 +82,10 @@ typedef enum {
     DF2_PLAN_GATE_SLICES = 3,   /* slices of d of the gate projection (<= 16) */
     DF2_PLAN_CONV_SLICES = 4,   /* k slices of the convolution's correction GEMM */
     DF2_PLAN_LAUNCHES = 5,      /* dflash2_select: 1 = one fused launch, 2 = scan, then
-                                   merges, pairs and walk, 3 (automatic) = scan with the
-                                   row merges, then pairs and walk */
+                                   merges, pairs and walk, 3 = scan with the row merges,
+                                   then pairs and walk, 4 = as 3 with the walks in a third
+                                   launch; automatic: 3, or 4 when the rows exceed one
+                                   resident wave of workgroups */
     DF2_PLAN_LM_RANGES = 6,     /* dflash2_lmhead_topk: vocabulary ranges (<= 256) */
     DF2_PLAN_GATE_GIVEUP = 7    /* failure-handling tests only: 1 = in dflash2_select
                                    under launches 1 or 2 (the plans whose row merges

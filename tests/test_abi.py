@@ -235,7 +235,7 @@ def test_plan_knobs_match_header_and_reject_bad_values(lib):
     assert declared == PLAN_KNOBS
     assert lib.dflash2_plan_override(max(PLAN_KNOBS.values()) + 1, 1) == DF2_EINVAL   # unknown knob
     assert lib.dflash2_plan_override(0, -1) == DF2_EINVAL                             # negative
-    assert lib.dflash2_plan_override(PLAN_KNOBS["launches"], 4) == DF2_EINVAL
+    assert lib.dflash2_plan_override(PLAN_KNOBS["launches"], 5) == DF2_EINVAL
     assert lib.dflash2_plan_override(PLAN_KNOBS["chunk_vectors"], 3) == DF2_EINVAL
     assert lib.dflash2_plan_override(PLAN_KNOBS["gate_giveup"], 2) == DF2_EINVAL
     for k in PLAN_KNOBS.values():

@@ -397,14 +397,15 @@ def test_select_edge_shapes(B, P, V, K, d, dtype):
 
 
 @pytest.mark.parametrize("r", [320, 512])
-@pytest.mark.parametrize("launches", [1, 2, 3])
+@pytest.mark.parametrize("launches", [1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_select_wide_gate(r, launches, dtype):
     """Gate ranks above one value per thread (r > 256, up to the 512 the
     library accepts): the row merge sums a second gate value per thread, the
     pair job loads a second one per position and takes 16 k steps, in the
-    fused launch and in both two-launch plans (in the three-stage one the
-    pair job takes H from the gate tile sums)."""
+    fused launch, in both two-launch plans (in the three-stage one the pair
+    job takes H from the gate tile sums) and with the walks in a third
+    launch."""
     say("select wide gate %s r=%d launches=%d" % (dtype, r, launches))
     wl = synth.Workload("wide", 1, B=3, P=5, V=3000, d=128, K=16, r=r, dtype=dtype, pair_scale=4.0)
     x = synth.make_inputs(wl, seed=r + 7)
@@ -428,12 +429,13 @@ def test_select_empty_batch():
 @pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1", "stress_b256"])
 def test_select_same_result_under_any_segment_plan(name):
     """The segment plan (segments per row, chunk width, words per merge) and
-    the choice of launches (one fused, scan then tail, or the three-stage
-    default) change neither the gate sums nor any comparison: candidate words
-    are exact, the merge is independent of how a row was cut, and every plan
-    sums H in slice order, so path and score are bit-identical across plans.
-    At the stress workload the scan grid and the 3840-row second launch are
-    each more than one resident wave."""
+    the choice of launches (one fused, scan then tail, the three-stage
+    default, or three stages with the walks in a third launch, the default
+    beyond one resident wave of rows) change neither the gate sums nor any
+    comparison: candidate words are exact, the merge is independent of how a
+    row was cut, and every plan sums H in slice order, so path and score are
+    bit-identical across plans.  At the stress workload the scan grid and the
+    3840-row pair launch are each more than one resident wave."""
     say("select under segment plans %s" % name)
     x = inputs(name)
     t = to_device(x)
@@ -444,11 +446,36 @@ def test_select_same_result_under_any_segment_plan(name):
                   {"chunk_vectors": 2, "segment_wgs": 300}, {"merge_words": 256},
                   {"launches": 1}, {"launches": 1, "segment_wgs": 300},
                   {"launches": 2}, {"launches": 2, "segment_wgs": 300},
-                  {"launches": 3, "segment_wgs": 300}, {"launches": 3, "merge_words": 256}):
+                  {"launches": 3}, {"launches": 3, "segment_wgs": 300}, {"launches": 3, "merge_words": 256},
+                  {"launches": 4}, {"launches": 4, "segment_wgs": 300}):
         with df2.plan(**knobs):
             p, s = df2.select(*args)
             torch.cuda.synchronize()
         assert torch.equal(p, ref[0]) and torch.equal(s, ref[1]), knobs
+
+
+@pytest.mark.parametrize("name", ["t27b_b8", "qwen3_4b_b1"])
+def test_select_walk_modes_same_in_every_plan(name):
+    """Every walk mode (max-sum, greedy, sampling) returns the same bits in
+    all four launch plans, including the one with the walks in a launch of
+    their own."""
+    say("select walk modes across launch plans %s" % name)
+    x = inputs(name)
+    t = to_device(x)
+    args = (t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], x.wl.K)
+    u = torch.from_numpy(np.random.default_rng(5).random((x.wl.B, x.wl.P), dtype=np.float32)).cuda()
+    runs = {"viterbi": lambda: df2.select(*args), "greedy": lambda: df2.select(*args, walk="greedy"),
+            "sample": lambda: df2.select_sample(*args, u=u)}
+    for wname, fn in runs.items():
+        ref = None
+        for launches in (1, 2, 3, 4):
+            with df2.plan(launches=launches):
+                out = [o.clone() for o in fn()]
+                torch.cuda.synchronize()
+            if ref is None:
+                ref = out
+            assert all(torch.equal(a, b) for a, b in zip(ref, out)), (wname, launches)
+    assert flags_clear()
 
 
 def test_select_deterministic_and_scratch_reuse():
