@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kWG, 5) void k_pairs_walk(Params p) {
 // last pair job of its sequence landed on the slowest XCD, filled its CUs
 // and held back the dispatch of its remaining rows.
 template <bool BF16, int MB>
-__global__ __launch_bounds__(kWG, 5) void k_pairs(Params p) {
+__global__ __launch_bounds__(kWG, 5) void k_pairs_rows(Params p) {
     __shared__ SharedAll sm;
     const int64_t row = blockIdx.x;
     const float hz[2] = {0.f, 0.f};
@@ -986,7 +986,7 @@ void launch_select(const Plan& pl, hipStream_t stream) {
                                dim3((unsigned)(pl.p.n_gate + pl.n_chunk_blocks)), block, 0,    \
                                stream, pl.p);                                                  \
             if (pl.walks) {                                                                    \
-                hipLaunchKernelGGL((k_pairs<BF, MB_>), dim3((unsigned)pl.p.rows), block, 0,    \
+                hipLaunchKernelGGL((k_pairs_rows<BF, MB_>), dim3((unsigned)pl.p.rows), block, 0, \
                                    stream, pl.p);                                              \
                 hipLaunchKernelGGL((k_walks<SM>), dim3((unsigned)pl.p.B), block, 0, stream,    \
                                    pl.p);                                                      \
