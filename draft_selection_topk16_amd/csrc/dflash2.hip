@@ -301,7 +301,7 @@ __device__ void pairs_fused(const Params& p, int b, int e0, int ne, int64_t own,
 
 // The walk of sequence b over its scored transitions, in the launch's walk
 // mode.  Every thread of the workgroup calls.
-template <bool SAMPLE>
+template <bool SAMPLE, bool PAIR32 = false>
 __device__ __forceinline__ void walk_of(const Params& p, int b, SharedAll& sm) {
     const int K = p.K, P = p.P;
     const int64_t rb = (int64_t)b * P;
@@ -313,7 +313,7 @@ __device__ __forceinline__ void walk_of(const Params& p, int b, SharedAll& sm) {
     else if (p.walk == kWalkGreedy)
         chain_seq<kChainGreedy>(Sq, ids, nullptr, 0.f, P, K, p.out_path + rb, nullptr, p.out_score + b, sm.wk);
     else
-        walk_seq(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
+        walk_seq<PAIR32>(Sq, ids, P, K, p.out_path + rb, p.out_score + b, sm.wk);
 }
 
 // Everything after a row's segments: the row merge (with the gate row H_t),
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(kWG, 5) void k_pairs_rows(Params p) {
 template <bool SAMPLE>
 __global__ __launch_bounds__(kWG, 5) void k_walks(Params p) {
     __shared__ SharedAll sm;
-    walk_of<SAMPLE>(p, (int)blockIdx.x, sm);
+    walk_of<SAMPLE, true>(p, (int)blockIdx.x, sm);
 }
 
 // Top-K alone: segments, then the row merge on last arrival.
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kWG) void k_walk(WalkArgs a) {
         chain_seq<kChainSample>(S, ids, a.u + rb, a.inv_tau, a.P, a.K, a.out_path + rb, a.out_q + rb,
                                 a.out_score + b, sm);
     else
-        walk_seq(S, ids, a.P, a.K, a.out_path + rb, a.out_score + b, sm);
+        walk_seq<true>(S, ids, a.P, a.K, a.out_path + rb, a.out_score + b, sm);
 }
 
 // Zeroes n words; clears the arrival counters of the no-allocation entry

@@ -37,7 +37,10 @@ struct WalkLds {
     uint8_t psi[kMaxP * kMaxK];     // Viterbi: [j][t], row j of kMaxP positions
     int32_t ids[kWalkIds];
     int32_t rank[kMaxP];
-    float qpick[kMaxP];             // sampling walk: probability of each choice
+    union {
+        float qpick[kMaxP];         // sampling walk: probability of each choice
+        float dq[kMaxK];            // Viterbi, 16 < K <= 32: delta of the last step
+    };
 };
 
 // The larger of two floats, as the plain instruction (fmaxf quiets each
@@ -172,10 +175,60 @@ __device__ float walk_steps_quad(int t0, int t1, int K, float dl, WalkLds& sm) {
     return dl;
 }
 
+// Wave 0, 16 < K <= 32: the same over a group with Kp = 32, two lanes per
+// candidate.  Lane 2 j + h takes predecessors 16 h .. 16 h + 15 of candidate
+// j: delta_{t-1} of those sixteen from sm.dq and the column piece S_t(16h ..
+// 16h + 15, j), four 16-byte LDS reads each, issued together (lane 2 j
+// writes delta_t(j) once the wave's reads of the step are issued, and LDS
+// keeps one wave's accesses in order); the pair combines its two partial
+// maxima by DPP.  Returns delta(j) in lane 2 j.
+__device__ float walk_steps_pair(int t0, int t1, int K, float dl, WalkLds& sm) {
+    const int lane = lane_id();
+    const int j = lane >> 1, h = lane & 1;
+    const bool jv = j < K;
+    const float* col = sm.ST + j * 32 + 16 * h;
+#pragma unroll 1
+    for (int t = t0; t < t1; ++t) {
+        const float* cp = col + (t - t0) * 1024;
+        if (t == 0) {
+            // delta_0(j) = S_0(prev, j): row 0 of the first block
+            dl = jv ? cp[0] : -INFINITY;
+            if (h == 0) sm.dq[j] = dl;
+            continue;
+        }
+        float v[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 sv = *reinterpret_cast<const float4*>(cp + 4 * g);
+            const float4 dv = *reinterpret_cast<const float4*>(sm.dq + 16 * h + 4 * g);
+            v[4 * g] = sv.x + dv.x;
+            v[4 * g + 1] = sv.y + dv.y;
+            v[4 * g + 2] = sv.z + dv.z;
+            v[4 * g + 3] = sv.w + dv.w;
+        }
+        float m;
+        int a;
+        best_of16(v, 16 * h, m, a);
+        const float mq = walk_max(m, __uint_as_float(quad_mov<kQuadSwap1>(__float_as_uint(m))));
+        uint32_t c = (m == mq) ? (uint32_t)a : 255u;
+        c = min(c, quad_mov<kQuadSwap1>(c));
+        dl = jv ? mq : -INFINITY;
+        if (h == 0) {
+            sm.dq[j] = dl;
+            // c < K for finite scores; the clamp keeps NaN inputs in bounds
+            if (jv) sm.psi[j * kMaxP + t] = (uint8_t)min((int)c, K - 1);
+        }
+    }
+    return dl;
+}
+
 // The walk of one sequence.  S: [P, K, K] scores (row i = predecessor rank,
 // column j = candidate rank; row 0 is used at t = 0), ids: [P, K] candidate
 // ids; both read with xload.  Writes out_path[0 .. P) and *out_score.
-// Every thread of the workgroup calls.
+// Every thread of the workgroup calls.  PAIR32: 16 < K <= 32 takes two lanes
+// per candidate (a kernel of its own can afford the registers; inlined
+// beside the pair job it spilled), else one.
+template <bool PAIR32 = false>
 __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int32_t* __restrict__ ids, int P,
                          int K, int32_t* __restrict__ out_path, float* __restrict__ out_score,
                          WalkLds& sm) {
@@ -211,7 +264,8 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
         __syncthreads();
         if (w == 0) {
             if (KP == 16) delta = walk_steps_quad(t0, t1, K, delta, sm);
-            else if (KP == 32) delta = walk_steps<32>(t0, t1, K, delta, sm);
+            else if (KP == 32) delta = PAIR32 ? walk_steps_pair(t0, t1, K, delta, sm)
+                                              : walk_steps<32>(t0, t1, K, delta, sm);
             else delta = walk_steps<64>(t0, t1, K, delta, sm);
         } else if (t0 == 0 && ids_lds) {
             // the other waves bring the candidate ids into LDS meanwhile, so
@@ -230,16 +284,26 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
     }
     if (w != 0) return;
     // final pick (smaller rank on ties): every lane reduces the broadcast
-    // deltas (candidate j in lane 4 j with K <= 16, else in lane j), then
-    // backtracks through psi
+    // deltas (candidate j in lane 4 j with K <= 16, 2 j with K <= 32, else
+    // in lane j), then backtracks through psi
     float m = -INFINITY;
     int jb = 0;
-    if (KP == 16) {
+    if (KP == 16 || (PAIR32 && KP == 32)) {
         // candidates j >= K already hold -inf
-        float v[16];
+        const int ls = KP == 16 ? 4 : 2;
+        for (int c = 0; c < KP; c += 16) {
+            float v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), 4 * u));
-        best_of16(v, 0, m, jb);
+            for (int u = 0; u < 16; ++u)
+                v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), (c + u) * ls));
+            float cb;
+            int ca;
+            best_of16(v, c, cb, ca);
+            if (c == 0 || cb > m) {
+                m = cb;
+                jb = ca;
+            }
+        }
     } else {
         for (int c = 0; c < K; c += 16) {
             float v[16];
