@@ -504,7 +504,7 @@ def main():
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selector runs per sequence with no "
-              "cross-GPU exchange, and this build has no multi-GPU path (--gpus %d refused)"
+              "cross-GPU exchange, and the library has no multi-GPU path (--gpus %d refused)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -98,7 +98,7 @@ typedef enum {
 typedef enum {
     DF2_OK = 0,
     DF2_EINVAL = 1,        /* bad pointer, size or combination of sizes */
-    DF2_EUNSUPPORTED = 2,  /* valid request outside what this build handles */
+    DF2_EUNSUPPORTED = 2,  /* valid request outside what the library handles */
     DF2_EHIP = 3,          /* HIP runtime or launch failure */
     DF2_ENOMEM = 4         /* scratch allocation failed */
 } df2_status;
