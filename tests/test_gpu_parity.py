@@ -364,20 +364,24 @@ def test_select_pair_dominant(name, kw):
     check_select(path, score, o, TOL[x.wl.dtype], name)
 
 
+@pytest.mark.parametrize("K,launches", [(16, 0), (16, 4), (24, 3), (24, 4), (32, 4), (5, 4)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_select_integer_exact(dtype):
+def test_select_integer_exact(dtype, K, launches):
     """Small-integer inputs keep every step exact on both sides (bf16 hi/lo
-    split included): paths and scores must match bit for bit."""
-    say("select integer-exact %s" % dtype)
-    rng = np.random.default_rng(7)
-    B, P, V, d, r, K = 6, 7, 3000, 64, 64, 16
+    split included): paths and scores must match bit for bit, also with the
+    walks in a launch of their own (K = 24 and 32 there walk two lanes per
+    candidate)."""
+    say("select integer-exact %s K=%d launches=%d" % (dtype, K, launches))
+    rng = np.random.default_rng(7 + K)
+    B, P, V, d, r = 6, 7, 3000, 64, 64
     wl = synth.Workload("int", 0, B=B, P=P, V=V, d=d, K=K, r=r, dtype=dtype)
     logits = rng.integers(-6, 7, size=(B, P, V)).astype(np.float32)
     x = synth.make_inputs(wl, seed=123, logits_override=logits)
     for k, shape in (("hidden", (B, P, d)), ("A", (V, r)), ("Bt", (V, r)), ("W", (r, d))):
         v = rng.integers(-2, 3, size=shape).astype(np.float32)
         setattr(x, k, synth.f32_to_bf16_bits(v) if dtype == "bf16" else v)
-    path, score = gpu_select(x)
+    with df2.plan(launches=launches):
+        path, score = gpu_select(x)
     o = run_oracle(x)
     assert np.array_equal(path, o["path"])
     assert np.array_equal(score.astype(np.float64), o["score"])
