@@ -222,6 +222,69 @@ __device__ float walk_steps_pair(int t0, int t1, int K, float dl, WalkLds& sm) {
     return dl;
 }
 
+// Wave 0, after the steps: the final pick (smaller rank on ties) over the
+// deltas -- candidate j in lane ls * j (ls = 4 or 2: candidates j >= K hold
+// -inf already), or ls = 0: in lane j, candidates j >= K skipped -- then
+// the backtrack through psi and the outputs.  ids_lds: the candidate ids
+// are in sm.ids, else they are read from ids.
+__device__ __forceinline__ void walk_finish(float delta, int ls, int P, int K, bool ids_lds,
+                                            const int32_t* __restrict__ ids,
+                                            int32_t* __restrict__ out_path,
+                                            float* __restrict__ out_score, WalkLds& sm) {
+    const int lane = lane_id();
+    float m = -INFINITY;
+    int jb = 0;
+    if (ls > 0) {
+        for (int c = 0; c < 64 / ls; c += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), (c + u) * ls));
+            float cb;
+            int ca;
+            best_of16(v, c, cb, ca);
+            if (c == 0 || cb > m) {
+                m = cb;
+                jb = ca;
+            }
+        }
+    } else {
+        for (int c = 0; c < K; c += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = (c + u < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), min(c + u, 63)))
+                                   : -INFINITY;
+            float cb;
+            int ca;
+            best_of16(v, c, cb, ca);
+            if (c == 0 || cb > m) {
+                m = cb;
+                jb = ca;
+            }
+        }
+    }
+    // backtrack (jj is uniform): lane j holds psi_t(j) of sixteen positions
+    // (one 16-byte read of its row), each step is one readlane, and lane t
+    // keeps the rank chosen at position t (P <= 64)
+    int jj = __builtin_amdgcn_readfirstlane(min(jb, K - 1));
+    int rk = 0;
+    for (int g = (P - 1) & ~15; g >= 0; g -= 16) {
+        const uint4 pw = *reinterpret_cast<const uint4*>(sm.psi + lane * kMaxP + g);
+#pragma unroll
+        for (int u = 15; u >= 0; --u) {
+            const int t = g + u;
+            if (t > P - 1 || t < 1) continue;
+            rk = (lane == t) ? jj : rk;
+            const uint32_t wd = u < 4 ? pw.x : (u < 8 ? pw.y : (u < 12 ? pw.z : pw.w));
+            jj = (int)((__builtin_amdgcn_readlane(wd, jj) >> (8 * (u & 3))) & 0xffu);
+        }
+    }
+    rk = (lane == 0) ? jj : rk;
+    if (lane == 0) *out_score = m;
+    if (lane < P) out_path[lane] = ids_lds ? sm.ids[lane * K + rk] : xload(ids + (int64_t)lane * K + rk);
+}
+
 // The walk of one sequence.  S: [P, K, K] scores (row i = predecessor rank,
 // column j = candidate rank; row 0 is used at t = 0), ids: [P, K] candidate
 // ids; both read with xload.  Writes out_path[0 .. P) and *out_score.
@@ -283,62 +346,8 @@ __device__ __forceinline__ void walk_seq(const float* __restrict__ S, const int3
         __syncthreads();
     }
     if (w != 0) return;
-    // final pick (smaller rank on ties): every lane reduces the broadcast
-    // deltas (candidate j in lane 4 j with K <= 16, 2 j with K <= 32, else
-    // in lane j), then backtracks through psi
-    float m = -INFINITY;
-    int jb = 0;
-    if (KP == 16 || (PAIR32 && KP == 32)) {
-        // candidates j >= K already hold -inf
-        const int ls = KP == 16 ? 4 : 2;
-        for (int c = 0; c < KP; c += 16) {
-            float v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), (c + u) * ls));
-            float cb;
-            int ca;
-            best_of16(v, c, cb, ca);
-            if (c == 0 || cb > m) {
-                m = cb;
-                jb = ca;
-            }
-        }
-    } else {
-        for (int c = 0; c < K; c += 16) {
-            float v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = (c + u < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(delta), min(c + u, 63)))
-                                   : -INFINITY;
-            float cb;
-            int ca;
-            best_of16(v, c, cb, ca);
-            if (c == 0 || cb > m) {
-                m = cb;
-                jb = ca;
-            }
-        }
-    }
-    // backtrack (jj is uniform): lane j holds psi_t(j) of sixteen positions
-    // (one 16-byte read of its row), each step is one readlane, and lane t
-    // keeps the rank chosen at position t (P <= 64)
-    int jj = __builtin_amdgcn_readfirstlane(min(jb, K - 1));
-    int rk = 0;
-    for (int g = (P - 1) & ~15; g >= 0; g -= 16) {
-        const uint4 pw = *reinterpret_cast<const uint4*>(sm.psi + lane * kMaxP + g);
-#pragma unroll
-        for (int u = 15; u >= 0; --u) {
-            const int t = g + u;
-            if (t > P - 1 || t < 1) continue;
-            rk = (lane == t) ? jj : rk;
-            const uint32_t wd = u < 4 ? pw.x : (u < 8 ? pw.y : (u < 12 ? pw.z : pw.w));
-            jj = (int)((__builtin_amdgcn_readlane(wd, jj) >> (8 * (u & 3))) & 0xffu);
-        }
-    }
-    rk = (lane == 0) ? jj : rk;
-    if (lane == 0) *out_score = m;
-    if (lane < P) out_path[lane] = ids_lds ? sm.ids[lane * K + rk] : xload(ids + (int64_t)lane * K + rk);
+    walk_finish(delta, KP == 16 ? 4 : ((PAIR32 && KP == 32) ? 2 : 0), P, K, ids_lds, ids, out_path,
+                out_score, sm);
 }
 
 // Walks whose choice at t depends only on the row of the token chosen at

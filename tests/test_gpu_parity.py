@@ -364,16 +364,18 @@ def test_select_pair_dominant(name, kw):
     check_select(path, score, o, TOL[x.wl.dtype], name)
 
 
-@pytest.mark.parametrize("K,launches", [(16, 0), (16, 4), (24, 3), (24, 4), (32, 4), (5, 4)])
+@pytest.mark.parametrize("K,launches,B", [(16, 0, 6), (16, 4, 6), (24, 3, 6), (24, 4, 6), (32, 4, 6),
+                                          (5, 4, 6), (16, 0, 2), (13, 0, 1), (5, 0, 2), (16, 3, 2)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_select_integer_exact(dtype, K, launches):
+def test_select_integer_exact(dtype, K, launches, B):
     """Small-integer inputs keep every step exact on both sides (bf16 hi/lo
     split included): paths and scores must match bit for bit, also with the
     walks in a launch of their own (K = 24 and 32 there walk two lanes per
-    candidate)."""
-    say("select integer-exact %s K=%d launches=%d" % (dtype, K, launches))
-    rng = np.random.default_rng(7 + K)
-    B, P, V, d, r = 6, 7, 3000, 64, 64
+    candidate) and with a gate of one m-block (B <= 2: H from the tile
+    sums)."""
+    say("select integer-exact %s K=%d launches=%d B=%d" % (dtype, K, launches, B))
+    rng = np.random.default_rng(7 + K + 100 * B)
+    P, V, d, r = 7, 3000, 64, 64
     wl = synth.Workload("int", 0, B=B, P=P, V=V, d=d, K=K, r=r, dtype=dtype)
     logits = rng.integers(-6, 7, size=(B, P, V)).astype(np.float32)
     x = synth.make_inputs(wl, seed=123, logits_override=logits)
@@ -472,7 +474,7 @@ def test_select_walk_modes_same_in_every_plan(name):
             "sample": lambda: df2.select_sample(*args, u=u)}
     for wname, fn in runs.items():
         ref = None
-        for launches in (1, 2, 3, 4):
+        for launches in (0, 1, 2, 3, 4):
             with df2.plan(launches=launches):
                 out = [o.clone() for o in fn()]
                 torch.cuda.synchronize()
