@@ -56,3 +56,23 @@ def test_noalloc_matches_select(order):
             assert torch.equal(p, ref_p), (name, rep)
             assert torch.equal(s, ref_s), (name, rep)
     assert df2.device_error() == 0
+
+
+@pytest.mark.parametrize("launches", [1, 2, 4])
+def test_noalloc_matches_select_in_every_plan(launches):
+    """The other launch plans (forced through the plan knob, which both entry
+    points read) on the static scratch: one fused launch, scan then tail, and
+    the walks in a launch of their own (the automatic plan beyond one
+    resident wave of rows), a larger call then a smaller one."""
+    with df2.plan(launches=launches):
+        for name in ("t27b_b8", "tiny_small"):
+            wl = synth.WORKLOADS["tiny_f32"].with_(V=5000) if name == "tiny_small" else synth.WORKLOADS[name]
+            say("select_noalloc %s launches=%d" % (name, launches))
+            t = to_device(synth.make_inputs(wl))
+            ref_p, ref_s = df2.select(t["logits"], t["hidden"], t["A"], t["Bt"], t["W"], t["prev"], wl.K)
+            ref_p, ref_s = ref_p.clone(), ref_s.clone()
+            p, s = select_noalloc(t, wl.K)
+            torch.cuda.synchronize()
+            assert torch.equal(p, ref_p), (name, launches)
+            assert torch.equal(s, ref_s), (name, launches)
+    assert df2.device_error() == 0
