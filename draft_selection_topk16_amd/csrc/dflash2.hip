@@ -7,8 +7,10 @@
 // the scores once from the last verified token.
 //
 // dflash2_select runs in two launches by default, k_scanm and then
-// k_pairs_walk (three stages: scan with the row merges, pairs, walk); the
-// plan can also run it as k_scan then k_tail, or as the single k_select.
+// k_pairs_walk (three stages: scan with the row merges, pairs, walk), and
+// in three beyond one resident wave of rows (k_scanm, k_pairs_rows, then
+// k_walks); the plan can also run it as k_scan then k_tail, or as the single
+// k_select.
 // Workgroups are dealt out in index order, and each one's job follows from
 // its index:
 //   * the first n_gate compute one slice of one gate tile (a partial of H);
@@ -776,7 +778,8 @@ struct Overrides {
     int gate_s = 0;       // gate slices of d (1..16)
     int conv_s = 0;       // k slices of the convolution's correction GEMM
     int launches = 0;     // dflash2_select: 1 = one fused launch, 2 = scan then tail,
-                          // 3 = scan with the row merges, then pairs and walk
+                          // 3 = scan with the row merges, then pairs and walk,
+                          // 4 = as 3 with the walks in a third launch
     int lm_ranges = 0;    // vocabulary ranges of the LM head (1..256)
     int gate_giveup = 0;  // 1: the row merges' gate wait gives up (failure-handling tests)
 };
@@ -1125,8 +1128,11 @@ df2_status select_common(const df2_dims* dims, const void* logits, const void* h
     // slowest slices went from 16 to 27 us).  Measured at V = 151936 (bf16,
     // us per call, three stages / scan then tail / fused): batch 1 (d = 2560)
     // 18.2 / 19.6 / 20.8, batch 8 (d = 5120) 22.3 / 23.4 / 26.4, batch 32
-    // 31.9 / 33.8 / 37.0; B = 256, P = 15, V = 262144: 481 / 527 / 488.  The
-    // launches plan knob forces any of the three.  Segment workgroups: about
+    // 31.9 / 33.8 / 37.0; B = 256, P = 15, V = 262144: 481 / 527 / 488 (as
+    // first measured).  Beyond one resident wave of rows the walks move to a
+    // third launch: left to the last pair job of each sequence they gathered
+    // on the slowest XCD and held back its dispatch (B = 256, P = 15: 484 ->
+    // 421 us).  The launches plan knob forces any plan.  Segment workgroups: about
     // three per CU for the two-launch plans, two and a half for the fused one,
     // within what the gate leaves of one resident wave (batch 32, three
     // stages: 31.8 us with 3 segments per row, 33.0 with 2, 34.2 with 4).
