@@ -11,11 +11,13 @@ literal greedy walk and the sampling walk are further modes, and H(h_t) is
 read as a bias-free linear map d -> r (see the header of oracle.c).  conv2 is
 the drafter's two-tap dynamic convolution ("A Lightweight Local
 Convolution"); lmhead_topk is the drafter's LM head followed by top-K, the
-logits the selector starts from.
+logits the selector starts from; philox_uniforms are the counter-based
+uniforms a sampling walk consumes (Philox4x64-10, Salmon et al., SC 2011).
 
 Every function here is pinned by CPU tests against something other than
 itself (brute-force enumeration, closed forms, exact integer cases, an
-independent sort); none is "parity unpinned".
+independent sort, numpy's own Philox and its published known answer); none
+is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -65,6 +67,10 @@ def _load():
         lib.orc_sample.restype = ctypes.c_int
         lib.orc_conv2.argtypes = [P, P, P, P, I, I, I, P, P]
         lib.orc_conv2.restype = None
+        lib.orc_philox4x64_10.argtypes = [P, P, P]
+        lib.orc_philox4x64_10.restype = None
+        lib.orc_philox_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I, I, P]
+        lib.orc_philox_uniforms.restype = None
         lib.orc_second_best.argtypes = [P, P, I, I, I, P]
         lib.orc_second_best.restype = ctypes.c_int
         lib.orc_lmhead_topk.argtypes = [P, P, I, I, I, ctypes.c_int32, P, P, P]
@@ -231,6 +237,27 @@ def conv2(x, x_prev, base, Wc):
     sig = np.empty_like(x)
     _load().orc_conv2(_p(x), _p(x_prev), _p(base), _p(Wc), Bn, P, d, _p(y), _p(sig))
     return y, sig
+
+
+def philox4x64_10(ctr, key) -> np.ndarray:
+    """One Philox4x64-10 block (see orc_philox4x64_10): 4 counter words and
+    2 key words in, 4 words out, all uint64."""
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint64).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64).reshape(2))
+    out = np.zeros(4, dtype=np.uint64)
+    _load().orc_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def philox_uniforms(seed: int, offset: int, n: int, first: int = 0) -> np.ndarray:
+    """Uniforms first .. first+n-1 of the call (seed, offset) as float32 (see
+    orc_philox_uniforms: word i mod 4 of the block at counter
+    (i // 4, offset, 0, 0) under key (seed, 0), mapped to (x >> 40) * 2^-24)."""
+    u = np.zeros(max(int(n), 0), dtype=np.float32)
+    if n > 0:
+        _load().orc_philox_uniforms(int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                    int(first), int(n), _p(u))
+    return u
 
 
 def path_sigma(sig, path_rank) -> np.ndarray:

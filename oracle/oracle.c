@@ -35,14 +35,16 @@
  *
  * The drafter's two-tap convolution (orc_conv2, section "A Lightweight Local
  * Convolution") and its LM head followed by top-K (orc_lmhead_topk, the
- * logits the selector starts from) are here too; their readings are stated
- * beside them.
+ * logits the selector starts from) are here too, and so is the counter-based
+ * generator of the sampling walk's uniforms (orc_philox_uniforms,
+ * Philox4x64-10); their readings are stated beside them.
  *
  * Parity pins (checked by the CPU test suite, not by this file): brute-force
  * enumeration of all K^P paths on tiny inputs, zeroed pair term reducing to
  * independent top-1 picks, K = 1 and P = 1 closed forms, exact integer
- * fixtures, logit-shift invariance, and an independent lexicographic sort for
- * top-K.
+ * fixtures, logit-shift invariance, an independent lexicographic sort for
+ * top-K, and numpy's Philox plus the published known answer for the
+ * generator.
  */
 #include <math.h>
 #include <stdint.h>
@@ -465,4 +467,57 @@ void orc_conv2(const double* x, const double* x_prev, const double* base, const 
                 }
             }
         }
+}
+
+/*
+ * Counter-based uniforms for the sampling walk (the selector's section:
+ * sampling draws from the same scores, so each draft position needs one
+ * uniform).  The generator is Philox4x64-10 as published by Salmon, Moraes,
+ * Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011):
+ * a 4-word counter and a 2-word key; each of 10 rounds multiplies counter
+ * words 0 and 2 by the two round multipliers, crosses the high and low
+ * halves of the products with words 3 and 1 and the key, then bumps the key
+ * by the two Weyl constants.
+ *
+ * Reading of how a draw maps onto the generator (the pages name none):
+ * uniform i of a call with (seed, offset) is word (i mod 4) of the block at
+ * counter (floor(i / 4), offset, 0, 0) under key (seed, 0), and the word x
+ * becomes the float (x >> 40) * 2^-24, exact in fp32 and in [0, 1).
+ */
+static const uint64_t orc_philox_m0 = 0xD2E7470EE14C6C93ull;
+static const uint64_t orc_philox_m1 = 0xCA5A826395121157ull;
+static const uint64_t orc_philox_w0 = 0x9E3779B97F4A7C15ull;  /* golden ratio */
+static const uint64_t orc_philox_w1 = 0xBB67AE8584CAA73Bull;  /* sqrt(3) - 1 */
+
+void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]) {
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        const unsigned __int128 p0 = (unsigned __int128)orc_philox_m0 * c0;
+        const unsigned __int128 p1 = (unsigned __int128)orc_philox_m1 * c2;
+        const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += orc_philox_w0;
+        k1 += orc_philox_w1;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* Uniforms first .. first + n - 1 of the call (seed, offset), as above. */
+void orc_philox_uniforms(uint64_t seed, uint64_t offset, int64_t first, int64_t n, float* u) {
+    const uint64_t key[2] = {seed, 0};
+    for (int64_t k = 0; k < n; ++k) {
+        const uint64_t i = (uint64_t)(first + k);
+        const uint64_t ctr[4] = {i / 4, offset, 0, 0};
+        uint64_t w[4];
+        orc_philox4x64_10(ctr, key, w);
+        u[k] = (float)((double)(w[i % 4] >> 40) * (1.0 / 16777216.0));
+    }
 }
