@@ -21,7 +21,9 @@ Prints ONE JSON line:
               walk, and how often the two walks' paths differ (on the timed
               workload and on its pair-dominant variant);
   sample      the same workloads with the sampling walk (temperature 1,
-              seeded uniforms resident on the device);
+              seeded uniforms resident on the device); beside it the device
+              generator of those uniforms (dflash2_philox_uniforms) alone, at
+              B*P uniforms per call and in bulk;
   conv        the drafter's two-tap dynamic convolution (dflash2_conv2) at
               the two drafter shapes: µs per call (HIP events) and % of HBM
               peak for its algorithmic bytes, input copies rotated;
@@ -406,6 +408,27 @@ def time_project(wl, steps: int, warmup: int, rotate_mb: float):
             "algorithmic_bytes": ab, "hbm_frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def time_philox(n: int, steps: int, warmup: int):
+    """dflash2_philox_uniforms alone: n uniforms per call, the offset advanced
+    every call as a serving loop does; HIP events around each call on the
+    launch stream.  Reports µs per call and the GB/s of uniforms written."""
+    import torch
+    import draft_selection_topk16_amd as df2
+    out = torch.empty((n,), dtype=torch.float32, device="cuda")
+    for i in range(warmup):
+        df2.philox_uniforms(0xD1F1A5, i, n, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        df2.philox_uniforms(0xD1F1A5, warmup + i, n, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = statistics.fmean(a.elapsed_time(b) for a, b in ev) * 1e3
+    return {"n": n, "us_per_call": us, "write_gb_per_s": 4.0 * n / (us * 1e-6) / 1e9}
+
+
 def lmhead_algorithmic_bytes(M: int, V: int, d: int, K: int) -> int:
     """Bytes the fused LM head must move: the weight once, the hidden states,
     and the candidate outputs (index and value)."""
@@ -579,6 +602,11 @@ def main():
                          "kernel_us_avg": sm["kernel_ms_avg"] * 1e3,
                          "positions_per_s": wl.B * wl.P / (sm["ms_per_step"] * 1e-3),
                          "timing": sm}
+        log("timing the device uniforms (Philox4x64-10)")
+        out["sample"]["philox_uniforms"] = {
+            "generator": "Philox4x64-10, one block per four uniforms (dflash2_philox_uniforms)",
+            "per_cycle": time_philox(wl.B * wl.P, 200, 20),
+            "bulk": time_philox(1 << 26, 20, 3)}
     r1 = None
     if not args.no_b1:
         wl1 = synth.WORKLOADS[args.b1_workload]

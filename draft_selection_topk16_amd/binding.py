@@ -29,7 +29,8 @@ EXPORTED = (
     "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_select_noalloc",
     "dflash2_topk", "dflash2_lmhead_topk",
     "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
-    "dflash2_sample_walk", "dflash2_conv2", "dflash2_device_error", "dflash2_plan_override",
+    "dflash2_sample_walk", "dflash2_philox_uniforms", "dflash2_conv2", "dflash2_device_error",
+    "dflash2_plan_override",
     "dflash2_release",
     "dflash2_status_string",
     "dflash2_last_error", "dflash2_version",
@@ -78,6 +79,7 @@ def load() -> ctypes.CDLL:
         "dflash2_walk": [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp],
         "dflash2_sample_walk": [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp],
         "dflash2_conv2": [vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp],
+        "dflash2_philox_uniforms": [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, vp, vp],
         "dflash2_device_error": [vp, u32p],
         "dflash2_plan_override": [ctypes.c_int, i32],
         "dflash2_release": [],
@@ -311,6 +313,21 @@ def sample_walk(S: torch.Tensor, cand: torch.Tensor, u: torch.Tensor,
                                    float(temperature), _dev(path, "path"), _dev(q, "q"),
                                    _dev(score, "score"), _stream(S.device)))
     return path, q, score
+
+
+def philox_uniforms(seed: int, offset: int, n: int, device=None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """n uniforms in [0, 1) from the device's Philox4x64-10 stream (seed, offset),
+    as a float32 tensor on `device` (default: the current CUDA device)."""
+    lib = load()
+    if out is None:
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        out = torch.empty((max(int(n), 0),), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or out.numel() < n or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of at least n elements")
+    _check(lib.dflash2_philox_uniforms(int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), int(n),
+                                       _dev(out, "out") if n > 0 else 0, _stream(out.device)))
+    return out
 
 
 def conv2(x: torch.Tensor, x_prev: torch.Tensor, base: torch.Tensor, W_c: torch.Tensor,

@@ -1386,6 +1386,10 @@ df2_status walk_common(const float* S, const int32_t* cand_idx, int32_t B, int32
 
 }  // namespace
 
+// The sampling walk's uniforms: a kernel family of its own (philox.hpp),
+// launched only by dflash2_philox_uniforms below.
+#include "philox.hpp"
+
 extern "C" {
 
 df2_status dflash2_walk(const float* S, const int32_t* cand_idx, int32_t B, int32_t P, int32_t K,
@@ -1411,6 +1415,26 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx, const fl
     }
     return walk_common(S, cand_idx, B, P, K, kWalkSample, u, inv_tau, out_path, out_q, out_score,
                        stream);
+}
+
+df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, float* out,
+                                   hipStream_t stream) {
+    g_last_error.clear();
+    if (n < 0) return fail(DF2_EINVAL, "n < 0");
+    if (n > ((int64_t)1 << 31)) return fail(DF2_EUNSUPPORTED, "n above 2^31");
+    if (n == 0) return DF2_OK;
+    if (!out) return fail(DF2_EINVAL, "NULL pointer argument");
+    if ((uintptr_t)out & 3u) return fail(DF2_EINVAL, "out must be 4-byte aligned");
+    // one thread per Philox block of four uniforms: at most 2^29 threads
+    const int64_t blocks = (n + 3) / 4;
+    const unsigned grid = (unsigned)((blocks + kPhiloxWG - 1) / kPhiloxWG);
+    const int vec = aligned16(out) ? 1 : 0;
+    return launch_checked(
+        [&] {
+            hipLaunchKernelGGL(k_philox_uniforms, dim3(grid), dim3(kPhiloxWG), 0, stream, seed,
+                               offset, n, out, vec);
+        },
+        "philox uniforms launch");
 }
 
 df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,

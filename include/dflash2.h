@@ -14,7 +14,8 @@
  * token.  This library reads H as a bias-free linear map d -> r,
  * H_t = W_H h_t, and the walk as a max-sum (Viterbi) pass with backtrack;
  * the section's literal greedy walk is available as a second walk mode, and
- * its sampling walk through dflash2_select_sample / dflash2_sample_walk.
+ * its sampling walk through dflash2_select_sample / dflash2_sample_walk,
+ * whose uniforms dflash2_philox_uniforms can draw on the device.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -314,6 +315,25 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx,
                                float temperature, int32_t* out_path,
                                float* out_q, float* out_score,
                                hipStream_t stream);
+
+/*
+ * Uniforms for the sampling walk, drawn on the device from a counter-based
+ * generator (same section: sampling draws from the same scores, one uniform
+ * per draft position), so a serving loop need not bring them from the host.
+ * The generator is Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+ * Random Numbers: As Easy as 1, 2, 3", SC 2011):
+ *     out[i] = (x >> 40) * 2^-24,  x = word (i mod 4) of
+ *              Philox4x64-10(counter = (i / 4, offset, 0, 0), key = (seed, 0))
+ * exact in fp32 and in [0, 1); the values depend on (seed, offset, i) only.
+ * Advance `offset` once per draft-verify cycle and pass the [B, P] result
+ * as dflash2_select_sample's u (same stream).
+ *   n    number of uniforms, 0 <= n <= 2^31 (n == 0 enqueues nothing;
+ *        n < 0 is DF2_EINVAL, n > 2^31 DF2_EUNSUPPORTED)
+ *   out  [n] float, device memory owned by the caller, 4-byte aligned
+ *        (16-byte alignment lets whole blocks go out in one store)
+ */
+df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n,
+                                   float* out, hipStream_t stream);
 
 /*
  * Two-tap dynamic depthwise convolution of the block drafter ("DFlash 2:

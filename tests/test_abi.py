@@ -101,6 +101,18 @@ def test_empty_batch_is_a_noop(lib):
     assert lib.dflash2_walk(FAKE, FAKE, 0, 3, 4, 1, FAKE, FAKE, None) == DF2_OK
     assert lib.dflash2_select_walk(ctypes.byref(Dims(0, 7, 32000, 1024, 256, 1)), FAKE, FAKE,
                                    FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, FAKE, None) == DF2_OK
+    assert lib.dflash2_philox_uniforms(1, 2, 0, None, None) == DF2_OK
+
+
+def test_philox_uniforms_rejects_bad_arguments(lib):
+    # every check runs on the host before a launch (no GPU needed)
+    assert lib.dflash2_philox_uniforms(1, 2, -1, FAKE, None) == DF2_EINVAL
+    assert b"n < 0" in lib.dflash2_last_error()
+    assert lib.dflash2_philox_uniforms(1, 2, 2**31 + 1, FAKE, None) == DF2_EUNSUPPORTED
+    assert lib.dflash2_philox_uniforms(1, 2, 16, None, None) == DF2_EINVAL
+    assert b"NULL" in lib.dflash2_last_error()
+    assert lib.dflash2_philox_uniforms(1, 2, 16, FAKE + 2, None) == DF2_EINVAL
+    assert b"aligned" in lib.dflash2_last_error()
 
 
 def test_stage_entry_points_reject_bad_arguments(lib):
