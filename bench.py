@@ -520,7 +520,7 @@ def main():
     ap.add_argument("--no-project", action="store_true")
     ap.add_argument("--no-lmhead", action="store_true")
     ap.add_argument("--lmhead-steps", type=int, default=20)
-    ap.add_argument("--only", choices=["project", "lmhead"], default=None,
+    ap.add_argument("--only", choices=["project", "lmhead", "philox"], default=None,
                     help="time one stage alone (for counter runs) and print its JSON object")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
     args = ap.parse_args()
@@ -547,6 +547,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if args.only == "project":
         print(json.dumps(time_project(wl, args.steps, args.warmup, args.rotate_mb)), flush=True)
+        return
+    if args.only == "philox":
+        print(json.dumps(time_philox(wl.B * wl.P, args.steps, args.warmup)), flush=True)
         return
     if args.only == "lmhead":
         print(json.dumps(time_lmhead(wl.name, args.steps, args.warmup, cpu_rows=1)), flush=True)
