@@ -326,7 +326,9 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx,
  *              Philox4x64-10(counter = (i / 4, offset, 0, 0), key = (seed, 0))
  * exact in fp32 and in [0, 1); the values depend on (seed, offset, i) only.
  * Advance `offset` once per draft-verify cycle and pass the [B, P] result
- * as dflash2_select_sample's u (same stream).
+ * as dflash2_select_sample's u (same stream).  seed and offset are kernel
+ * arguments: a call captured into a HIP graph replays the same uniforms
+ * every time unless the caller updates the captured node's arguments.
  *   n    number of uniforms, 0 <= n <= 2^31 (n == 0 enqueues nothing;
  *        n < 0 is DF2_EINVAL, n > 2^31 DF2_EUNSUPPORTED)
  *   out  [n] float, device memory owned by the caller, 4-byte aligned
