@@ -6,11 +6,11 @@ inputs.  Importing the package does not load the library: the first call
 does, and raises if it has not been built.
 """
 from .binding import (PreparedSelect, SelectorError, conv2, device_error, lmhead_topk, load,
-                      pair_scores, philox_uniforms, plan,
+                      pair_scores, philox_uniforms, philox_uniforms_next, plan,
                       plan_override, project, release, sample_walk, select, select_sample, topk, version,
                       viterbi, walk)
 
 __all__ = ["PreparedSelect", "SelectorError", "conv2", "device_error", "lmhead_topk", "load",
-           "pair_scores", "philox_uniforms", "plan",
+           "pair_scores", "philox_uniforms", "philox_uniforms_next", "plan",
            "plan_override", "project", "release", "sample_walk", "select", "select_sample", "topk", "version",
            "viterbi", "walk"]

@@ -29,7 +29,8 @@ EXPORTED = (
     "dflash2_select", "dflash2_select_walk", "dflash2_select_sample", "dflash2_select_noalloc",
     "dflash2_topk", "dflash2_lmhead_topk",
     "dflash2_project", "dflash2_pair_scores", "dflash2_viterbi", "dflash2_walk",
-    "dflash2_sample_walk", "dflash2_philox_uniforms", "dflash2_conv2", "dflash2_device_error",
+    "dflash2_sample_walk", "dflash2_philox_uniforms", "dflash2_philox_uniforms_next",
+    "dflash2_conv2", "dflash2_device_error",
     "dflash2_plan_override",
     "dflash2_release",
     "dflash2_status_string",
@@ -80,6 +81,7 @@ def load() -> ctypes.CDLL:
         "dflash2_sample_walk": [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp],
         "dflash2_conv2": [vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp],
         "dflash2_philox_uniforms": [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, vp, vp],
+        "dflash2_philox_uniforms_next": [ctypes.c_uint64, vp, ctypes.c_int64, vp, vp],
         "dflash2_device_error": [vp, u32p],
         "dflash2_plan_override": [ctypes.c_int, i32],
         "dflash2_release": [],
@@ -327,6 +329,21 @@ def philox_uniforms(seed: int, offset: int, n: int, device=None,
         raise ValueError("out must be a contiguous float32 tensor of at least n elements")
     _check(lib.dflash2_philox_uniforms(int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), int(n),
                                        _dev(out, "out") if n > 0 else 0, _stream(out.device)))
+    return out
+
+
+def philox_uniforms_next(seed: int, offset: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """out.numel() uniforms of the stream (seed, offset[0]) into `out`, then
+    offset[0] += 1 on the device (offset: int64 tensor of one element on the
+    GPU, read as uint64); safe to capture in a CUDA/HIP graph."""
+    lib = load()
+    if offset.dtype != torch.int64 or offset.numel() != 1:
+        raise ValueError("offset must be an int64 tensor of one element")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    n = out.numel()
+    _check(lib.dflash2_philox_uniforms_next(int(seed) & (2**64 - 1), _dev(offset, "offset"), n,
+                                            _dev(out, "out"), _stream(out.device)))
     return out
 
 

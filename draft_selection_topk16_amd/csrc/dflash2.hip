@@ -1417,9 +1417,10 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx, const fl
                        stream);
 }
 
-df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, float* out,
-                                   hipStream_t stream) {
-    g_last_error.clear();
+namespace {
+
+// Checks shared by both uniforms entry points; *grid receives the launch width.
+df2_status philox_args(int64_t n, const float* out, unsigned* grid) {
     if (n < 0) return fail(DF2_EINVAL, "n < 0");
     if (n > ((int64_t)1 << 31)) return fail(DF2_EUNSUPPORTED, "n above 2^31");
     if (n == 0) return DF2_OK;
@@ -1427,14 +1428,46 @@ df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, fl
     if ((uintptr_t)out & 3u) return fail(DF2_EINVAL, "out must be 4-byte aligned");
     // one thread per Philox block of four uniforms: at most 2^29 threads
     const int64_t blocks = (n + 3) / 4;
-    const unsigned grid = (unsigned)((blocks + kPhiloxWG - 1) / kPhiloxWG);
+    *grid = (unsigned)((blocks + kPhiloxWG - 1) / kPhiloxWG);
+    return DF2_OK;
+}
+
+}  // namespace
+
+df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, float* out,
+                                   hipStream_t stream) {
+    g_last_error.clear();
+    unsigned grid = 0;
+    const df2_status st = philox_args(n, out, &grid);
+    if (st != DF2_OK || n == 0) return st;
     const int vec = aligned16(out) ? 1 : 0;
     return launch_checked(
         [&] {
             hipLaunchKernelGGL(k_philox_uniforms, dim3(grid), dim3(kPhiloxWG), 0, stream, seed,
-                               offset, n, out, vec);
+                               offset, (const uint64_t*)nullptr, n, out, vec);
         },
         "philox uniforms launch");
+}
+
+df2_status dflash2_philox_uniforms_next(uint64_t seed, uint64_t* offset, int64_t n, float* out,
+                                        hipStream_t stream) {
+    g_last_error.clear();
+    unsigned grid = 0;
+    const df2_status st = philox_args(n, out, &grid);
+    if (st != DF2_OK || n == 0) return st;
+    if (!offset) return fail(DF2_EINVAL, "NULL pointer argument");
+    if ((uintptr_t)offset & 7u) return fail(DF2_EINVAL, "offset must be 8-byte aligned");
+    const int vec = aligned16(out) ? 1 : 0;
+    const df2_status s1 = launch_checked(
+        [&] {
+            hipLaunchKernelGGL(k_philox_uniforms, dim3(grid), dim3(kPhiloxWG), 0, stream, seed,
+                               (uint64_t)0, (const uint64_t*)offset, n, out, vec);
+        },
+        "philox uniforms launch");
+    if (s1 != DF2_OK) return s1;
+    return launch_checked(
+        [&] { hipLaunchKernelGGL(k_philox_bump, dim3(1), dim3(64), 0, stream, offset); },
+        "philox offset launch");
 }
 
 df2_status dflash2_viterbi(const float* S, const int32_t* cand_idx, int32_t B, int32_t P,

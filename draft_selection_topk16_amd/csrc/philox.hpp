@@ -54,12 +54,16 @@ __device__ __forceinline__ float philox_unit(uint64_t x) {
 
 // Thread t of the grid writes uniforms 4t .. 4t+3 (those below n).  The grid
 // covers ceil(n / 4) threads; `vec` (out 16-byte aligned) lets whole blocks
-// go out as one 16-byte store.
+// go out as one 16-byte store.  With offset_ptr set, the offset is read from
+// device memory (k_philox_bump advances it afterwards, in stream order), so
+// a captured graph draws fresh uniforms on every replay.
 __global__ void __launch_bounds__(kPhiloxWG)
-k_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, float* __restrict__ out, int vec) {
+k_philox_uniforms(uint64_t seed, uint64_t offset, const uint64_t* __restrict__ offset_ptr,
+                  int64_t n, float* __restrict__ out, int vec) {
     const int64_t blk = (int64_t)blockIdx.x * kPhiloxWG + threadIdx.x;
     const int64_t i0 = blk * 4;
     if (i0 >= n) return;
+    if (offset_ptr) offset = *offset_ptr;
     const PhiloxBlock b = philox4x64_10((uint64_t)blk, offset, 0, 0, seed, 0);
     float u[4];
 #pragma unroll
@@ -71,6 +75,11 @@ k_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, float* __restrict__
         for (int q = 0; q < 4; ++q)
             if (i0 + q < n) out[i0 + q] = u[q];
     }
+}
+
+// One thread: the device-resident offset moves to the next cycle.
+__global__ void k_philox_bump(uint64_t* __restrict__ offset_ptr) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *offset_ptr += 1;
 }
 
 }  // namespace df2

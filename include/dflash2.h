@@ -328,7 +328,8 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx,
  * Advance `offset` once per draft-verify cycle and pass the [B, P] result
  * as dflash2_select_sample's u (same stream).  seed and offset are kernel
  * arguments: a call captured into a HIP graph replays the same uniforms
- * every time unless the caller updates the captured node's arguments.
+ * every time (dflash2_philox_uniforms_next keeps the offset on the device
+ * for that case).
  *   n    number of uniforms, 0 <= n <= 2^31 (n == 0 enqueues nothing;
  *        n < 0 is DF2_EINVAL, n > 2^31 DF2_EUNSUPPORTED)
  *   out  [n] float, device memory owned by the caller, 4-byte aligned
@@ -336,6 +337,21 @@ df2_status dflash2_sample_walk(const float* S, const int32_t* cand_idx,
  */
 df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n,
                                    float* out, hipStream_t stream);
+
+/*
+ * dflash2_philox_uniforms with the offset kept in device memory, for a
+ * serving loop that replays a captured HIP graph: the uniforms use the
+ * value *offset holds when the launch runs, then a second launch on the same
+ * stream adds one to it, so every replay draws the next cycle's uniforms.
+ * Nothing is allocated and no memset is enqueued.
+ *   offset  [1] uint64, device memory owned by the caller, 8-byte aligned;
+ *           calls that share it must be ordered (same stream)
+ * Other arguments as for dflash2_philox_uniforms; n == 0 enqueues nothing
+ * and leaves *offset as it is.
+ */
+df2_status dflash2_philox_uniforms_next(uint64_t seed, uint64_t* offset,
+                                        int64_t n, float* out,
+                                        hipStream_t stream);
 
 /*
  * Two-tap dynamic depthwise convolution of the block drafter ("DFlash 2:

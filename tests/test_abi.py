@@ -113,6 +113,13 @@ def test_philox_uniforms_rejects_bad_arguments(lib):
     assert b"NULL" in lib.dflash2_last_error()
     assert lib.dflash2_philox_uniforms(1, 2, 16, FAKE + 2, None) == DF2_EINVAL
     assert b"aligned" in lib.dflash2_last_error()
+    assert lib.dflash2_philox_uniforms_next(1, FAKE, 0, None, None) == DF2_OK
+    assert lib.dflash2_philox_uniforms_next(1, FAKE, -1, FAKE, None) == DF2_EINVAL
+    assert lib.dflash2_philox_uniforms_next(1, None, 16, FAKE, None) == DF2_EINVAL
+    assert b"NULL" in lib.dflash2_last_error()
+    assert lib.dflash2_philox_uniforms_next(1, FAKE + 4, 16, FAKE, None) == DF2_EINVAL
+    assert b"offset" in lib.dflash2_last_error()
+    assert lib.dflash2_philox_uniforms_next(1, FAKE, 16, FAKE + 1, None) == DF2_EINVAL
 
 
 def test_stage_entry_points_reject_bad_arguments(lib):

@@ -108,3 +108,45 @@ def test_select_sample_on_device_uniforms(name):
     check_sample(path.cpu().numpy(), q.cpu().numpy(), score.cpu().numpy(), o,
                  TOL_SAMPLE[x.wl.dtype], name)
     assert df2.device_error() == 0
+
+
+def test_uniforms_next_advances_the_device_offset():
+    """Eager calls: each uses the offset the device holds, then adds one."""
+    say("philox uniforms with a device offset, eager")
+    off = torch.tensor([41], dtype=torch.int64, device="cuda")
+    out = torch.empty((227,), dtype=torch.float32, device="cuda")
+    for k in range(3):
+        df2.philox_uniforms_next(9, off, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out.cpu().numpy()), bits(oracle.philox_uniforms(9, 41 + k, 227)))
+        assert int(off.item()) == 42 + k
+
+
+def test_uniforms_next_in_a_captured_graph():
+    """One call captured in a graph and replayed four times, with eager GPU
+    work between the replays: every replay draws the next offset's
+    uniforms, equal to the oracle's, and leaves the offset one further."""
+    say("philox uniforms with a device offset, graph replays")
+    off = torch.tensor([0], dtype=torch.int64, device="cuda")
+    out = torch.empty((224,), dtype=torch.float32, device="cuda")
+    other = torch.empty((1000,), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        df2.philox_uniforms_next(77, off, out)         # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        df2.philox_uniforms_next(77, off, out)
+    torch.cuda.synchronize()
+    off.fill_(1000)
+    torch.cuda.synchronize()
+    for i in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out.cpu().numpy()), bits(oracle.philox_uniforms(77, 1000 + i, 224))), i
+        assert int(off.item()) == 1001 + i
+        df2.philox_uniforms(5, i, 1000, out=other)      # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(other.cpu().numpy()), bits(oracle.philox_uniforms(5, i, 1000)))
