@@ -23,7 +23,8 @@ Prints ONE JSON line:
   sample      the same workloads with the sampling walk (temperature 1,
               seeded uniforms resident on the device); beside it the device
               generator of those uniforms (dflash2_philox_uniforms) alone, at
-              B*P uniforms per call and in bulk;
+              B*P uniforms per call and in bulk, and the cycle with both (the
+              uniforms drawn on the device, then the sampling select);
   conv        the drafter's two-tap dynamic convolution (dflash2_conv2) at
               the two drafter shapes: µs per call (HIP events) and % of HBM
               peak for its algorithmic bytes, input copies rotated;
@@ -173,9 +174,14 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi
     results, paths = {}, {}
     g = torch.Generator().manual_seed(0xDF2)
     u = torch.rand((wl.B, wl.P), generator=g, dtype=torch.float32).cuda()
+    off = torch.zeros((1,), dtype=torch.int64, device="cuda")
     for walk in walks:
-        calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K, walk=walk, u=u, temperature=1.0)
+        calls = [df2.PreparedSelect(l, h, A, Bt, W, prev, wl.K,
+                                    walk="sample" if walk == "sample_dev" else walk, u=u,
+                                    temperature=1.0)
                  for (l, h) in sets]
+        if walk == "sample_dev":
+            calls = [_DrawThenSelect(c, u, off, stream) for c in calls]
         torch.cuda.synchronize()
         results[walk] = _time_calls(calls, nsets, steps, warmup, stream)
         results[walk].update(rotation_sets=nsets, rotation_mb=nsets * per_set / 1e6)
@@ -188,6 +194,26 @@ def time_workload(wl, steps: int, warmup: int, rotate_mb: float, walks=("viterbi
     del sets
     torch.cuda.empty_cache()
     return x, results, paths
+
+
+class _DrawThenSelect:
+    """One serving-loop cycle of the sampling walk: the cycle's uniforms drawn
+    on the device (dflash2_philox_uniforms_next, offset in device memory),
+    then the prepared sampling select that reads them.  The generator's
+    arguments are marshalled once."""
+
+    def __init__(self, call, u, off, stream):
+        import draft_selection_topk16_amd as df2
+        self.call = call
+        self.out_path = call.out_path
+        self._fn = df2.load().dflash2_philox_uniforms_next
+        self._args = (0xD1F1A5, off.data_ptr(), u.numel(), u.data_ptr(), stream.cuda_stream)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise RuntimeError("dflash2_philox_uniforms_next failed: %d" % st)
+        self.call()
 
 
 def _time_graph(sets, A, Bt, W, prev, wl, steps: int):
@@ -555,7 +581,7 @@ def main():
         print(json.dumps(time_lmhead(wl.name, args.steps, args.warmup, cpu_rows=1)), flush=True)
         return
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
-    walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy", "sample")
+    walks = ("viterbi",) if args.no_greedy else ("viterbi", "greedy", "sample", "sample_dev")
     x, allres, paths = time_workload(wl, args.steps, args.warmup, args.rotate_mb, walks)
     res = allres["viterbi"]
     pos_per_s = wl.B * wl.P / (res["ms_per_step"] * 1e-3)
@@ -605,6 +631,12 @@ def main():
                          "kernel_us_avg": sm["kernel_ms_avg"] * 1e3,
                          "positions_per_s": wl.B * wl.P / (sm["ms_per_step"] * 1e-3),
                          "timing": sm}
+        sd = allres["sample_dev"]
+        out["sample"]["with_device_uniforms"] = {
+            "cycle": "dflash2_philox_uniforms_next, then the sampling select, per step",
+            "us_per_cycle": sd["ms_per_step"] * 1e3,
+            "kernel_us_avg": sd["kernel_ms_avg"] * 1e3,
+            "positions_per_s": wl.B * wl.P / (sd["ms_per_step"] * 1e-3)}
         log("timing the device uniforms (Philox4x64-10)")
         out["sample"]["philox_uniforms"] = {
             "generator": "Philox4x64-10, one block per four uniforms (dflash2_philox_uniforms)",
@@ -632,7 +664,9 @@ def main():
             s1 = allr1["sample"]
             out["sample"]["b1"] = {"workload": wl1.name,
                                    "us_per_cycle": s1["ms_per_step"] * 1e3,
-                                   "kernel_us_avg": s1["kernel_ms_avg"] * 1e3}
+                                   "kernel_us_avg": s1["kernel_ms_avg"] * 1e3,
+                                   "with_device_uniforms_us_per_cycle":
+                                       allr1["sample_dev"]["ms_per_step"] * 1e3}
     if not args.no_greedy:
         wlp = wl.with_(pair_scale=8.0)
         log("greedy vs Viterbi on the pair-dominant variant of %s" % wl.name)

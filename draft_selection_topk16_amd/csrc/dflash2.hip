@@ -1444,7 +1444,7 @@ df2_status dflash2_philox_uniforms(uint64_t seed, uint64_t offset, int64_t n, fl
     return launch_checked(
         [&] {
             hipLaunchKernelGGL(k_philox_uniforms, dim3(grid), dim3(kPhiloxWG), 0, stream, seed,
-                               offset, (const uint64_t*)nullptr, n, out, vec);
+                               offset, (uint64_t*)nullptr, n, out, vec, 0);
         },
         "philox uniforms launch");
 }
@@ -1458,13 +1458,16 @@ df2_status dflash2_philox_uniforms_next(uint64_t seed, uint64_t* offset, int64_t
     if (!offset) return fail(DF2_EINVAL, "NULL pointer argument");
     if ((uintptr_t)offset & 7u) return fail(DF2_EINVAL, "offset must be 8-byte aligned");
     const int vec = aligned16(out) ? 1 : 0;
+    // one workgroup (n <= 1024) advances the offset itself after a barrier;
+    // a wider grid leaves it to a one-thread launch behind it
+    const int bump = grid == 1 ? 1 : 0;
     const df2_status s1 = launch_checked(
         [&] {
             hipLaunchKernelGGL(k_philox_uniforms, dim3(grid), dim3(kPhiloxWG), 0, stream, seed,
-                               (uint64_t)0, (const uint64_t*)offset, n, out, vec);
+                               (uint64_t)0, offset, n, out, vec, bump);
         },
         "philox uniforms launch");
-    if (s1 != DF2_OK) return s1;
+    if (s1 != DF2_OK || bump) return s1;
     return launch_checked(
         [&] { hipLaunchKernelGGL(k_philox_bump, dim3(1), dim3(64), 0, stream, offset); },
         "philox offset launch");

@@ -55,15 +55,29 @@ __device__ __forceinline__ float philox_unit(uint64_t x) {
 // Thread t of the grid writes uniforms 4t .. 4t+3 (those below n).  The grid
 // covers ceil(n / 4) threads; `vec` (out 16-byte aligned) lets whole blocks
 // go out as one 16-byte store.  With offset_ptr set, the offset is read from
-// device memory (k_philox_bump advances it afterwards, in stream order), so
-// a captured graph draws fresh uniforms on every replay.
+// device memory, so a captured graph draws fresh uniforms on every replay;
+// it then moves on by one: inside this kernel when the grid is one
+// workgroup (`bump`: every thread holds the value in a register before the
+// barrier, and only then does thread 0 write), else by k_philox_bump
+// afterwards in stream order.
 __global__ void __launch_bounds__(kPhiloxWG)
-k_philox_uniforms(uint64_t seed, uint64_t offset, const uint64_t* __restrict__ offset_ptr,
-                  int64_t n, float* __restrict__ out, int vec) {
+k_philox_uniforms(uint64_t seed, uint64_t offset, uint64_t* __restrict__ offset_ptr,
+                  int64_t n, float* __restrict__ out, int vec, int bump) {
     const int64_t blk = (int64_t)blockIdx.x * kPhiloxWG + threadIdx.x;
     const int64_t i0 = blk * 4;
+    if (offset_ptr) {
+        const uint64_t v = *offset_ptr;
+        // wave-uniform value moved to scalar registers: the load has
+        // returned before the barrier below
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+        offset = ((uint64_t)hi << 32) | lo;
+        if (bump) {
+            __syncthreads();
+            if (threadIdx.x == 0) *offset_ptr = offset + 1;
+        }
+    }
     if (i0 >= n) return;
-    if (offset_ptr) offset = *offset_ptr;
     const PhiloxBlock b = philox4x64_10((uint64_t)blk, offset, 0, 0, seed, 0);
     float u[4];
 #pragma unroll

@@ -110,25 +110,29 @@ def test_select_sample_on_device_uniforms(name):
     assert df2.device_error() == 0
 
 
-def test_uniforms_next_advances_the_device_offset():
-    """Eager calls: each uses the offset the device holds, then adds one."""
-    say("philox uniforms with a device offset, eager")
+@pytest.mark.parametrize("n", [1, 227, 1024, 1025, 3840])
+def test_uniforms_next_advances_the_device_offset(n):
+    """Eager calls: each uses the offset the device holds, then adds one (in
+    the generator's own workgroup up to 1024 uniforms, by a second launch
+    beyond)."""
+    say("philox uniforms with a device offset, eager, n=%d" % n)
     off = torch.tensor([41], dtype=torch.int64, device="cuda")
-    out = torch.empty((227,), dtype=torch.float32, device="cuda")
+    out = torch.empty((n,), dtype=torch.float32, device="cuda")
     for k in range(3):
         df2.philox_uniforms_next(9, off, out)
         torch.cuda.synchronize()
-        assert np.array_equal(bits(out.cpu().numpy()), bits(oracle.philox_uniforms(9, 41 + k, 227)))
+        assert np.array_equal(bits(out.cpu().numpy()), bits(oracle.philox_uniforms(9, 41 + k, n)))
         assert int(off.item()) == 42 + k
 
 
-def test_uniforms_next_in_a_captured_graph():
+@pytest.mark.parametrize("n", [224, 3840])
+def test_uniforms_next_in_a_captured_graph(n):
     """One call captured in a graph and replayed four times, with eager GPU
     work between the replays: every replay draws the next offset's
     uniforms, equal to the oracle's, and leaves the offset one further."""
-    say("philox uniforms with a device offset, graph replays")
+    say("philox uniforms with a device offset, graph replays, n=%d" % n)
     off = torch.tensor([0], dtype=torch.int64, device="cuda")
-    out = torch.empty((224,), dtype=torch.float32, device="cuda")
+    out = torch.empty((n,), dtype=torch.float32, device="cuda")
     other = torch.empty((1000,), dtype=torch.float32, device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -145,7 +149,7 @@ def test_uniforms_next_in_a_captured_graph():
     for i in range(4):
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(bits(out.cpu().numpy()), bits(oracle.philox_uniforms(77, 1000 + i, 224))), i
+        assert np.array_equal(bits(out.cpu().numpy()), bits(oracle.philox_uniforms(77, 1000 + i, n))), i
         assert int(off.item()) == 1001 + i
         df2.philox_uniforms(5, i, 1000, out=other)      # eager work between replays
         torch.cuda.synchronize()
